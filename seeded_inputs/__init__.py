@@ -1,0 +1,152 @@
+"""Seeded synthetic operands for the FP16/BF16 GEMM and for its CPU oracle.
+
+This module is the only code shared by the GPU path's tests/bench and the
+oracle.  It produces *input bit patterns* and the workload table; it holds
+none of the GEMM arithmetic (no products, sums or output rounding).
+
+Generator (counter-based, so any element can be regenerated on its own):
+
+    key(seed, stream) = seed * 0x9E3779B97F4A7C15 + stream * 2**40      (mod 2**64)
+    x(seed, stream, i) = mix64(key(seed, stream) + i)
+    mix64(z) = the SplitMix64 output function (Steele, Lea and Flood,
+               "Fast splittable pseudorandom number generators", OOPSLA 2014):
+               z ^= z >> 30; z *= 0xBF58476D1CE4E5B9;
+               z ^= z >> 27; z *= 0x94D049BB133111EB;
+               z ^= z >> 31
+
+Distributions, for the element at flat index i = row * ld + col (ld = the
+row stride in elements; padding elements get values too):
+
+    uniform[-1,1)  : u(i) = (x >> 11) * 2**-53;  v = 2 u - 1
+    normal(0,1)    : Box-Muller on the two uniforms drawn at 2i and 2i+1:
+                     v = sqrt(-2 ln(1 - u(2i))) * cos(2 pi u(2i+1))
+    integers [-2,2]: v = (x mod 5) - 2
+
+The double v is rounded once to the operand type: FP16 by numpy's
+float64->float16 cast (round to nearest even), BF16 by float64->float32
+(numpy) then float32->bfloat16 (torch), both round-to-nearest-even.
+Stream 2r holds A and 2r+1 holds B of rotation set r (r = 0 is the set
+that is checked).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+
+def _mix64(z: np.ndarray) -> np.ndarray:
+    z = z ^ (z >> np.uint64(30))
+    z = z * _M1
+    z = z ^ (z >> np.uint64(27))
+    z = z * _M2
+    return z ^ (z >> np.uint64(31))
+
+
+def raw_u64(seed: int, stream: int, start: int, count: int) -> np.ndarray:
+    """SplitMix64 outputs for counters start .. start+count-1."""
+    key = (int(seed) * 0x9E3779B97F4A7C15 + int(stream) * (1 << 40)) & ((1 << 64) - 1)
+    with np.errstate(over="ignore"):
+        idx = np.arange(start, start + count, dtype=np.uint64)
+        return _mix64(np.uint64(key) + idx)
+
+
+def _unit(x: np.ndarray) -> np.ndarray:
+    return (x >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+
+
+def values(dist: str, seed: int, stream: int, count: int, start: int = 0) -> np.ndarray:
+    """float64 draws for flat indices start .. start+count-1."""
+    if dist == "uniform":
+        return 2.0 * _unit(raw_u64(seed, stream, start, count)) - 1.0
+    if dist == "normal":
+        u = _unit(raw_u64(seed, stream, 2 * start, 2 * count))
+        u1, u2 = u[0::2], u[1::2]
+        return np.sqrt(-2.0 * np.log1p(-u1)) * np.cos(2.0 * math.pi * u2)
+    if dist == "int5":
+        return (raw_u64(seed, stream, start, count) % np.uint64(5)).astype(np.float64) - 2.0
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def to_bits(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values once to FP16/BF16 and return their uint16 bit patterns."""
+    if dtype == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        import torch
+
+        f32 = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32))
+        return f32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(f"unknown operand type {dtype!r}")
+
+
+def matrix_bits(dtype: str, dist: str, rows: int, cols: int, ld: int | None = None,
+                seed: int = 1, stream: int = 0, scale: float = 1.0) -> np.ndarray:
+    """A rows x ld uint16 array (row-major, row stride ld) of seeded operand bits.
+
+    Only the first ``cols`` columns are meant to be read; the padding columns
+    hold draws too (they must never influence a result)."""
+    ld = cols if ld is None else ld
+    if ld < cols:
+        raise ValueError("ld < cols")
+    v = values(dist, seed, stream, rows * ld)
+    if scale != 1.0:
+        v = v * scale
+    return to_bits(v, dtype).reshape(rows, ld)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic GEMM workload: C (MxN) = A (MxK) . B, B given KxN (trans_b=0) or NxK (trans_b=1)."""
+    name: str
+    dtype: str          # "f16" | "bf16" operands
+    M: int
+    N: int
+    K: int
+    trans_b: int
+    dist: str           # "uniform" | "normal" | "normal_scaled" (normal / sqrt(K))
+    out: str            # "same" | "f32"
+    seed: int
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def algorithmic_bytes(self) -> int:
+        out_bytes = 4 if self.out == "f32" else 2
+        return 2 * (self.M * self.K + self.K * self.N) + out_bytes * self.M * self.N
+
+    def operands(self, rotation: int = 0):
+        """(A bits MxK, B bits) for rotation set ``rotation``."""
+        dist, scale = self.dist, 1.0
+        if dist == "normal_scaled":
+            dist, scale = "normal", 1.0 / math.sqrt(self.K)
+        a = matrix_bits(self.dtype, dist, self.M, self.K, seed=self.seed,
+                        stream=2 * rotation, scale=scale)
+        if self.trans_b:
+            b = matrix_bits(self.dtype, dist, self.N, self.K, seed=self.seed,
+                            stream=2 * rotation + 1, scale=scale)
+        else:
+            b = matrix_bits(self.dtype, dist, self.K, self.N, seed=self.seed,
+                            stream=2 * rotation + 1, scale=scale)
+        return a, b
+
+
+# The five workloads: a 256^3 case the oracle finishes in seconds, a 1024^3
+# case with B given transposed, the 4096x4096x8192 FP16 compute-bound shape the
+# MI355X figures are quoted on, an 8192^3 BF16 case and a tall-skinny
+# 16384x2048x8192 case with FP32 output.
+WORKLOADS = {
+    "f16_256": Workload("f16_256", "f16", 256, 256, 256, 0, "uniform", "same", 1001),
+    "f16_1024_bt": Workload("f16_1024_bt", "f16", 1024, 1024, 1024, 1, "normal_scaled", "same", 1002),
+    "f16_4096x4096x8192": Workload("f16_4096x4096x8192", "f16", 4096, 4096, 8192, 1, "uniform", "same", 1003),
+    "bf16_8192": Workload("bf16_8192", "bf16", 8192, 8192, 8192, 1, "normal", "same", 1004),
+    "f16_16384x2048x8192_f32out": Workload("f16_16384x2048x8192_f32out", "f16", 16384, 2048, 8192, 0,
+                                           "uniform", "f32", 1005),
+}
+HEADLINE = "f16_4096x4096x8192"
