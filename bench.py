@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 warp-pipelined GEMM; prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one C = A.B launch of the whole product (FP16 operands, FP32
+accumulation, FP16 output) on the compute-bound 4096x4096x8192 shape, on
+inputs already resident in HBM.  Inputs are seeded synthetic matrices (A and
+B uniform in [-1, 1), B given N x K); enough rotating input sets are kept on
+the device that one pass over them exceeds the 256 MB last-level cache, and
+consecutive steps use consecutive sets.  Warm-up launches are untimed; the K
+timed launches are bracketed by device synchronisation and timed with HIP
+events on the stream they are enqueued on.  Throughput = 2MNK / time.
+
+The CPU baseline runs the oracle (a plain binary64 triple loop) on a bounded
+block of output rows of the same workload, on the host's cores, and the GPU
+result on those rows is checked against it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import seeded_inputs as si  # noqa: E402
+
+METRIC = "FP16 GEMM TFLOP/s at M=N=4096,K=8192 and % of MI355X MFMA peak"
+# Published MI355X dense MFMA peak for FP16/BF16 (TFLOP/s).
+PEAK_TFLOPS = 2500.0
+# 256 CUs x 4 SIMDs x 1024 FLOP/clk x 2.4 GHz, the same peak from the unit counts.
+PEAK_TFLOPS_UNITS = 256 * 4 * 1024 * 2.4e9 / 1e12
+# The pages' MI355X figure for this exact metric and shape (8-wave warp-pipelined
+# Triton kernel, FP16, M=N=4096, K=8192): context for vs_baseline.
+PAGES_TFLOPS = {"f16_4096x4096x8192": 1437.0}
+MALL_BYTES = 256 * 2 ** 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "matrix_core_scheduling_amd", "csrc", "gemm_pipelined.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from the committed counter runs, if they were taken
+    on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS))
+    ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "generic"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
+    a = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this GEMM runs on a single MI355X and nothing here "
+              "shards it across GPUs (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import matrix_core_scheduling_amd as mcs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if not os.path.exists(mcs.LIBRARY):
+        from matrix_core_scheduling_amd import build
+        build.build()
+    mcs.load()
+
+    w = si.WORKLOADS[a.workload]
+    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    set_bytes = 2 * (w.M * w.K + w.K * w.N)
+    nrot = max(1, math.ceil(2 * MALL_BYTES / set_bytes))
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {w.name}: generating {nrot} rotating input sets", file=sys.stderr, flush=True)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.reshape(-1).view(np.int16)).to(dev).view(tdt)
+
+    host0 = None
+    sets = []
+    for r in range(nrot):
+        ab, bb = w.operands(r)
+        if r == 0:
+            host0 = (ab, bb)
+        sets.append((to_dev(ab), to_dev(bb)))
+        del ab, bb
+    cdt = torch.float32 if w.out == "f32" else tdt
+    outs = [torch.empty(w.M * w.N, dtype=cdt, device=dev) for _ in range(nrot)]
+    out_type = mcs.GEMM_OUT_F32 if w.out == "f32" else mcs.GEMM_OUT_SAME
+    dtype = mcs.GEMM_DTYPE_F16 if w.dtype == "f16" else mcs.GEMM_DTYPE_BF16
+    sched = {"auto": mcs.GEMM_SCHED_AUTO, "pipelined": mcs.GEMM_SCHED_PIPELINED,
+             "in_phase": mcs.GEMM_SCHED_IN_PHASE, "generic": mcs.GEMM_SCHED_GENERIC}[a.schedule]
+    lda, ldb, ldc = w.K, (w.K if w.trans_b else w.N), w.N
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    fn = mcs.load().gemm_f16 if w.dtype == "f16" else mcs.load().gemm_bf16
+
+    def launch(i):
+        A, B = sets[i % nrot]
+        C = outs[i % nrot]
+        if sched == mcs.GEMM_SCHED_AUTO:
+            st = fn(w.M, w.N, w.K, A.data_ptr(), lda, B.data_ptr(), ldb, w.trans_b, C.data_ptr(), ldc,
+                    out_type, sh)
+        else:
+            st = mcs.gemm_ex(dtype, w.M, w.N, w.K, A.data_ptr(), lda, B.data_ptr(), ldb, w.trans_b,
+                             C.data_ptr(), ldc, out_type, sched, sh)
+        if st != mcs.GEMM_OK:
+            raise mcs.GemmError(st, "launch")
+
+    print(f"[bench] warm-up {a.warmup}", file=sys.stderr, flush=True)
+    for i in range(a.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(a.steps):
+        launch(a.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / a.steps
+    tflops = w.flops / (ms_step * 1e-3) / 1e12
+
+    # five more batches of >= ~50 ms, median of their per-launch means (stability)
+    per = max(1, int(math.ceil(50.0 / max(ms_step, 1e-3))))
+    batch_ms = []
+    for b in range(5):
+        x0 = torch.cuda.Event(enable_timing=True)
+        x1 = torch.cuda.Event(enable_timing=True)
+        x0.record(stream)
+        for i in range(per):
+            launch(i + b)
+        x1.record(stream)
+        torch.cuda.synchronize()
+        batch_ms.append(x0.elapsed_time(x1) / per)
+    batch_med = float(np.median(batch_ms))
+
+    # result of set 0 for the check below (same launch configuration)
+    launch(0)
+    torch.cuda.synchronize()
+    info = mcs.gemm_kernel_info(dtype, w.trans_b, out_type,
+                                mcs.GEMM_SCHED_PIPELINED if sched == mcs.GEMM_SCHED_AUTO else sched)
+
+    cpu = None
+    check = None
+    if not a.no_cpu_baseline:
+        import oracle
+
+        ab, bb = host0
+        threads = host_threads()
+        probe_rows = 4
+        t = time.perf_counter()
+        oracle.gemm(ab, bb, w.dtype, w.trans_b, rows=(0, probe_rows), nthreads=threads, with_sabs=False)
+        per_row = (time.perf_counter() - t) / probe_rows
+        rows = int(min(w.M, max(2 * threads, a.cpu_seconds / max(per_row, 1e-6))))
+        rows = max(2, rows - rows % 2)
+        half = rows // 2
+        blocks = [(0, half), (w.M - half, w.M)]
+        print(f"[bench] CPU oracle on {rows} rows with {threads} threads", file=sys.stderr, flush=True)
+        t = time.perf_counter()
+        refs = [oracle.gemm(ab, bb, w.dtype, w.trans_b, rows=blk, nthreads=threads) for blk in blocks]
+        cpu_s = time.perf_counter() - t
+        cpu = {"value": round(2.0 * rows * w.N * w.K / cpu_s / 1e12, 6), "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"output rows [0,{half}) and [{w.M - half},{w.M}) of the same product "
+                         f"({rows}x{w.N}x{w.K}), {cpu_s:.1f} s on {cpu_model()}"}
+        Cg = outs[0].view(w.M, w.N).cpu()
+        if w.out == "f32":
+            cg = Cg.double().numpy()
+        else:
+            cg = oracle.decode(Cg.view(torch.int16).numpy().view(np.uint16), w.dtype)
+        bad = 0
+        for (r0, r1), (cref, sabs) in zip(blocks, refs):
+            bad += int((~oracle.within_tolerance(cg[r0:r1], cref, sabs)).sum())
+        check = {"rows": rows, "elements": rows * w.N, "outside_tolerance": bad, "pass": bad == 0}
+
+    traffic = traffic_for(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tflops / PAGES_TFLOPS[w.name], 4) if w.name in PAGES_TFLOPS else None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "operands": w.dtype,
+                   "accumulate": "f32", "out": w.dtype if w.out == "same" else "f32",
+                   "b_layout": "N x K row-major" if w.trans_b else "K x N row-major",
+                   "values": w.dist, "seed": w.seed, "rotating_sets": nrot,
+                   "schedule": a.schedule},
+        "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
+        "pct_of_unit_peak": round(100.0 * tflops / PEAK_TFLOPS_UNITS, 2),
+        "batch_median_ms": round(batch_med, 6),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": traffic},
+        "kernel": {"vgprs": info["num_regs"], "scratch_bytes_per_lane": info["local_bytes"],
+                   "lds_bytes": info["shared_bytes"], "threads": info["block_threads"]},
+        "cpu_baseline": cpu,
+        "check": check,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if (check is None or check["pass"]) else 3
+
+
+if __name__ == "__main__":
+    sys.exit(main())

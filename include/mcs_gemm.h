@@ -1,0 +1,138 @@
+/*
+ * mcs_gemm.h -- C ABI of libmcs_gemm.so, a gfx950 (MI355X) dense GEMM
+ *
+ *     C = A . B        FP16 or BF16 operands, FP32 accumulation,
+ *                      FP16/BF16 (same as the operands) or FP32 output.
+ *
+ * The operation is the tiled dense product of "Two Waves, One Stage Apart:
+ * Warp-Pipelining Triton GEMMs on AMD Instinct" (opening section: a tiled
+ * GEMM computes on one pair of operand tiles while it prepares the next;
+ * throughput is counted as 2MNK / elapsed time, Table 1).  The kernel holds
+ * two wave groups one stage apart (sections "Two Waves, One Stage Apart",
+ * "Creating and Closing the Offset", "MI350 Series (gfx950, CDNA 4): Three
+ * Overlapping Flows"); its buffer-resource loads with out-of-range reads
+ * returning zero follow "Porting High-Performance HIP Kernels to FlyDSL",
+ * section "Buffer Resource Descriptors".
+ *
+ * Definition (every element, exactly up to FP32 rounding):
+ *     C[i*ldc + j] = sum_{k<K} A[i*lda + k] * b(k, j)
+ *     b(k, j) = B[k*ldb + j]   if trans_b == 0   (B stored K x N, row-major)
+ *             = B[j*ldb + k]   if trans_b == 1   (B stored N x K, row-major)
+ * All matrices are row-major; leading dimensions are in ELEMENTS.  C is
+ * overwritten (no alpha/beta).  K == 0 writes zeros.  M == 0 or N == 0 is a
+ * no-op.  The FP32 -> FP16/BF16 output conversion rounds to nearest even.
+ *
+ * Ownership and threading: the caller owns every buffer and the stream.  The
+ * library keeps no per-call state and allocates nothing, so calls from
+ * several host threads are safe.  Every call is ASYNCHRONOUS: it validates,
+ * enqueues one kernel on `stream` (0 = the null stream) and returns; the
+ * caller synchronises.  C must not overlap A or B.
+ *
+ * Errors are reported before anything is enqueued (nothing runs on error):
+ *   GEMM_EINVAL       null pointer where data is needed, negative size,
+ *                     leading dimension below its minimum, bad flag value;
+ *   GEMM_EUNSUPPORTED a size the kernels cannot index (any dimension or
+ *                     leading dimension >= 2^31, or more than 2^31-1 tiles);
+ *   GEMM_EHIP         the launch itself failed (hipGetLastError() holds it).
+ * Alignment is never an error: operands that are not 16-byte aligned (or
+ * leading dimensions / K that are not multiples of 8) take a slower generic
+ * GPU kernel instead of the pipelined one.
+ */
+#ifndef MCS_GEMM_H
+#define MCS_GEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_EINVAL = -1,
+    GEMM_EUNSUPPORTED = -3,
+    GEMM_EHIP = -4
+};
+
+enum gemm_out_type {
+    GEMM_OUT_SAME = 0,   /* FP16 for gemm_f16, BF16 for gemm_bf16 */
+    GEMM_OUT_F32 = 1
+};
+
+enum gemm_dtype {
+    GEMM_DTYPE_F16 = 0,
+    GEMM_DTYPE_BF16 = 1
+};
+
+/* Kernel schedule selector for gemm_ex. */
+enum gemm_schedule {
+    GEMM_SCHED_AUTO = 0,       /* what gemm_f16 / gemm_bf16 use: PIPELINED when
+                                  the operands allow it, else GENERIC */
+    GEMM_SCHED_PIPELINED = 1,  /* 8 waves, two groups held one stage apart */
+    GEMM_SCHED_IN_PHASE = 2,   /* same kernel and stages, groups kept in phase
+                                  (no entry/exit offset): the ablation baseline */
+    GEMM_SCHED_GENERIC = 3     /* plain LDS-tiled FMA kernel, any alignment */
+};
+
+/*
+ * gemm_f16 / gemm_bf16 -- C = A . B with FP16 / BF16 operands.
+ *   M, N, K    sizes (>= 0)
+ *   A          device pointer, M x K operand, row stride lda >= max(K, 1)
+ *   B          device pointer, K x N (trans_b = 0, ldb >= max(N, 1)) or
+ *              N x K (trans_b = 1, ldb >= max(K, 1))
+ *   C          device pointer, M x N result, row stride ldc >= max(N, 1);
+ *              element type set by out_type (gemm_out_type)
+ *   stream     HIP stream the kernel is enqueued on
+ * Returns a gemm_status.
+ */
+int gemm_f16(int64_t M, int64_t N, int64_t K,
+             const void *A, int64_t lda,
+             const void *B, int64_t ldb, int trans_b,
+             void *C, int64_t ldc, int out_type,
+             hipStream_t stream);
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const void *A, int64_t lda,
+              const void *B, int64_t ldb, int trans_b,
+              void *C, int64_t ldc, int out_type,
+              hipStream_t stream);
+
+/*
+ * gemm_ex -- the same product with the operand type (gemm_dtype) and the
+ * kernel schedule (gemm_schedule) chosen by the caller.  PIPELINED and
+ * IN_PHASE need 16-byte aligned A, B, C, lda/ldb/ldc and K multiples of 8;
+ * asking for them otherwise returns GEMM_EINVAL.
+ */
+int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K,
+            const void *A, int64_t lda,
+            const void *B, int64_t ldb, int trans_b,
+            void *C, int64_t ldc, int out_type, int schedule,
+            hipStream_t stream);
+
+/* Static description of one compiled kernel variant (from the code object). */
+typedef struct gemm_kernel_attrs {
+    int num_regs;          /* VGPRs per lane as reported by the runtime */
+    int local_bytes;       /* private (scratch) bytes per lane: 0 means no spills */
+    int shared_bytes;      /* static LDS per workgroup */
+    int max_threads;       /* maximum workgroup size */
+    int block_threads;     /* workgroup size the library launches */
+    int tile_m, tile_n, tile_k;
+} gemm_kernel_attrs;
+
+/*
+ * gemm_kernel_info -- attributes of the kernel gemm_ex would launch for
+ * (dtype, trans_b, out_type, schedule).  Needs a HIP device.  Returns a
+ * gemm_status; *out is filled on GEMM_OK.
+ */
+int gemm_kernel_info(int dtype, int trans_b, int out_type, int schedule,
+                     gemm_kernel_attrs *out);
+
+/* Static text for a gemm_status value. */
+const char *gemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MCS_GEMM_H */

@@ -1,0 +1,151 @@
+"""Python binding of libmcs_gemm.so, the gfx950 warp-pipelined FP16/BF16 GEMM.
+
+The functions ``gemm_f16``, ``gemm_bf16``, ``gemm_ex``, ``gemm_kernel_info`` and
+``gemm_status_string`` mirror the C ABI in ``include/mcs_gemm.h`` one to one
+(sizes, raw device pointers as integers, a raw ``hipStream_t``).  ``gemm``
+marshals torch tensors onto them: torch provides device memory and the
+current stream, every step of the product runs in the library's HIP kernels.
+
+There is no fallback: if the library is not built, every call raises.
+Build it with ``python -m matrix_core_scheduling_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libmcs_gemm.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "mcs_gemm.h")
+
+GEMM_OK, GEMM_EINVAL, GEMM_EUNSUPPORTED, GEMM_EHIP = 0, -1, -3, -4
+GEMM_OUT_SAME, GEMM_OUT_F32 = 0, 1
+GEMM_DTYPE_F16, GEMM_DTYPE_BF16 = 0, 1
+GEMM_SCHED_AUTO, GEMM_SCHED_PIPELINED, GEMM_SCHED_IN_PHASE, GEMM_SCHED_GENERIC = 0, 1, 2, 3
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {gemm_status_string(status)} ({status})" if what else
+                         f"{gemm_status_string(status)} ({status})")
+
+
+class GemmKernelAttrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("num_regs", "local_bytes", "shared_bytes", "max_threads",
+                                            "block_threads", "tile_m", "tile_n", "tile_k")]
+
+
+_lib = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m matrix_core_scheduling_amd.build` "
+                           "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(path)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    sig = [i64, i64, i64, vp, i64, vp, i64, ci, vp, i64, ci]
+    for name in ("gemm_f16", "gemm_bf16"):
+        f = getattr(lib, name)
+        f.argtypes = sig + [vp]
+        f.restype = ci
+    lib.gemm_ex.argtypes = [ci] + sig + [ci, vp]
+    lib.gemm_ex.restype = ci
+    lib.gemm_kernel_info.argtypes = [ci, ci, ci, ci, ctypes.POINTER(GemmKernelAttrs)]
+    lib.gemm_kernel_info.restype = ci
+    lib.gemm_status_string.argtypes = [ci]
+    lib.gemm_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER) -> list[str]:
+    """Names of the functions include/mcs_gemm.h declares."""
+    text = open(path).read()
+    return re.findall(r"^(?:int|const char \*)\s*(\w+)\s*\(", text, flags=re.M)
+
+
+# ---- the C ABI, one to one --------------------------------------------------
+
+def gemm_f16(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream) -> int:
+    return load().gemm_f16(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream)
+
+
+def gemm_bf16(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream) -> int:
+    return load().gemm_bf16(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream)
+
+
+def gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream) -> int:
+    return load().gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream)
+
+
+def gemm_kernel_info(dtype: int, trans_b: int, out_type: int, schedule: int) -> dict:
+    a = GemmKernelAttrs()
+    st = load().gemm_kernel_info(dtype, trans_b, out_type, schedule, ctypes.byref(a))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_kernel_info")
+    return {n: getattr(a, n) for n, _ in GemmKernelAttrs._fields_}
+
+
+def gemm_status_string(status: int) -> str:
+    return load().gemm_status_string(status).decode()
+
+
+# ---- torch marshalling ---------------------------------------------------
+
+def _stream_handle(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+
+
+def gemm(A, B, trans_b: bool = False, out=None, out_dtype=None,
+         schedule: int = GEMM_SCHED_AUTO, stream=None):
+    """C = A @ B (trans_b=False, B is K x N) or A @ B.T (trans_b=True, B is N x K).
+
+    A, B: 2-D float16/bfloat16 CUDA tensors with unit column stride (rows may
+    be padded: the row stride is passed as the leading dimension).  ``out``
+    (M x N, unit column stride) is written in place if given; otherwise a
+    tensor of ``out_dtype`` (default: the operand dtype; float32 allowed) is
+    allocated by torch.  Runs on the current stream (or ``stream``) and does
+    not synchronise."""
+    import torch
+
+    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("A and B must both be float16 or both bfloat16")
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    if A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A and B need unit column stride")
+    M, K = A.shape
+    if trans_b:
+        N, Kb = B.shape
+    else:
+        Kb, N = B.shape
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
+    if out.shape != (M, N) or (out.stride(1) != 1 and N > 1):
+        raise ValueError("out must be M x N with unit column stride")
+    if out.dtype == torch.float32:
+        out_type = GEMM_OUT_F32
+    elif out.dtype == A.dtype:
+        out_type = GEMM_OUT_SAME
+    else:
+        raise TypeError("out must have the operand dtype or float32")
+    dtype = GEMM_DTYPE_F16 if A.dtype == torch.float16 else GEMM_DTYPE_BF16
+    lda = A.stride(0) if M > 1 else max(K, 1)
+    ldb = B.stride(0) if B.shape[0] > 1 else max(B.shape[1], 1)
+    ldc = out.stride(0) if M > 1 else max(N, 1)
+    st = gemm_ex(dtype, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, int(bool(trans_b)),
+                 out.data_ptr(), ldc, out_type, schedule, _stream_handle(stream))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm")
+    return out

@@ -1,0 +1,106 @@
+// Generic GEMM kernel for operands the pipelined kernel cannot take (pointers
+// or leading dimensions not 16-byte aligned, K not a multiple of 8, very wide
+// rows): C = A . B with FP32 fused multiply-adds in increasing k, 64-bit
+// indexing, element loads.  Same definition as the pipelined kernel, slower.
+#include "internal.h"
+
+namespace mcs {
+namespace {
+
+template <bool kBF16>
+__device__ __forceinline__ float widen(uint16_t bits) {
+    if constexpr (kBF16)
+        return __uint_as_float(static_cast<uint32_t>(bits) << 16);
+    else
+        return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+}
+
+constexpr int kGenK = 16;
+
+// 64x64 output tile per 256-thread workgroup; thread (ty, tx) owns rows
+// ty + 16*i and columns tx + 16*j, i, j < 4.
+template <bool kBF16, bool kTransB, bool kOutF32>
+__global__ void __launch_bounds__(kGenThreads) gemm_generic_kernel(GemmParams p) {
+    __shared__ float As[kGenK][kGenTile + 1];
+    __shared__ float Bs[kGenK][kGenTile + 1];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kGenTile;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kGenTile;
+    float acc[4][4];
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+    for (int64_t k0 = 0; k0 < p.K; k0 += kGenK) {
+        for (int e = threadIdx.x; e < kGenK * kGenTile; e += kGenThreads) {
+            const int kk = e % kGenK, mm = e / kGenK;
+            const int64_t gm = m0 + mm, gk = k0 + kk;
+            As[kk][mm] = (gm < p.M && gk < p.K) ? widen<kBF16>(p.A[gm * p.lda + gk]) : 0.f;
+        }
+        for (int e = threadIdx.x; e < kGenK * kGenTile; e += kGenThreads) {
+            int kk, nn;
+            if constexpr (kTransB) { kk = e % kGenK; nn = e / kGenK; }
+            else { nn = e % kGenTile; kk = e / kGenTile; }
+            const int64_t gn = n0 + nn, gk = k0 + kk;
+            float v = 0.f;
+            if (gn < p.N && gk < p.K)
+                v = widen<kBF16>(kTransB ? p.B[gn * p.ldb + gk] : p.B[gk * p.ldb + gn]);
+            Bs[kk][nn] = v;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < kGenK; ++kk)
+            for (int i = 0; i < 4; ++i)
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_fmaf(As[kk][ty + 16 * i], Bs[kk][tx + 16 * j], acc[i][j]);
+        __syncthreads();
+    }
+    for (int i = 0; i < 4; ++i) {
+        const int64_t gm = m0 + ty + 16 * i;
+        if (gm >= p.M) continue;
+        for (int j = 0; j < 4; ++j) {
+            const int64_t gn = n0 + tx + 16 * j;
+            if (gn >= p.N) continue;
+            if constexpr (kOutF32) {
+                reinterpret_cast<float *>(p.C)[gm * p.ldc + gn] = acc[i][j];
+            } else if constexpr (kBF16) {
+                reinterpret_cast<__bf16 *>(p.C)[gm * p.ldc + gn] = static_cast<__bf16>(acc[i][j]);
+            } else {
+                reinterpret_cast<_Float16 *>(p.C)[gm * p.ldc + gn] = static_cast<_Float16>(acc[i][j]);
+            }
+        }
+    }
+}
+
+// C = 0 for K == 0 (an empty sum).  One thread per element, grid-stride.
+template <bool kOutF32>
+__global__ void __launch_bounds__(256) zero_fill(GemmParams p) {
+    const int64_t total = static_cast<int64_t>(p.M) * p.N;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total;
+         e += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t i = e / p.N, j = e % p.N;
+        if constexpr (kOutF32)
+            reinterpret_cast<float *>(p.C)[i * p.ldc + j] = 0.f;
+        else
+            reinterpret_cast<uint16_t *>(p.C)[i * p.ldc + j] = 0;
+    }
+}
+
+}  // namespace
+
+const void *generic_kernel(bool bf16, bool trans_b, bool out_f32) {
+#define MCS_PICK(B, T, O)                                 \
+    if (bf16 == B && trans_b == T && out_f32 == O)        \
+        return reinterpret_cast<const void *>(&gemm_generic_kernel<B, T, O>);
+    MCS_PICK(false, false, false) MCS_PICK(false, false, true)
+    MCS_PICK(false, true, false) MCS_PICK(false, true, true)
+    MCS_PICK(true, false, false) MCS_PICK(true, false, true)
+    MCS_PICK(true, true, false) MCS_PICK(true, true, true)
+#undef MCS_PICK
+    return nullptr;
+}
+
+const void *zero_fill_kernel(bool out_f32) {
+    return out_f32 ? reinterpret_cast<const void *>(&zero_fill<true>)
+                   : reinterpret_cast<const void *>(&zero_fill<false>);
+}
+
+}  // namespace mcs

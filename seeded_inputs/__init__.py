@@ -35,9 +35,11 @@ import math
 
 import numpy as np
 
-_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
+
+
+_CHUNK = 1 << 20
 
 
 def _mix64(z: np.ndarray) -> np.ndarray:
@@ -48,29 +50,95 @@ def _mix64(z: np.ndarray) -> np.ndarray:
     return z ^ (z >> np.uint64(31))
 
 
+def _key(seed: int, stream: int) -> int:
+    return (int(seed) * 0x9E3779B97F4A7C15 + int(stream) * (1 << 40)) & ((1 << 64) - 1)
+
+
+class _Scratch:
+    """Chunk buffers reused across calls (fresh pages are slow on some hosts)."""
+
+    def __init__(self):
+        self.base = np.arange(2 * _CHUNK, dtype=np.uint64)
+        self.z = np.empty(2 * _CHUNK, dtype=np.uint64)
+        self.t = np.empty(2 * _CHUNK, dtype=np.uint64)
+        self.f = np.empty(2 * _CHUNK, dtype=np.float64)
+        self.g = np.empty(_CHUNK, dtype=np.float64)
+
+
+_scratch = None
+
+
+def _mix_chunk(key: int, start: int, m: int, sc: _Scratch) -> np.ndarray:
+    """mix64(key + start + i) for i < m, in sc.z[:m] (in place, no allocation)."""
+    z, t = sc.z[:m], sc.t[:m]
+    with np.errstate(over="ignore"):
+        np.add(sc.base[:m], np.uint64((key + start) & ((1 << 64) - 1)), out=z)
+        for shift, mul in ((30, _M1), (27, _M2)):
+            np.right_shift(z, np.uint64(shift), out=t)
+            np.bitwise_xor(z, t, out=z)
+            np.multiply(z, mul, out=z)
+        np.right_shift(z, np.uint64(31), out=t)
+        np.bitwise_xor(z, t, out=z)
+    return z
+
+
 def raw_u64(seed: int, stream: int, start: int, count: int) -> np.ndarray:
     """SplitMix64 outputs for counters start .. start+count-1."""
-    key = (int(seed) * 0x9E3779B97F4A7C15 + int(stream) * (1 << 40)) & ((1 << 64) - 1)
+    key = _key(seed, stream)
     with np.errstate(over="ignore"):
         idx = np.arange(start, start + count, dtype=np.uint64)
         return _mix64(np.uint64(key) + idx)
 
 
-def _unit(x: np.ndarray) -> np.ndarray:
-    return (x >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+def _values_into(dist: str, seed: int, stream: int, start: int, out: np.ndarray, scale: float = 1.0):
+    """Write float64 draws for flat indices start .. start+len(out)-1 into out
+    (any float dtype: the float64 draw is cast once on assignment)."""
+    global _scratch
+    if _scratch is None:
+        _scratch = _Scratch()
+    sc = _scratch
+    key = _key(seed, stream)
+    count = out.size
+    for c0 in range(0, count, _CHUNK):
+        m = min(_CHUNK, count - c0)
+        f = sc.f[:m]
+        if dist == "uniform":
+            z = _mix_chunk(key, start + c0, m, sc)
+            np.right_shift(z, np.uint64(11), out=z)
+            np.multiply(z, 2.0 ** -52, out=f, casting="unsafe")       # 2u, u = (x >> 11) 2^-53
+            np.subtract(f, 1.0, out=f)
+        elif dist == "normal":
+            z = _mix_chunk(key, 2 * (start + c0), 2 * m, sc)
+            np.right_shift(z, np.uint64(11), out=z)
+            u = sc.f[:2 * m]
+            np.multiply(z, 2.0 ** -53, out=u, casting="unsafe")
+            g = sc.g[:m]
+            np.multiply(u[1::2], 2.0 * math.pi, out=g)              # 2 pi u(2i+1)
+            np.cos(g, out=g)
+            r = u[0::2]                                              # -> sqrt(-2 ln(1 - u(2i)))
+            np.negative(r, out=r)
+            np.log1p(r, out=r)
+            np.multiply(r, -2.0, out=r)
+            np.sqrt(r, out=r)
+            np.multiply(r, g, out=g)
+            f = g
+        elif dist == "int5":
+            z = _mix_chunk(key, start + c0, m, sc)
+            np.remainder(z, np.uint64(5), out=z)
+            np.subtract(z, np.uint64(2), out=z)                     # 0, 1 wrap around ...
+            np.copyto(f, z.view(np.int64), casting="unsafe")         # ... and read back as -2, -1
+        else:
+            raise ValueError(f"unknown distribution {dist!r}")
+        if scale != 1.0:
+            np.multiply(f, scale, out=f)
+        out[c0:c0 + m] = f
 
 
 def values(dist: str, seed: int, stream: int, count: int, start: int = 0) -> np.ndarray:
     """float64 draws for flat indices start .. start+count-1."""
-    if dist == "uniform":
-        return 2.0 * _unit(raw_u64(seed, stream, start, count)) - 1.0
-    if dist == "normal":
-        u = _unit(raw_u64(seed, stream, 2 * start, 2 * count))
-        u1, u2 = u[0::2], u[1::2]
-        return np.sqrt(-2.0 * np.log1p(-u1)) * np.cos(2.0 * math.pi * u2)
-    if dist == "int5":
-        return (raw_u64(seed, stream, start, count) % np.uint64(5)).astype(np.float64) - 2.0
-    raise ValueError(f"unknown distribution {dist!r}")
+    out = np.empty(count, dtype=np.float64)
+    _values_into(dist, seed, stream, start, out)
+    return out
 
 
 def to_bits(v: np.ndarray, dtype: str) -> np.ndarray:
@@ -94,10 +162,18 @@ def matrix_bits(dtype: str, dist: str, rows: int, cols: int, ld: int | None = No
     ld = cols if ld is None else ld
     if ld < cols:
         raise ValueError("ld < cols")
-    v = values(dist, seed, stream, rows * ld)
-    if scale != 1.0:
-        v = v * scale
-    return to_bits(v, dtype).reshape(rows, ld)
+    n = rows * ld
+    if dtype == "f16":
+        out = np.empty(n, dtype=np.float16)
+        _values_into(dist, seed, stream, 0, out, scale)
+        return out.view(np.uint16).reshape(rows, ld)
+    out = np.empty(n, dtype=np.uint16)
+    buf = np.empty(min(n, _CHUNK), dtype=np.float32)
+    for c0 in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - c0)
+        _values_into(dist, seed, stream, c0, buf[:m], scale)
+        out[c0:c0 + m] = to_bits(buf[:m], "bf16")
+    return out.reshape(rows, ld)
 
 
 @dataclasses.dataclass(frozen=True)

@@ -1,0 +1,93 @@
+"""Helpers for the GPU tests: upload seeded operand bits, run the library
+through its C ABI, and read results back as float64."""
+from __future__ import annotations
+
+import numpy as np
+
+import matrix_core_scheduling_amd as mcs
+import oracle
+
+TORCH_DT = {}
+
+
+def _torch():
+    import torch
+    if not TORCH_DT:
+        TORCH_DT.update({"f16": torch.float16, "bf16": torch.bfloat16})
+    return torch
+
+
+def upload(bits: np.ndarray, elem: str, pad_front: int = 0):
+    """uint16 bits (rows x ld) -> device tensor of the operand dtype.  With
+    pad_front > 0 the data starts pad_front elements into the allocation
+    (to build misaligned operands)."""
+    torch = _torch()
+    flat = np.ascontiguousarray(bits).reshape(-1).view(np.int16)
+    t = torch.empty(flat.size + pad_front, dtype=torch.int16, device="cuda")
+    t[pad_front:].copy_(torch.from_numpy(flat.copy()))
+    return t.view(TORCH_DT[elem]), pad_front
+
+
+def run(elem: str, M: int, N: int, K: int, a_bits, b_bits, trans_b: int, out: str = "same",
+        schedule: int = mcs.GEMM_SCHED_AUTO, ldc: int | None = None, c_fill: float | None = None,
+        a_offset: int = 0, entry: str = "ex", return_raw: bool = False):
+    """C = A.B on the GPU through the C ABI; returns (C float64 M x N, raw C bits or None)."""
+    torch = _torch()
+    print(f"[gpu] {entry} elem={elem} M={M} N={N} K={K} trans_b={trans_b} out={out} "
+          f"sched={schedule} ldc={ldc} a_off={a_offset}", flush=True)
+    lda = a_bits.shape[1]
+    ldb = b_bits.shape[1]
+    A, off = upload(a_bits, elem, a_offset)
+    B, _ = upload(b_bits, elem)
+    ldc = N if ldc is None else ldc
+    cdt = torch.float32 if out == "f32" else TORCH_DT[elem]
+    C = torch.empty(max(M, 1) * ldc, dtype=cdt, device="cuda")
+    if c_fill is not None:
+        C.fill_(c_fill)
+    out_type = mcs.GEMM_OUT_F32 if out == "f32" else mcs.GEMM_OUT_SAME
+    stream = torch.cuda.current_stream().cuda_stream
+    a_ptr = A.data_ptr() + 2 * off
+    if entry == "ex":
+        dt = mcs.GEMM_DTYPE_F16 if elem == "f16" else mcs.GEMM_DTYPE_BF16
+        st = mcs.gemm_ex(dt, M, N, K, a_ptr, lda, B.data_ptr(), ldb, trans_b, C.data_ptr(), ldc,
+                         out_type, schedule, stream)
+    else:
+        fn = mcs.gemm_f16 if elem == "f16" else mcs.gemm_bf16
+        st = fn(M, N, K, a_ptr, lda, B.data_ptr(), ldb, trans_b, C.data_ptr(), ldc, out_type, stream)
+    assert st == mcs.GEMM_OK, mcs.gemm_status_string(st)
+    torch.cuda.synchronize()
+    full = C.view(max(M, 1), ldc)
+    raw = full.cpu()
+    if out == "f32":
+        vals = raw.double().numpy()
+        bits = raw.numpy().view(np.uint32)
+    else:
+        bits = raw.view(torch.int16).numpy().view(np.uint16)
+        vals = oracle.decode(bits, elem)
+    if return_raw:
+        return vals[:M, :N], bits, vals
+    return vals[:M, :N], bits[:M, :N]
+
+
+def assert_within_tolerance(c, cref, sabs, what=""):
+    ok = oracle.within_tolerance(c, cref, sabs)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i, j = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} of {ok.size} elements outside tolerance; first at "
+                             f"({i},{j}): got {c[i, j]!r}, oracle {cref[i, j]!r}, Sabs {sabs[i, j]!r}")
+
+
+def assert_bit_exact(c_bits, cref, elem, out, what=""):
+    """Integer regime: C must be the round-to-nearest-even of the exact value."""
+    if out == "f32":
+        want = cref.astype(np.float32)
+        got = c_bits.view(np.float32)
+        eq = got.astype(np.float64) == want.astype(np.float64)
+    else:
+        want = oracle.round_to(cref, elem)
+        eq = oracle.decode(c_bits, elem) == oracle.decode(want, elem)     # +0 == -0
+    if not eq.all():
+        bad = np.argwhere(~eq)
+        i, j = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} elements differ; first at ({i},{j}) oracle {cref[i, j]}")

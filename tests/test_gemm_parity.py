@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: every element within |C - Cref| <= 2e-3 * Sabs + 2^-10 * |Cref|, and
+bit-exact (round-to-nearest-even of the exact value) for integer operands in
+[-2, 2] with K <= 512, where FP32 accumulation is exact in any order.
+"""
+import numpy as np
+import pytest
+
+import matrix_core_scheduling_amd as mcs
+import oracle
+import seeded_inputs as si
+from tests.gpu_util import assert_bit_exact, assert_within_tolerance, run
+
+pytestmark = pytest.mark.gpu
+
+SCHEDS = {"pipelined": mcs.GEMM_SCHED_PIPELINED, "in_phase": mcs.GEMM_SCHED_IN_PHASE,
+          "generic": mcs.GEMM_SCHED_GENERIC}
+
+
+def operands(elem, dist, M, N, K, trans_b, seed, lda=None, ldb=None, nan_pad=False):
+    a = si.matrix_bits(elem, dist, M, K, ld=lda, seed=seed, stream=0)
+    if trans_b:
+        b = si.matrix_bits(elem, dist, N, K, ld=ldb, seed=seed, stream=1)
+    else:
+        b = si.matrix_bits(elem, dist, K, N, ld=ldb, seed=seed, stream=1)
+    if nan_pad:
+        nan = 0x7E00 if elem == "f16" else 0x7FC0
+        a[:, K:] = nan
+        if trans_b:
+            b[:, K:] = nan
+        else:
+            b[:, N:] = nan
+    return a, b
+
+
+def ref(a, b, elem, trans_b, K, N):
+    return oracle.gemm(a, b, elem, trans_b, K=K, N=N)
+
+
+def rup8(x):
+    return (x + 7) // 8 * 8
+
+
+# ---- small and ragged shapes: every element --------------------------------
+
+SHAPES = [(256, 256, 256), (1, 1, 8), (17, 33, 8), (300, 520, 200), (513, 257, 72), (64, 640, 1000)]
+
+
+@pytest.mark.parametrize("sched", ["pipelined", "in_phase"])
+@pytest.mark.parametrize("out", ["same", "f32"])
+@pytest.mark.parametrize("trans_b", [0, 1])
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes_every_element(shape, elem, trans_b, out, sched):
+    M, N, K = shape
+    lda = rup8(K) + 8                      # padded rows, padding filled with NaN
+    ldb = (rup8(K) + 8) if trans_b else (rup8(N) + 8)
+    a, b = operands(elem, "uniform", M, N, K, trans_b, seed=100 + M + N + K, lda=lda, ldb=ldb,
+                    nan_pad=True)
+    cref, sabs = ref(a, b, elem, trans_b, K, N)
+    c, _ = run(elem, M, N, K, a, b, trans_b, out=out, schedule=SCHEDS[sched])
+    assert_within_tolerance(c, cref, sabs, f"{shape} {elem} tb={trans_b} {out} {sched}")
+
+
+@pytest.mark.parametrize("trans_b", [0, 1])
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+def test_generic_kernel_every_element(elem, trans_b):
+    M, N, K = 130, 77, 45                  # K % 8 != 0 and odd sizes: only the generic kernel
+    a, b = operands(elem, "normal", M, N, K, trans_b, seed=3)
+    cref, sabs = ref(a, b, elem, trans_b, K, N)
+    c, _ = run(elem, M, N, K, a, b, trans_b, schedule=mcs.GEMM_SCHED_AUTO)
+    assert_within_tolerance(c, cref, sabs, "generic")
+    c, _ = run(elem, M, N, K, a, b, trans_b, schedule=mcs.GEMM_SCHED_GENERIC, out="f32")
+    assert_within_tolerance(c, cref, sabs, "generic f32")
+
+
+# ---- exact-integer regime: bit-exact ------------------------------------------
+
+INT_SHAPES = [(256, 256, 32), (512, 256, 64), (256, 512, 192), (512, 512, 448), (1024, 1024, 512)]
+
+
+@pytest.mark.parametrize("out", ["same", "f32"])
+@pytest.mark.parametrize("trans_b", [0, 1])
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", INT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_integer_regime_bit_exact(shape, elem, trans_b, out):
+    M, N, K = shape
+    a, b = operands(elem, "int5", M, N, K, trans_b, seed=7 + K)
+    cref = oracle.gemm(a, b, elem, trans_b, with_sabs=False)
+    _, bits = run(elem, M, N, K, a, b, trans_b, out=out, schedule=mcs.GEMM_SCHED_PIPELINED)
+    assert_bit_exact(bits, cref, elem, out, f"int {shape} {elem} tb={trans_b} {out}")
+
+
+# ---- closed forms ---------------------------------------------------------------
+
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+def test_identity_gives_b(elem):
+    n, m = 512, 384
+    one = 0x3C00 if elem == "f16" else 0x3F80
+    eye = np.zeros((n, n), np.uint16)
+    eye[np.arange(n), np.arange(n)] = one
+    b = si.matrix_bits(elem, "normal", n, m, seed=11, stream=1)               # K x N
+    _, bits = run(elem, n, m, n, eye, b, 0)
+    assert np.array_equal(oracle.decode(bits, elem), oracle.decode(b, elem))
+    bt = np.ascontiguousarray(b.T)                                            # N x K
+    _, bits = run(elem, n, m, n, eye, bt, 1)
+    assert np.array_equal(oracle.decode(bits, elem), oracle.decode(b, elem))
+
+
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+def test_permutation_permutes_rows(elem):
+    n, m = 256, 320
+    one = 0x3C00 if elem == "f16" else 0x3F80
+    perm = np.random.default_rng(5).permutation(n)
+    P = np.zeros((n, n), np.uint16)
+    P[np.arange(n), perm] = one
+    b = si.matrix_bits(elem, "uniform", n, m, seed=12, stream=1)
+    _, bits = run(elem, n, m, n, P, b, 0)
+    assert np.array_equal(oracle.decode(bits, elem), oracle.decode(b[perm], elem))
+
+
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+def test_all_ones_gives_k(elem):
+    M, N, K = 256, 512, 8192                   # 8192 = 2^13: exact in both output types
+    one = 0x3C00 if elem == "f16" else 0x3F80
+    a = np.full((M, K), one, np.uint16)
+    b = np.full((N, K), one, np.uint16)
+    c, _ = run(elem, M, N, K, a, b, 1)
+    assert np.all(c == K)
+
+
+def test_rank_one_integer():
+    rng = np.random.default_rng(8)
+    M, N, K = 300, 260, 96
+    u = rng.integers(-3, 4, M).astype(np.float16)
+    v = rng.integers(-3, 4, N).astype(np.float16)
+    a = np.repeat(u[:, None], K, axis=1).view(np.uint16)
+    b = np.repeat(v[None, :], K, axis=0).view(np.uint16)
+    c, _ = run("f16", M, N, K, np.ascontiguousarray(a), np.ascontiguousarray(b), 0, out="f32")
+    assert np.array_equal(c, K * np.outer(u.astype(np.float64), v.astype(np.float64)))
+
+
+# ---- the five workloads, in the configuration the benchmark launches -----------
+
+def sample_points(M, N, count, seed):
+    rng = np.random.default_rng(seed)
+    ii = list(rng.integers(0, M, count))
+    jj = list(rng.integers(0, N, count))
+    # tile corners and edges of the 256x256 output tiles and of the matrix
+    for i in sorted({0, 127, 128, 255, 256, M // 2, M - 1} & set(range(M))):
+        for j in sorted({0, 127, 128, 255, 256, N // 2, N - 1} & set(range(N))):
+            ii.append(i)
+            jj.append(j)
+    return np.array(ii), np.array(jj)
+
+
+@pytest.mark.parametrize("name", list(si.WORKLOADS))
+def test_workload(name):
+    w = si.WORKLOADS[name]
+    a, b = w.operands(0)
+    c, _ = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, entry="abi")
+    if w.M * w.N * w.K <= 2 ** 31:
+        cref, sabs = oracle.gemm(a, b, w.dtype, w.trans_b)
+        assert_within_tolerance(c, cref, sabs, name)
+    else:
+        ii, jj = sample_points(w.M, w.N, 3000, seed=w.seed)
+        cref, sabs = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
+        assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name)
+        # properties at every element: finite, and bounded by the operands
+        assert np.isfinite(c).all()
+
+
+# ---- invariants --------------------------------------------------------------
+
+def test_deterministic_and_schedules_agree_bitwise():
+    w = si.WORKLOADS["f16_1024_bt"]
+    a, b = w.operands(0)
+    outs = [run("f16", w.M, w.N, w.K, a, b, 1, schedule=s)[1]
+            for s in (mcs.GEMM_SCHED_PIPELINED, mcs.GEMM_SCHED_PIPELINED, mcs.GEMM_SCHED_IN_PHASE)]
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0], outs[2])
+
+
+def test_repeated_runs_are_bitwise_identical():
+    M, N, K = 2048, 2048, 4096
+    a, b = operands("bf16", "normal", M, N, K, 1, seed=99)
+    first = run("bf16", M, N, K, a, b, 1)[1]
+    for _ in range(5):
+        assert np.array_equal(run("bf16", M, N, K, a, b, 1)[1], first)
+
+
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+def test_b_layouts_agree_bitwise(elem):
+    M, N, K = 384, 640, 1216
+    a, b = operands(elem, "uniform", M, N, K, 0, seed=41)
+    c0 = run(elem, M, N, K, a, b, 0, out="f32")[1]
+    c1 = run(elem, M, N, K, a, np.ascontiguousarray(b.T), 1, out="f32")[1]
+    assert np.array_equal(c0, c1)
+
+
+# ---- edge cases ----------------------------------------------------------------
+
+def test_k_zero_writes_zeros():
+    a = np.zeros((64, 8), np.uint16)
+    b = np.zeros((64, 8), np.uint16)
+    c, _ = run("f16", 64, 48, 0, a, b, 1, c_fill=7.0)
+    assert np.all(c == 0)
+
+
+def test_m_zero_is_a_no_op():
+    torch = pytest.importorskip("torch")
+    C = torch.full((4, 8), 3.0, dtype=torch.float16, device="cuda")
+    st = mcs.gemm_f16(0, 8, 16, 0, 16, 0, 16, 1, C.data_ptr(), 8, 0, 0)
+    torch.cuda.synchronize()
+    assert st == mcs.GEMM_OK and bool((C == 3).all())
+
+
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+def test_output_padding_untouched(elem):
+    M, N, K, ldc = 200, 100, 136, 136
+    a, b = operands(elem, "uniform", M, N, K, 1, seed=13)
+    c, bits, full = run(elem, M, N, K, a, b, 1, ldc=ldc, c_fill=5.0, return_raw=True)
+    assert np.all(full[:, N:] == 5.0)
+    cref, sabs = ref(a, b, elem, 1, K, N)
+    assert_within_tolerance(c, cref, sabs, "ldc > N")
+
+
+def test_misaligned_operand_takes_generic_path_and_is_correct():
+    M, N, K = 100, 70, 64
+    a, b = operands("f16", "uniform", M, N, K, 1, seed=17)
+    cref, sabs = ref(a, b, "f16", 1, K, N)
+    c, _ = run("f16", M, N, K, a, b, 1, a_offset=1)          # A starts 2 bytes into its buffer
+    assert_within_tolerance(c, cref, sabs, "misaligned A")
+
+
+def test_kernels_have_no_spills():
+    for dt in (mcs.GEMM_DTYPE_F16, mcs.GEMM_DTYPE_BF16):
+        for out in (mcs.GEMM_OUT_SAME, mcs.GEMM_OUT_F32):
+            info = mcs.gemm_kernel_info(dt, 1, out, mcs.GEMM_SCHED_PIPELINED)
+            assert info["local_bytes"] == 0, info
+            assert info["shared_bytes"] == 128 * 1024, info
+            assert info["block_threads"] == 512
