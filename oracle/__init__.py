@@ -174,7 +174,22 @@ def gemm_points(*args, **kw):
     return default().gemm_points(*args, **kw)
 
 
-def within_tolerance(c, cref, sabs) -> np.ndarray:
-    """Per-element acceptance: |c - Cref| <= 2e-3 * Sabs + 2^-10 * |Cref|."""
+def bf16_half_ulp(x) -> np.ndarray:
+    """Half the spacing of bfloat16 values at |x| (8 significant bits)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
+def within_tolerance(c, cref, sabs, out: str = "f16") -> np.ndarray:
+    """Per-element acceptance: |c - Cref| <= 2e-3 * Sabs + 2^-10 * |Cref|.
+
+    The 2^-10 |Cref| term covers rounding the FP32 sum to an FP16 (or FP32)
+    output, whose half-spacing is at most 2^-11 |C|.  A BF16 output has 8
+    significant bits, so a correctly rounded BF16 result can sit up to 2^-8 |C|
+    from Cref; for out="bf16" that half-spacing is added to the bound."""
     c = np.asarray(c, dtype=np.float64)
-    return np.abs(c - cref) <= 2e-3 * sabs + (2.0 ** -10) * np.abs(cref)
+    bound = 2e-3 * sabs + (2.0 ** -10) * np.abs(cref)
+    if out == "bf16":
+        bound = bound + bf16_half_ulp(cref)
+    return np.abs(c - cref) <= bound

@@ -30,8 +30,11 @@ def upload(bits: np.ndarray, elem: str, pad_front: int = 0):
 
 def run(elem: str, M: int, N: int, K: int, a_bits, b_bits, trans_b: int, out: str = "same",
         schedule: int = mcs.GEMM_SCHED_AUTO, ldc: int | None = None, c_fill: float | None = None,
-        a_offset: int = 0, entry: str = "ex", return_raw: bool = False):
-    """C = A.B on the GPU through the C ABI; returns (C float64 M x N, raw C bits or None)."""
+        a_offset: int = 0, entry: str = "ex", return_raw: bool = False, allow_refusal: bool = False):
+    """C = A.B on the GPU through the C ABI; returns (C float64 M x N, raw C bits).
+
+    With allow_refusal, a GEMM_EINVAL answer (the requested schedule cannot
+    take these operands; nothing was launched) returns None instead."""
     torch = _torch()
     print(f"[gpu] {entry} elem={elem} M={M} N={N} K={K} trans_b={trans_b} out={out} "
           f"sched={schedule} ldc={ldc} a_off={a_offset}", flush=True)
@@ -54,6 +57,8 @@ def run(elem: str, M: int, N: int, K: int, a_bits, b_bits, trans_b: int, out: st
     else:
         fn = mcs.gemm_f16 if elem == "f16" else mcs.gemm_bf16
         st = fn(M, N, K, a_ptr, lda, B.data_ptr(), ldb, trans_b, C.data_ptr(), ldc, out_type, stream)
+    if allow_refusal and st == mcs.GEMM_EINVAL:
+        return None
     assert st == mcs.GEMM_OK, mcs.gemm_status_string(st)
     torch.cuda.synchronize()
     full = C.view(max(M, 1), ldc)
@@ -69,8 +74,9 @@ def run(elem: str, M: int, N: int, K: int, a_bits, b_bits, trans_b: int, out: st
     return vals[:M, :N], bits[:M, :N]
 
 
-def assert_within_tolerance(c, cref, sabs, what=""):
-    ok = oracle.within_tolerance(c, cref, sabs)
+def assert_within_tolerance(c, cref, sabs, what="", out="f16"):
+    """out: the output element type ("f16", "bf16" or "f32")."""
+    ok = oracle.within_tolerance(c, cref, sabs, out=out)
     if not ok.all():
         bad = np.argwhere(~ok)
         i, j = bad[0]

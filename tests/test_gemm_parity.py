@@ -44,7 +44,14 @@ def rup8(x):
 
 # ---- small and ragged shapes: every element --------------------------------
 
-SHAPES = [(256, 256, 256), (1, 1, 8), (17, 33, 8), (300, 520, 200), (513, 257, 72), (64, 640, 1000)]
+SHAPES = [(256, 256, 256), (1, 1, 8), (17, 33, 8), (300, 520, 200), (513, 257, 72), (64, 640, 1000),
+          (258, 130, 136)]
+
+
+def pipelined_eligible(N, K, trans_b):
+    """The documented conditions, given 16-byte aligned buffers and leading
+    dimensions that are multiples of 8: K % 8 == 0, and an even N when B is K x N."""
+    return K % 8 == 0 and (trans_b or N % 2 == 0)
 
 
 @pytest.mark.parametrize("sched", ["pipelined", "in_phase"])
@@ -56,11 +63,22 @@ def test_shapes_every_element(shape, elem, trans_b, out, sched):
     M, N, K = shape
     lda = rup8(K) + 8                      # padded rows, padding filled with NaN
     ldb = (rup8(K) + 8) if trans_b else (rup8(N) + 8)
+    ldc = rup8(N) + 8                      # padded output rows must stay untouched
     a, b = operands(elem, "uniform", M, N, K, trans_b, seed=100 + M + N + K, lda=lda, ldb=ldb,
                     nan_pad=True)
     cref, sabs = ref(a, b, elem, trans_b, K, N)
-    c, _ = run(elem, M, N, K, a, b, trans_b, out=out, schedule=SCHEDS[sched])
-    assert_within_tolerance(c, cref, sabs, f"{shape} {elem} tb={trans_b} {out} {sched}")
+    got = run(elem, M, N, K, a, b, trans_b, out=out, schedule=SCHEDS[sched], ldc=ldc, c_fill=-3.0,
+              return_raw=True, allow_refusal=True)
+    if got is None:
+        # refused before launch, as documented; the default schedule must still be right
+        assert not pipelined_eligible(N, K, trans_b)
+        got = run(elem, M, N, K, a, b, trans_b, out=out, ldc=ldc, c_fill=-3.0, return_raw=True)
+    else:
+        assert pipelined_eligible(N, K, trans_b)
+    c, _, full = got
+    assert_within_tolerance(c, cref, sabs, f"{shape} {elem} tb={trans_b} {out} {sched}",
+                            out=elem if out == "same" else "f32")
+    assert np.all(full[:, N:] == -3.0)
 
 
 @pytest.mark.parametrize("trans_b", [0, 1])
@@ -70,7 +88,7 @@ def test_generic_kernel_every_element(elem, trans_b):
     a, b = operands(elem, "normal", M, N, K, trans_b, seed=3)
     cref, sabs = ref(a, b, elem, trans_b, K, N)
     c, _ = run(elem, M, N, K, a, b, trans_b, schedule=mcs.GEMM_SCHED_AUTO)
-    assert_within_tolerance(c, cref, sabs, "generic")
+    assert_within_tolerance(c, cref, sabs, "generic", out=elem)
     c, _ = run(elem, M, N, K, a, b, trans_b, schedule=mcs.GEMM_SCHED_GENERIC, out="f32")
     assert_within_tolerance(c, cref, sabs, "generic f32")
 
@@ -162,11 +180,12 @@ def test_workload(name):
     c, _ = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, entry="abi")
     if w.M * w.N * w.K <= 2 ** 31:
         cref, sabs = oracle.gemm(a, b, w.dtype, w.trans_b)
-        assert_within_tolerance(c, cref, sabs, name)
+        assert_within_tolerance(c, cref, sabs, name, out=w.dtype if w.out == "same" else "f32")
     else:
         ii, jj = sample_points(w.M, w.N, 3000, seed=w.seed)
         cref, sabs = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
-        assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name)
+        assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name,
+                                out=w.dtype if w.out == "same" else "f32")
         # properties at every element: finite, and bounded by the operands
         assert np.isfinite(c).all()
 
@@ -223,7 +242,7 @@ def test_output_padding_untouched(elem):
     c, bits, full = run(elem, M, N, K, a, b, 1, ldc=ldc, c_fill=5.0, return_raw=True)
     assert np.all(full[:, N:] == 5.0)
     cref, sabs = ref(a, b, elem, 1, K, N)
-    assert_within_tolerance(c, cref, sabs, "ldc > N")
+    assert_within_tolerance(c, cref, sabs, "ldc > N", out=elem)
 
 
 def test_misaligned_operand_takes_generic_path_and_is_correct():

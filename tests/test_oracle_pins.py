@@ -31,6 +31,20 @@ def test_tolerance_formula():
     assert not oracle.within_tolerance(cref + 1.001 * lim, cref, sabs).any()
 
 
+def test_bf16_output_bound_admits_exactly_the_rounding():
+    """For a BF16 output the bound grows by half a BF16 spacing: a correctly
+    rounded value passes, the neighbour beyond it fails."""
+    import numpy as np
+    cref = np.array([-1.027321845293045, 300.7, 1e-3])
+    sabs = np.abs(cref)                       # same-sign sums: Sabs = |Cref|
+    r = oracle.decode(oracle.round_to(cref, "bf16"), "bf16")
+    assert oracle.within_tolerance(r, cref, sabs, out="bf16").all()
+    assert not oracle.within_tolerance(r, cref, sabs, out="f16")[0]
+    step = 2 * oracle.bf16_half_ulp(cref)
+    far = r + np.sign(r - cref) * step        # next bfloat16 away from Cref
+    assert not oracle.within_tolerance(far, cref, sabs, out="bf16").any()
+
+
 def test_rejects_bad_arguments():
     import numpy as np
     a = np.zeros((2, 3), np.uint16)
