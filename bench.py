@@ -99,8 +99,8 @@ def copy_calibration(mib: int) -> int:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS))
     ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "generic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -46,9 +46,10 @@
 //
 // Data layout.  LDS: two buffers of 64 KiB, each [A0 | A1 | B0 | B1] halves of
 // 16 KiB.  A half (and a B half when B is N x K) is 128 rows x 64 k, 128-byte
-// rows of eight 16-byte chunks stored at chunk ^ swz(row), swz(r) =
-// (r ^ (r >> 3)) & 7, so the 16 rows read together by ds_read_b128 fall in
-// distinct banks.  A B half when B is K x N is 64 k-rows x 128 n (256-byte
+// rows of eight 16-byte chunks stored at chunk ^ (row & 7).  With this XOR
+// the fragment reads (16 consecutive rows, one k-chunk per 16 lanes) show no
+// LDS bank conflicts on gfx950, where (r ^ (r >> 3)) & 7 showed two-way
+// conflicts (SQ_LDS_BANK_CONFLICT over SQ_LDS_IDX_ACTIVE measured per layout).  A B half when B is K x N is 64 k-rows x 128 n (256-byte
 // rows) with chunk ^ 2*((k & 3) + 4*((k >> 3) & 1)), read with the gfx950
 // transposing ds_read_b64_tr_b16 into the K-major MFMA operand.
 // Wave (wm, wn) = (wave & 3, wave >> 2) owns rows 32wm..32wm+31 of every A half
@@ -170,7 +171,7 @@ struct Pipeline {
         lds0 = 0;
 
         const int l16 = lane & 15, lg = lane >> 4;
-        const int swz = (lane & 7) ^ ((lane >> 3) & 1);
+        const int swz = lane & 7;                  // = row & 7 for the 16 rows of a read
         for (int ks = 0; ks < 2; ++ks) {
             rdA[ks] = (32 * wm + l16) * 128 + (((4 * ks) | lg) ^ swz) * 16;
             rdB[ks] = (64 * wn + l16) * 128 + (((4 * ks) | lg) ^ swz) * 16;
@@ -186,11 +187,12 @@ struct Pipeline {
                 rdBt[nt] = (8 * lg + (l16 >> 2)) * 256 + ((ch ^ fb) * 16) + 8 * (l16 & 1);
             }
         }
-        // copies: wave w moves 1-KiB pieces 2w and 2w+1 of every half
+        // copies: wave w moves 1-KiB pieces 2w and 2w+1 of every half; lane
+        // (x, pch) fills physical chunk pch of row 8*piece + x
         const int x = lane >> 3, pch = lane & 7;
         for (int i = 0; i < 2; ++i) {
             const int row = 16 * wave + 8 * i + x;            // row of the half
-            const int c = pch ^ x ^ i;                         // logical 16-byte k-chunk
+            const int c = pch ^ x;                             // logical 16-byte k-chunk (row & 7 = x)
             cpAchunk[i] = c;
             cpA[i] = static_cast<uint32_t>(row * p.lda * 2 + c * 16);
             if constexpr (kTransB)

@@ -1,0 +1,175 @@
+"""Turn rocprofv3 CSV output into the short summaries kept under profiles/.
+
+    python -m matrix_core_scheduling_amd.profiling stats DIR [--kernel SUBSTR]
+    python -m matrix_core_scheduling_amd.profiling counters DIR [DIR ...] [--kernel SUBSTR]
+    python -m matrix_core_scheduling_amd.profiling traffic --fetch DIR --write DIR
+           --copy-fetch DIR --copy-write DIR --copy-mib N --workload NAME [--update FILE]
+
+DIR is a rocprofv3 output directory written with --output-format csv.
+Counter rows come one per hardware instance; they are summed per dispatch
+and then averaged over the dispatches of the kernel.
+
+Derived figures (MI355X: 8 XCDs, 1024 SIMDs):
+  clock_GHz     = GRBM_GUI_ACTIVE / n_xcc / duration    (GRBM counts per XCD)
+  mfma_busy     = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / n_xcc * simds)
+  lds_conflict  = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+  HBM bytes     = counter KiB * 1024 * (known copy bytes / counter KiB of the copy)
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "gemm_pipelined.hip")
+
+
+def _one(d: str, pattern: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no {pattern} under {d}")
+    return hits[0]
+
+
+def agent(d: str) -> dict:
+    for r in csv.DictReader(open(_one(d, "*agent_info.csv"))):
+        if r.get("Name", "").startswith("gfx"):
+            return r
+    return {}
+
+
+def kernel_stats(d: str, kernel: str = "") -> list[dict]:
+    out = []
+    for r in csv.DictReader(open(_one(d, "*kernel_stats.csv"))):
+        if kernel in r["Name"]:
+            out.append({"name": r["Name"], "calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
+                        "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])})
+    return out
+
+
+def counters(dirs, kernel: str = "") -> dict:
+    """{kernel name: {counter: mean per dispatch, '_duration_ns': mean, '_dispatches': n}}"""
+    per = collections.defaultdict(float)
+    dur = {}
+    name = {}
+    for d in dirs:
+        for r in csv.DictReader(open(_one(d, "*counter_collection.csv"))):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            key = (d, int(r["Dispatch_Id"]))
+            per[(key, r["Counter_Name"])] += float(r["Counter_Value"])
+            dur[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            name[key] = r["Kernel_Name"]
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (key, c), v in per.items():
+        acc[name[key]][c].append(v)
+    durs = collections.defaultdict(list)
+    for key, ns in dur.items():
+        durs[name[key]].append(ns)
+    res = {}
+    for k, cs in acc.items():
+        res[k] = {c: sum(v) / len(v) for c, v in cs.items()}
+        res[k]["_duration_ns"] = sum(durs[k]) / len(durs[k])
+        res[k]["_dispatches"] = len(durs[k])
+    return res
+
+
+def derived(c: dict, n_xcc: int, simds: int) -> dict:
+    out = {}
+    ns = c.get("_duration_ns")
+    if "GRBM_GUI_ACTIVE" in c and ns:
+        cyc = c["GRBM_GUI_ACTIVE"] / n_xcc
+        out["clock_GHz"] = cyc / ns
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            out["mfma_busy"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds)
+    if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
+        out["lds_conflict_ratio"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+    if "SQ_INSTS_VALU_MFMA_MOPS_F16" in c:
+        out["mfma_flop"] = c["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
+        out["mfma_flop_bf16"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    return out
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, kernel="gemm_pipelined",
+            copy_kernel="copyBuffer") -> dict:
+    copy_bytes = copy_mib * 2 ** 20
+    cf = counters([copy_fetch_dir], copy_kernel)
+    cw = counters([copy_write_dir], copy_kernel)
+    if not cf or not cw:
+        raise RuntimeError("copy kernel not found in the calibration runs")
+    fetch_kib_copy = next(iter(cf.values()))["FETCH_SIZE"]
+    write_kib_copy = next(iter(cw.values()))["WRITE_SIZE"]
+    f_scale = copy_bytes / (fetch_kib_copy * 1024)
+    w_scale = copy_bytes / (write_kib_copy * 1024)
+    g_f = next(iter(counters([fetch_dir], kernel).values()))
+    g_w = next(iter(counters([write_dir], kernel).values()))
+    fetch = g_f["FETCH_SIZE"] * 1024 * f_scale
+    write = g_w["WRITE_SIZE"] * 1024 * w_scale
+    return {"fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+            "hbm_bytes_per_launch": round(fetch + write), "fetch_scale": round(f_scale, 5),
+            "write_scale": round(w_scale, 5), "copy_calibration_mib": copy_mib,
+            "kernel_source_sha256": kernel_source_hash()}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--kernel", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", default="")
+    t = sub.add_parser("traffic")
+    for f in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + f.replace("_", "-"), required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--update", default=None, help="JSON file to add the result to")
+    a = ap.parse_args(argv)
+
+    if a.cmd == "stats":
+        print("| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|")
+        for k in kernel_stats(a.dir, a.kernel):
+            print(f"| `{k['name']}` | {k['calls']} | {k['avg_ns'] / 1e3:.2f} | {k['min_ns'] / 1e3:.2f} | "
+                  f"{k['max_ns'] / 1e3:.2f} |")
+    elif a.cmd == "counters":
+        ag = agent(a.dirs[0])
+        n_xcc, simds = int(ag.get("Num_Xcc", 8)), int(ag.get("Simd_Count", 1024))
+        for k, cs in counters(a.dirs, a.kernel).items():
+            print(f"kernel: `{k}` ({cs['_dispatches']} dispatches, mean duration "
+                  f"{cs['_duration_ns'] / 1e3:.2f} us under counter collection)\n")
+            print("| counter | mean per dispatch |\n|---|---|")
+            for n, v in sorted(cs.items()):
+                if not n.startswith("_"):
+                    print(f"| {n} | {v:.6g} |")
+            for n, v in derived(cs, n_xcc, simds).items():
+                print(f"| (derived) {n} | {v:.6g} |")
+            print()
+    elif a.cmd == "traffic":
+        r = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib)
+        print(json.dumps(r, indent=1))
+        if a.update:
+            data = {}
+            if os.path.exists(a.update):
+                data = json.load(open(a.update))
+            data[a.workload] = r
+            with open(a.update, "w") as f:
+                json.dump(data, f, indent=1, sort_keys=True)
+                f.write("\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
