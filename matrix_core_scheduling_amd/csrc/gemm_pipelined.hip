@@ -34,10 +34,13 @@
 //
 // Schedule of K-step t (cur = buffer of t, nxt = buffer of t+1); aX/bX are
 // the A rows / B columns of half X; reads fill registers for later stages:
-//     S0 MFMA Q00 (a0 b0)      S1 mem: copy b0[cur]<-t+2, read b1[cur]
-//     S2 MFMA Q01 (a0 b1)      S3 mem: copy b1[cur]<-t+2, read a1[cur]
-//     S4 MFMA Q10 (a1 b0)      S5 mem: copy a1[cur]<-t+2, read a0[nxt]
-//     S6 MFMA Q11 (a1 b1)      S7 mem: copy a0[nxt]<-t+3, read b0[nxt]
+//     S0 MFMA Q00 (a0 b0)      S1 mem: read b1[cur], copy b0[cur]<-t+2
+//     S2 MFMA Q01 (a0 b1)      S3 mem: read a1[cur], copy b1[cur]<-t+2
+//     S4 MFMA Q10 (a1 b0)      S5 mem: read a0[nxt], copy a1[cur]<-t+2
+//     S6 MFMA Q11 (a1 b1)      S7 mem: read b0[nxt], copy a0[nxt]<-t+3
+// The LDS reads open each memory stage so that their latency overlaps the
+// address and descriptor work of the copies: the memory stage, not the
+// MFMA stage, bounds each interval between two rendezvous.
 // Each memory stage issues two copies per wave; the half each stage must wait
 // for was issued six memory stages earlier, so every memory stage ends with
 // vmcnt(12).  Copies of K-steps past the end use an empty buffer window, so
@@ -374,32 +377,32 @@ gemm_pipelined_kernel(GemmParams p) {
             rendezvous();
             // S1
             mem_stage_begin();
-            pl.copy_b(s + 2, cur, 0);
             pl.read_b(b1, cur, 1);
+            pl.copy_b(s + 2, cur, 0);
             mem_stage_end();
             // S2
             quadrant<kBF16>(acc[0][1], a0, b1);
             rendezvous();
             // S3
             mem_stage_begin();
-            pl.copy_b(s + 2, cur, 1);
             pl.read_a(a1, cur, 1);
+            pl.copy_b(s + 2, cur, 1);
             mem_stage_end();
             // S4
             quadrant<kBF16>(acc[1][0], a1, b0);
             rendezvous();
             // S5
             mem_stage_begin();
-            pl.copy_a(s + 2, cur, 1);
             pl.read_a(a0, nxt, 0);
+            pl.copy_a(s + 2, cur, 1);
             mem_stage_end();
             // S6
             quadrant<kBF16>(acc[1][1], a1, b1);
             rendezvous();
             // S7
             mem_stage_begin();
-            pl.copy_a(s + 3, nxt, 0);
             pl.read_b(b0, nxt, 0);
+            pl.copy_a(s + 3, nxt, 0);
             mem_stage_end();
         }
     }
