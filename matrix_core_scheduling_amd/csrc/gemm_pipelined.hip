@@ -33,19 +33,27 @@
 //     stage later than an in-phase schedule would allow because group B lags.
 //
 // Schedule of K-step t (cur = buffer of t, nxt = buffer of t+1); aX/bX are
-// the A rows / B columns of half X; reads fill registers for later stages:
+// the A rows / B columns of half X; reads fill registers for later stages.
+// B given N x K, fragments read one stage ahead:
 //     S0 MFMA Q00 (a0 b0)      S1 mem: read b1[cur], copy b0[cur]<-t+2
 //     S2 MFMA Q01 (a0 b1)      S3 mem: read a1[cur], copy b1[cur]<-t+2
 //     S4 MFMA Q10 (a1 b0)      S5 mem: read a0[nxt], copy a1[cur]<-t+2
 //     S6 MFMA Q11 (a1 b1)      S7 mem: read b0[nxt], copy a0[nxt]<-t+3
+// Each memory stage ends with vmcnt(12) lgkmcnt(0): the half read two stages
+// later was copied six memory stages (twelve copies) earlier, and a half is
+// refilled two stages after its last read.
+// B given K x N, fragments read two stages ahead (same copies):
+//     S1 read a1[cur]   S3 read a0[nxt]   S5 read b0[nxt]   S7 read b1[nxt]
+// Memory stages end with vmcnt(10); each MFMA stage ends with lgkmcnt(0),
+// completing the reads of the memory stage before it; a half is refilled
+// four stages after its last read.  This variant holds one more fragment set
+// (96 instead of 80 VGPRs) but frees the memory stage from waiting for LDS,
+// and it is the one the transposed reads fit without spilling.
 // The LDS reads open each memory stage so that their latency overlaps the
-// address and descriptor work of the copies: the memory stage, not the
-// MFMA stage, bounds each interval between two rendezvous.
-// Each memory stage issues two copies per wave; the half each stage must wait
-// for was issued six memory stages earlier, so every memory stage ends with
-// vmcnt(12).  Copies of K-steps past the end use an empty buffer window, so
-// they write zeros (buffer loads outside the window return zero), which keeps
-// every stage identical; an odd K-step count is padded with one zero step.
+// address and descriptor work of the copies.  Copies of K-steps past the end
+// use an empty buffer window, so they write zeros (buffer loads outside the
+// window return zero), which keeps every stage identical; an odd K-step
+// count is padded with one zero step.
 //
 // Data layout.  LDS: two buffers of 64 KiB, each [A0 | A1 | B0 | B1] halves of
 // 16 KiB.  A half (and a B half when B is N x K) is 128 rows x 64 k, 128-byte
@@ -58,7 +66,9 @@
 // Wave (wm, wn) = (wave & 3, wave >> 2) owns rows 32wm..32wm+31 of every A half
 // and columns 64wn..64wn+63 of every B half: a 32x64 block of each quadrant.
 // MFMA: v_mfma_f32_16x16x32_{f16,bf16} with the B fragment as the first
-// operand, so each lane ends with four consecutive columns of one row.
+// operand, so each lane ends with four consecutive columns of one row; for a
+// 16-bit output, lanes l and l^16 trade halves of two neighbouring tiles so
+// every lane stores eight consecutive columns (16 bytes).
 #include "internal.h"
 
 namespace mcs {
@@ -70,6 +80,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -80,7 +91,11 @@ constexpr uint32_t kHalf = 16384;          // bytes of one operand half in LDS
 constexpr uint32_t kBuf = 4 * kHalf;       // one K-step: A0 A1 B0 B1
 constexpr uint32_t kOffA = 0, kOffB = 2 * kHalf;
 constexpr uint32_t kOutOfWindow = 0x80000000u;  // >= every buffer window used here
-constexpr int kCopyWait = 12;              // vmcnt at the end of each memory stage
+// Fragment reads run one stage ahead of their MFMA stage when B is given
+// N x K and two stages ahead when B is given K x N (whose transposed reads
+// spill at one stage ahead); the copy wait follows from that (see below).
+template <bool kTransB> constexpr int kReadAhead = kTransB ? 1 : 2;
+template <bool kTransB> constexpr int kCopyWait = kTransB ? 12 : 10;
 
 // ---- instruction helpers -----------------------------------------------
 
@@ -163,6 +178,12 @@ struct Pipeline {
     int wave;
     const GemmParams &p;
     int m0, n0;
+    // per-half copy windows (uniform; computed once): first row (A, or B given
+    // N x K) or first column (B given K x N) of the half, the window's bytes
+    // before the k-extent, and whether the half holds any valid row/column
+    const uint16_t *aRow[2], *bBase[2];
+    uint32_t aSpan[2], bSpan[2];
+    bool aLive[2], bLive[2];
 
     __device__ __forceinline__ Pipeline(const GemmParams &prm, int tm, int tn) : p(prm) {
         const int tid = threadIdx.x;
@@ -172,6 +193,21 @@ struct Pipeline {
         m0 = tm * kTileM;
         n0 = tn * kTileN;
         lds0 = 0;
+        for (int h = 0; h < 2; ++h) {
+            const int rows = min(max(p.M - (m0 + 128 * h), 0), 128);
+            aLive[h] = rows > 0;
+            aRow[h] = p.A + (int64_t)(m0 + 128 * h) * p.lda;
+            aSpan[h] = rows > 0 ? static_cast<uint32_t>((rows - 1) * p.lda * 2) : 0u;
+            const int cols = min(max(p.N - (n0 + 128 * h), 0), 128);
+            bLive[h] = cols > 0;
+            if constexpr (kTransB) {
+                bBase[h] = p.B + (int64_t)(n0 + 128 * h) * p.ldb;
+                bSpan[h] = cols > 0 ? static_cast<uint32_t>((cols - 1) * p.ldb * 2) : 0u;
+            } else {
+                bBase[h] = p.B + n0 + 128 * h;
+                bSpan[h] = static_cast<uint32_t>(cols * 2);
+            }
+        }
 
         const int l16 = lane & 15, lg = lane >> 4;
         const int swz = lane & 7;                  // = row & 7 for the 16 rows of a read
@@ -213,14 +249,12 @@ struct Pipeline {
     }
 
     // Copy half h of operand A (rows m0+128h..) for K-step s into buffer `buf`.
+    // The window ends at the last valid byte of the half's last valid row, so
+    // rows >= M and every k >= K (steps past the end: an empty window) read 0.
     __device__ __forceinline__ void copy_a(int s, uint32_t buf, int h) const {
-        const int k0 = s * kTileK;
-        const int kv = p.K - k0;                               // k left (may be <= 0)
-        const int r0 = m0 + 128 * h;
-        const int rows = min(max(p.M - r0, 0), 128);
-        const uint32_t nrec = (kv > 0 && rows > 0)
-            ? static_cast<uint32_t>(((int64_t)(rows - 1) * p.lda + kv) * 2) : 0u;
-        const i32x4 rs = make_rsrc(p.A + (int64_t)r0 * p.lda + k0, nrec);
+        const int kv = p.K - s * kTileK;                      // k left (may be <= 0)
+        const uint32_t nrec = (aLive[h] && kv > 0) ? aSpan[h] + 2u * static_cast<uint32_t>(kv) : 0u;
+        const i32x4 rs = make_rsrc(aRow[h] + s * kTileK, nrec);
         const uint32_t dst = lds0 + buf + kOffA + h * kHalf + 2 * wave * 1024;
         for (int i = 0; i < 2; ++i) {
             const uint32_t v = (cpAchunk[i] * 8 < kv) ? cpA[i] : kOutOfWindow;
@@ -230,24 +264,22 @@ struct Pipeline {
 
     // Copy half h of operand B (columns n0+128h..) for K-step s into buffer `buf`.
     __device__ __forceinline__ void copy_b(int s, uint32_t buf, int h) const {
-        const int k0 = s * kTileK;
-        const int kv = p.K - k0;
-        const int c0 = n0 + 128 * h;
-        const int cols = min(max(p.N - c0, 0), 128);
+        const int kv = p.K - s * kTileK;
         const uint32_t dst = lds0 + buf + kOffB + h * kHalf + 2 * wave * 1024;
         if constexpr (kTransB) {
-            const uint32_t nrec = (kv > 0 && cols > 0)
-                ? static_cast<uint32_t>(((int64_t)(cols - 1) * p.ldb + kv) * 2) : 0u;
-            const i32x4 rs = make_rsrc(p.B + (int64_t)c0 * p.ldb + k0, nrec);
+            const uint32_t nrec = (bLive[h] && kv > 0) ? bSpan[h] + 2u * static_cast<uint32_t>(kv) : 0u;
+            const i32x4 rs = make_rsrc(bBase[h] + s * kTileK, nrec);
             for (int i = 0; i < 2; ++i) {
                 const uint32_t v = (cpAchunk[i] * 8 < kv) ? cpB[i] : kOutOfWindow;
                 copy16(rs, dst + i * 1024, v);
             }
         } else {
+            // k-rows k0 .. k0+rows-1; the window ends at the last valid column
+            // of the last valid k-row
             const int rows = min(kv, kTileK);
-            const uint32_t nrec = (rows > 0 && cols > 0)
-                ? static_cast<uint32_t>(((int64_t)(rows - 1) * p.ldb + cols) * 2) : 0u;
-            const i32x4 rs = make_rsrc(p.B + (int64_t)k0 * p.ldb + c0, nrec);
+            const uint32_t nrec = (bLive[h] && kv > 0)
+                ? static_cast<uint32_t>(rows - 1) * static_cast<uint32_t>(p.ldb * 2) + bSpan[h] : 0u;
+            const i32x4 rs = make_rsrc(bBase[h] + (int64_t)s * kTileK * p.ldb, nrec);
             for (int i = 0; i < 2; ++i) {
                 const uint32_t v = (cpBrow[i] < kv) ? cpB[i] : kOutOfWindow;
                 copy16(rs, dst + i * 1024, v);
@@ -290,11 +322,27 @@ __device__ __forceinline__ void quadrant(f32x4 (&acc)[2][4], const i32x4 (&a)[2]
 
 __device__ __forceinline__ void mem_stage_begin() { __builtin_amdgcn_s_setprio(1); }
 
+// End of a memory stage: this wave's copies for the reads two stages later
+// have landed; with reads one stage ahead, so have its own LDS reads (their
+// registers feed the next stage and their half may be refilled two stages on).
+template <bool kTransB>
 __device__ __forceinline__ void mem_stage_end() {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kCopyWait>();
-    wait_lgkmcnt<0>();
+    wait_vmcnt<kCopyWait<kTransB>>();
+    if constexpr (kReadAhead<kTransB> == 1) wait_lgkmcnt<0>();
     __builtin_amdgcn_s_setprio(0);
+    rendezvous();
+}
+
+// End of an MFMA stage: with reads two stages ahead, the LDS reads the
+// preceding memory stage issued complete here, before the rendezvous after
+// which the other group may refill (three or more stages after the read).
+template <bool kTransB>
+__device__ __forceinline__ void mfma_stage_end() {
+    if constexpr (kReadAhead<kTransB> == 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkmcnt<0>();
+    }
     rendezvous();
 }
 
@@ -348,17 +396,19 @@ gemm_pipelined_kernel(GemmParams p) {
     pl.copy_b(1, kBuf, 0);
     pl.copy_b(1, kBuf, 1);
     pl.copy_a(1, kBuf, 1);
+    constexpr int kWait = kCopyWait<kTransB>;
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kCopyWait>();            // a0(0), b0(0) landed (this wave's part)
+    wait_vmcnt<kWait>();                // a0(0), b0(0) (and b1(0)) landed: this wave's part
     rendezvous();                       // ... and every wave's part
     pl.read_a(a0, 0, 0);
     pl.read_b(b0, 0, 0);
+    if constexpr (kReadAhead<kTransB> == 2) pl.read_b(b1, 0, 1);
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt<0>();
     rendezvous();                       // every wave has read a0[0]
     pl.copy_a(2, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kCopyWait>();            // b1(0) landed
+    wait_vmcnt<kWait>();                // b1(0) (or a1(0)) landed
     rendezvous();
 
     if constexpr (kOffset) {
@@ -372,38 +422,39 @@ gemm_pipelined_kernel(GemmParams p) {
         for (int u = 0; u < 2; ++u) {
             const uint32_t cur = u ? kBuf : 0u, nxt = u ? 0u : kBuf;
             const int s = t + u;
+            constexpr bool k1 = kReadAhead<kTransB> == 1;
             // S0
             quadrant<kBF16>(acc[0][0], a0, b0);
-            rendezvous();
+            mfma_stage_end<kTransB>();
             // S1
             mem_stage_begin();
-            pl.read_b(b1, cur, 1);
+            if constexpr (k1) pl.read_b(b1, cur, 1); else pl.read_a(a1, cur, 1);
             pl.copy_b(s + 2, cur, 0);
-            mem_stage_end();
+            mem_stage_end<kTransB>();
             // S2
             quadrant<kBF16>(acc[0][1], a0, b1);
-            rendezvous();
+            mfma_stage_end<kTransB>();
             // S3
             mem_stage_begin();
-            pl.read_a(a1, cur, 1);
+            if constexpr (k1) pl.read_a(a1, cur, 1); else pl.read_a(a0, nxt, 0);
             pl.copy_b(s + 2, cur, 1);
-            mem_stage_end();
+            mem_stage_end<kTransB>();
             // S4
             quadrant<kBF16>(acc[1][0], a1, b0);
-            rendezvous();
+            mfma_stage_end<kTransB>();
             // S5
             mem_stage_begin();
-            pl.read_a(a0, nxt, 0);
+            if constexpr (k1) pl.read_a(a0, nxt, 0); else pl.read_b(b0, nxt, 0);
             pl.copy_a(s + 2, cur, 1);
-            mem_stage_end();
+            mem_stage_end<kTransB>();
             // S6
             quadrant<kBF16>(acc[1][1], a1, b1);
-            rendezvous();
+            mfma_stage_end<kTransB>();
             // S7
             mem_stage_begin();
-            pl.read_b(b0, nxt, 0);
+            if constexpr (k1) pl.read_b(b0, nxt, 0); else pl.read_b(b1, nxt, 1);
             pl.copy_a(s + 3, nxt, 0);
-            mem_stage_end();
+            mem_stage_end<kTransB>();
         }
     }
 
@@ -419,15 +470,17 @@ gemm_pipelined_kernel(GemmParams p) {
     // the loop.
     const int lane = __lane_id();
     const int wm = wave & 3, wn = wave >> 2;
+    const int g = lane >> 4;
     for (int qa = 0; qa < 2; ++qa)
         for (int mt = 0; mt < 2; ++mt) {
             const int row = pl.m0 + 128 * qa + 32 * wm + 16 * mt + (lane & 15);
             if (row >= p.M) continue;
-            for (int qb = 0; qb < 2; ++qb)
-                for (int nt = 0; nt < 4; ++nt) {
-                    const int col = pl.n0 + 128 * qb + 64 * wn + 16 * nt + 4 * (lane >> 4);
-                    const f32x4 v = acc[qa][qb][mt][nt];
-                    if constexpr (kOutF32) {
+            for (int qb = 0; qb < 2; ++qb) {
+                const int col0 = pl.n0 + 128 * qb + 64 * wn;
+                if constexpr (kOutF32) {
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const int col = col0 + 16 * nt + 4 * g;
+                        const f32x4 v = acc[qa][qb][mt][nt];
                         float *c = reinterpret_cast<float *>(p.C) + (int64_t)row * p.ldc + col;
                         if (col + 4 <= p.N) {
                             *reinterpret_cast<f32x4 *>(c) = v;
@@ -435,25 +488,38 @@ gemm_pipelined_kernel(GemmParams p) {
                             for (int r = 0; r < 4; ++r)
                                 if (col + r < p.N) c[r] = v[r];
                         }
-                    } else {
-                        uint16_t *c = reinterpret_cast<uint16_t *>(p.C) + (int64_t)row * p.ldc + col;
-                        i32x2 packed;
+                    }
+                } else {
+                    // Tiles nt and nt+1: lanes g and g^1 trade four values so
+                    // each lane holds eight consecutive columns (16 bytes).
+                    for (int nt = 0; nt < 4; nt += 2) {
+                        i32x2 h0, h1;
                         if constexpr (kBF16) {
-                            bf16x4 h = __builtin_convertvector(v, bf16x4);
-                            packed = __builtin_bit_cast(i32x2, h);
+                            h0 = __builtin_bit_cast(i32x2, __builtin_convertvector(acc[qa][qb][mt][nt], bf16x4));
+                            h1 = __builtin_bit_cast(i32x2, __builtin_convertvector(acc[qa][qb][mt][nt + 1], bf16x4));
                         } else {
-                            f16x4 h = __builtin_convertvector(v, f16x4);
-                            packed = __builtin_bit_cast(i32x2, h);
+                            h0 = __builtin_bit_cast(i32x2, __builtin_convertvector(acc[qa][qb][mt][nt], f16x4));
+                            h1 = __builtin_bit_cast(i32x2, __builtin_convertvector(acc[qa][qb][mt][nt + 1], f16x4));
                         }
-                        if (col + 4 <= p.N) {
-                            *reinterpret_cast<i32x2 *>(c) = packed;
+                        const bool odd = g & 1;
+                        const i32x2 send = odd ? h0 : h1;
+                        i32x2 recv;
+                        recv.x = __shfl_xor(send.x, 16);
+                        recv.y = __shfl_xor(send.y, 16);
+                        const i32x4 out = odd ? i32x4{recv.x, recv.y, h1.x, h1.y}
+                                              : i32x4{h0.x, h0.y, recv.x, recv.y};
+                        const int col = col0 + 16 * nt + (odd ? 16 + 4 * (g - 1) : 4 * g);
+                        uint16_t *c = reinterpret_cast<uint16_t *>(p.C) + (int64_t)row * p.ldc + col;
+                        if (col + 8 <= p.N) {
+                            *reinterpret_cast<i32x4 *>(c) = out;
                         } else {
-                            const i16x4 e = __builtin_bit_cast(i16x4, packed);
-                            for (int r = 0; r < 4; ++r)
+                            const i16x8 e = __builtin_bit_cast(i16x8, out);
+                            for (int r = 0; r < 8; ++r)
                                 if (col + r < p.N) c[r] = static_cast<uint16_t>(e[r]);
                         }
                     }
                 }
+            }
         }
 }
 
