@@ -11,13 +11,18 @@
 // while the other reads LDS, issues copies and computes addresses.
 //
 // gfx950 layout (section "MI350 Series (gfx950, CDNA 4): Three Overlapping
-// Flows", Figure 7): a 256x256 output tile is four 128x128 quadrants; each
-// quadrant has one MFMA stage and one memory stage, giving eight stages per
-// 64-deep K-step and sixteen per iteration of the loop, which is unrolled
-// twice so each LDS buffer is addressed statically.  Copies of future tiles
-// go straight from global memory into LDS (buffer_load ... lds), the operand
-// halves are double buffered, and three flows overlap: copies of a future
-// K-step, LDS reads for the next quadrant, and MFMA on the current one.
+// Flows", Figure 7): a 256x256 output tile is four 128x128 quadrants.  The
+// pages give each quadrant its own MFMA stage and memory stage (eight stages
+// per 64-deep K-step); here two quadrants share a stage, four stages per
+// K-step, because each rendezvous costs the MFMA pipe ~75 cycles (measured
+// with the memory work removed) and 16 MFMAs (256 cycles) were too little
+// work to cover it ("Stage Size and Register Pressure": stages must hold
+// enough matrix work to cover preparation without excessive barrier
+// overhead).  The loop is unrolled twice so each LDS buffer is addressed
+// statically.  Copies of future tiles go straight from global memory into
+// LDS (buffer_load ... lds), the operand halves are double buffered, and
+// three flows overlap: copies of a future K-step, LDS reads for the next
+// stage, and MFMA on the current one.
 //
 // Stage boundary (section "What Lands in the Instruction Stream"):
 //     [s_waitcnt only where a dependency needs it] sched_barrier s_barrier sched_barrier
@@ -33,22 +38,17 @@
 //     stage later than an in-phase schedule would allow because group B lags.
 //
 // Schedule of K-step t (cur = buffer of t, nxt = buffer of t+1); aX/bX are
-// the A rows / B columns of half X; reads fill registers for later stages.
-// B given N x K, fragments read one stage ahead:
-//     S0 MFMA Q00 (a0 b0)      S1 mem: read b1[cur], copy b0[cur]<-t+2
-//     S2 MFMA Q01 (a0 b1)      S3 mem: read a1[cur], copy b1[cur]<-t+2
-//     S4 MFMA Q10 (a1 b0)      S5 mem: read a0[nxt], copy a1[cur]<-t+2
-//     S6 MFMA Q11 (a1 b1)      S7 mem: read b0[nxt], copy a0[nxt]<-t+3
-// Each memory stage ends with vmcnt(12) lgkmcnt(0): the half read two stages
-// later was copied six memory stages (twelve copies) earlier, and a half is
-// refilled two stages after its last read.
-// B given K x N, fragments read two stages ahead (same copies):
-//     S1 read a1[cur]   S3 read a0[nxt]   S5 read b0[nxt]   S7 read b1[nxt]
-// Memory stages end with vmcnt(10); each MFMA stage ends with lgkmcnt(0),
-// completing the reads of the memory stage before it; a half is refilled
-// four stages after its last read.  This variant holds one more fragment set
-// (96 instead of 80 VGPRs) but frees the memory stage from waiting for LDS,
-// and it is the one the transposed reads fit without spilling.
+// the A rows / B columns of half X; reads fill registers for the next stage:
+//     S0 MFMA Q00 + Q10 (a0 a1 . b0)
+//     S1 mem: read b1[cur];          copy a0, a1, b0 [cur] <- t+2
+//     S2 MFMA Q01 + Q11 (a0 a1 . b1)
+//     S3 mem: read a0, a1, b0 [nxt];  copy b1[cur] <- t+2
+// Every refill comes two stages after the last read of its half (a0/a1/b0
+// of step t are read in S3 of step t-1, b1 in S1).  Each half read in stage
+// R was copied with eight copies of this wave issued after it by the end of
+// stage R-2 (S1 copies six, S3 two), so both memory stages end with
+// vmcnt(8) lgkmcnt(0); every copy has a full K-step to land.  At most 64
+// fragment VGPRs are live (a0 a1 b0 b1 is 16+16+32+32, never all four).
 // The LDS reads open each memory stage so that their latency overlaps the
 // address and descriptor work of the copies.  Copies of K-steps past the end
 // use an empty buffer window, so they write zeros (buffer loads outside the
@@ -91,11 +91,7 @@ constexpr uint32_t kHalf = 16384;          // bytes of one operand half in LDS
 constexpr uint32_t kBuf = 4 * kHalf;       // one K-step: A0 A1 B0 B1
 constexpr uint32_t kOffA = 0, kOffB = 2 * kHalf;
 constexpr uint32_t kOutOfWindow = 0x80000000u;  // >= every buffer window used here
-// Fragment reads run one stage ahead of their MFMA stage when B is given
-// N x K and two stages ahead when B is given K x N (whose transposed reads
-// spill at one stage ahead); the copy wait follows from that (see below).
-template <bool kTransB> constexpr int kReadAhead = kTransB ? 1 : 2;
-template <bool kTransB> constexpr int kCopyWait = kTransB ? 12 : 10;
+constexpr int kCopyWait = 8;               // vmcnt at the end of each memory stage
 
 // ---- instruction helpers -----------------------------------------------
 
@@ -135,6 +131,13 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_record
 // Issued from inline assembly so the compiler neither reorders it nor adds
 // waits of its own: the schedule's explicit vmcnt waits cover it.
 __device__ __forceinline__ void copy16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+    // Both values are wave-uniform by construction; readfirstlane states it so
+    // the "s" operands always land in SGPRs (it folds away for SGPR values).
+    rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+    rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+    rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+    rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
@@ -323,26 +326,13 @@ __device__ __forceinline__ void quadrant(f32x4 (&acc)[2][4], const i32x4 (&a)[2]
 __device__ __forceinline__ void mem_stage_begin() { __builtin_amdgcn_s_setprio(1); }
 
 // End of a memory stage: this wave's copies for the reads two stages later
-// have landed; with reads one stage ahead, so have its own LDS reads (their
-// registers feed the next stage and their half may be refilled two stages on).
-template <bool kTransB>
+// have landed, and so have its own LDS reads (their registers feed the next
+// stage and their half may be refilled two stages on).
 __device__ __forceinline__ void mem_stage_end() {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kCopyWait<kTransB>>();
-    if constexpr (kReadAhead<kTransB> == 1) wait_lgkmcnt<0>();
+    wait_vmcnt<kCopyWait>();
+    wait_lgkmcnt<0>();
     __builtin_amdgcn_s_setprio(0);
-    rendezvous();
-}
-
-// End of an MFMA stage: with reads two stages ahead, the LDS reads the
-// preceding memory stage issued complete here, before the rendezvous after
-// which the other group may refill (three or more stages after the read).
-template <bool kTransB>
-__device__ __forceinline__ void mfma_stage_end() {
-    if constexpr (kReadAhead<kTransB> == 2) {
-        __builtin_amdgcn_sched_barrier(0);
-        wait_lgkmcnt<0>();
-    }
     rendezvous();
 }
 
@@ -386,29 +376,25 @@ gemm_pipelined_kernel(GemmParams p) {
                     acc[qa][qb][mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     i32x4 a0[2][2], a1[2][2], b0[4][2], b1[4][2];
 
-    // ---- prologue: the copy stream of steps 0 and 1 in steady-state order,
-    // then the first fragments, then the refill of a0 that S7 would issue.
+    // ---- prologue: the copy stream of steps 0 and 1 in steady-state order
+    // (a0 a1 b0, then b1, per step), then the fragments S0 of step 0 needs.
     pl.copy_a(0, 0, 0);
+    pl.copy_a(0, 0, 1);
     pl.copy_b(0, 0, 0);
     pl.copy_b(0, 0, 1);
-    pl.copy_a(0, 0, 1);
     pl.copy_a(1, kBuf, 0);
+    pl.copy_a(1, kBuf, 1);
     pl.copy_b(1, kBuf, 0);
     pl.copy_b(1, kBuf, 1);
-    pl.copy_a(1, kBuf, 1);
-    constexpr int kWait = kCopyWait<kTransB>;
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kWait>();                // a0(0), b0(0) (and b1(0)) landed: this wave's part
+    wait_vmcnt<10>();                   // a0(0) a1(0) b0(0) landed (this wave's part)
     rendezvous();                       // ... and every wave's part
     pl.read_a(a0, 0, 0);
+    pl.read_a(a1, 0, 1);
     pl.read_b(b0, 0, 0);
-    if constexpr (kReadAhead<kTransB> == 2) pl.read_b(b1, 0, 1);
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt<0>();
-    rendezvous();                       // every wave has read a0[0]
-    pl.copy_a(2, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kWait>();                // b1(0) (or a1(0)) landed
+    wait_vmcnt<kCopyWait>();            // b1(0) landed: the state at the end of S3 of step -1
     rendezvous();
 
     if constexpr (kOffset) {
@@ -422,39 +408,28 @@ gemm_pipelined_kernel(GemmParams p) {
         for (int u = 0; u < 2; ++u) {
             const uint32_t cur = u ? kBuf : 0u, nxt = u ? 0u : kBuf;
             const int s = t + u;
-            constexpr bool k1 = kReadAhead<kTransB> == 1;
-            // S0
+            // S0: quadrants Q00 and Q10
             quadrant<kBF16>(acc[0][0], a0, b0);
-            mfma_stage_end<kTransB>();
+            quadrant<kBF16>(acc[1][0], a1, b0);
+            rendezvous();
             // S1
             mem_stage_begin();
-            if constexpr (k1) pl.read_b(b1, cur, 1); else pl.read_a(a1, cur, 1);
+            pl.read_b(b1, cur, 1);
+            pl.copy_a(s + 2, cur, 0);
+            pl.copy_a(s + 2, cur, 1);
             pl.copy_b(s + 2, cur, 0);
-            mem_stage_end<kTransB>();
-            // S2
+            mem_stage_end();
+            // S2: quadrants Q01 and Q11
             quadrant<kBF16>(acc[0][1], a0, b1);
-            mfma_stage_end<kTransB>();
+            quadrant<kBF16>(acc[1][1], a1, b1);
+            rendezvous();
             // S3
             mem_stage_begin();
-            if constexpr (k1) pl.read_a(a1, cur, 1); else pl.read_a(a0, nxt, 0);
+            pl.read_a(a0, nxt, 0);
+            pl.read_a(a1, nxt, 1);
+            pl.read_b(b0, nxt, 0);
             pl.copy_b(s + 2, cur, 1);
-            mem_stage_end<kTransB>();
-            // S4
-            quadrant<kBF16>(acc[1][0], a1, b0);
-            mfma_stage_end<kTransB>();
-            // S5
-            mem_stage_begin();
-            if constexpr (k1) pl.read_a(a0, nxt, 0); else pl.read_b(b0, nxt, 0);
-            pl.copy_a(s + 2, cur, 1);
-            mem_stage_end<kTransB>();
-            // S6
-            quadrant<kBF16>(acc[1][1], a1, b1);
-            mfma_stage_end<kTransB>();
-            // S7
-            mem_stage_begin();
-            if constexpr (k1) pl.read_b(b0, nxt, 0); else pl.read_b(b1, nxt, 1);
-            pl.copy_a(s + 3, nxt, 0);
-            mem_stage_end<kTransB>();
+            mem_stage_end();
         }
     }
 
