@@ -19,7 +19,6 @@ result on those rows is checked against it.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -41,23 +40,20 @@ PEAK_TFLOPS_UNITS = 256 * 4 * 1024 * 2.4e9 / 1e12
 PAGES_TFLOPS = {"f16_4096x4096x8192": 1437.0}
 MALL_BYTES = 256 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "matrix_core_scheduling_amd", "csrc", "gemm_pipelined.hip")
-
-
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
-
-
-def traffic_for(workload: str):
+def traffic_for(workload: str, schedule: str):
     """HBM bytes per launch from the committed counter runs, if they were taken
-    on the current kernel source; otherwise None."""
+    on the current source of the kernel that runs; otherwise None."""
+    from matrix_core_scheduling_amd import profiling
+
+    kernel = "pipelined" if schedule in ("auto", "pipelined") else schedule
+    if kernel not in profiling.KERNEL_SOURCES:
+        return None
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f).get(workload)
+            t = json.load(f).get(profiling.traffic_key(workload, kernel))
     except (OSError, ValueError):
         return None
-    if not t or t.get("kernel_source_sha256") != kernel_source_hash():
+    if not t or t.get("kernel_source_sha256") != profiling.kernel_source_hash(kernel):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -102,7 +98,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS))
-    ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "generic"])
+    ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "interleaved", "generic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -153,7 +149,8 @@ def main(argv=None) -> int:
     out_type = mcs.GEMM_OUT_F32 if w.out == "f32" else mcs.GEMM_OUT_SAME
     dtype = mcs.GEMM_DTYPE_F16 if w.dtype == "f16" else mcs.GEMM_DTYPE_BF16
     sched = {"auto": mcs.GEMM_SCHED_AUTO, "pipelined": mcs.GEMM_SCHED_PIPELINED,
-             "in_phase": mcs.GEMM_SCHED_IN_PHASE, "generic": mcs.GEMM_SCHED_GENERIC}[a.schedule]
+             "in_phase": mcs.GEMM_SCHED_IN_PHASE, "interleaved": mcs.GEMM_SCHED_INTERLEAVED,
+             "generic": mcs.GEMM_SCHED_GENERIC}[a.schedule]
     lda, ldb, ldc = w.K, (w.K if w.trans_b else w.N), w.N
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
@@ -249,7 +246,7 @@ def main(argv=None) -> int:
                                                   out=w.dtype if w.out == "same" else "f32")).sum())
         check = {"rows": rows, "elements": rows * w.N, "outside_tolerance": bad, "pass": bad == 0}
 
-    traffic = traffic_for(w.name)
+    traffic = traffic_for(w.name, a.schedule)
     line = {
         "metric": METRIC,
         "value": round(tflops, 3),

@@ -72,7 +72,13 @@ enum gemm_schedule {
     GEMM_SCHED_PIPELINED = 1,  /* 8 waves, two groups held one stage apart */
     GEMM_SCHED_IN_PHASE = 2,   /* same kernel and stages, groups kept in phase
                                   (no entry/exit offset): the ablation baseline */
-    GEMM_SCHED_GENERIC = 3     /* plain LDS-tiled FMA kernel, any alignment */
+    GEMM_SCHED_GENERIC = 3,    /* plain LDS-tiled FMA kernel, any alignment */
+    GEMM_SCHED_INTERLEAVED = 4 /* 4 waves, one per SIMD, each interleaving its
+                                  own MFMA, LDS reads and copies ("Porting
+                                  High-Performance HIP Kernels to FlyDSL",
+                                  section "A More Complex Kernel"); same tile,
+                                  loader, LDS layout and epilogue as PIPELINED:
+                                  the ablation of warp-pipelining itself */
 };
 
 /*
@@ -100,9 +106,10 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
 
 /*
  * gemm_ex -- the same product with the operand type (gemm_dtype) and the
- * kernel schedule (gemm_schedule) chosen by the caller.  PIPELINED and
- * IN_PHASE need 16-byte aligned A, B, C, lda/ldb/ldc and K multiples of 8;
- * asking for them otherwise returns GEMM_EINVAL.
+ * kernel schedule (gemm_schedule) chosen by the caller.  PIPELINED,
+ * IN_PHASE and INTERLEAVED need 16-byte aligned A, B, C, lda/ldb/ldc and K
+ * multiples of 8, and an even N when B is K x N; asking for them otherwise
+ * returns GEMM_EINVAL (nothing is launched).
  */
 int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K,
             const void *A, int64_t lda,

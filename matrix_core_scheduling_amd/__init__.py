@@ -22,7 +22,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "mcs_gemm.h")
 GEMM_OK, GEMM_EINVAL, GEMM_EUNSUPPORTED, GEMM_EHIP = 0, -1, -3, -4
 GEMM_OUT_SAME, GEMM_OUT_F32 = 0, 1
 GEMM_DTYPE_F16, GEMM_DTYPE_BF16 = 0, 1
-GEMM_SCHED_AUTO, GEMM_SCHED_PIPELINED, GEMM_SCHED_IN_PHASE, GEMM_SCHED_GENERIC = 0, 1, 2, 3
+GEMM_SCHED_AUTO, GEMM_SCHED_PIPELINED, GEMM_SCHED_IN_PHASE, GEMM_SCHED_GENERIC, GEMM_SCHED_INTERLEAVED = 0, 1, 2, 3, 4
 
 
 class GemmError(RuntimeError):

@@ -1,0 +1,337 @@
+// Device-side pieces shared by the 256x256x64 MFMA kernels (the 8-wave
+// warp-pipelined kernel and the 4-wave within-wave-interleaved kernel): the
+// LDS layout, the global -> LDS copy loader, the instruction helpers, the
+// tile order and the fused output store.  The two kernels differ only in how
+// their waves divide the tile and schedule the work.
+#pragma once
+
+#include "internal.h"
+
+namespace mcs {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS: two buffers (one per K-step in flight), each [A0 | A1 | B0 | B1]
+// halves of 16 KiB.  An A half (and a B half when B is N x K) is 128 rows x
+// 64 k, 128-byte rows of eight 16-byte chunks stored at chunk ^ (row & 7).  A
+// B half when B is K x N is 64 k-rows x 128 n, 256-byte rows with chunk ^
+// 2*((k & 3) + 4*((k >> 3) & 1)), read with ds_read_b64_tr_b16.
+constexpr uint32_t kHalf = 16384;          // bytes of one operand half in LDS
+constexpr uint32_t kBuf = 4 * kHalf;       // one K-step: A0 A1 B0 B1
+constexpr uint32_t kOffA = 0, kOffB = 2 * kHalf;
+constexpr uint32_t kOutOfWindow = 0x80000000u;  // >= every buffer window used here
+
+// ---- instruction helpers -----------------------------------------------
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    // GFX9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
+}
+
+// Stage boundary: scheduling wall, workgroup rendezvous, scheduling wall.
+__device__ __forceinline__ void rendezvous() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// 128-bit buffer resource: base, stride 0, num_records bytes, GFX9 config word.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_records) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = static_cast<int>(static_cast<uint32_t>(p));
+    r.y = static_cast<int>(static_cast<uint32_t>(p >> 32) & 0xFFFFu);
+    r.z = static_cast<int>(num_records);
+    r.w = 0x00020000;
+    return r;
+}
+
+// One 16-byte-per-lane copy global -> LDS.  The lane's 16 bytes land at
+// lds_base + 16*lane; voff selects the global bytes (>= num_records reads 0).
+// Issued from inline assembly so the compiler neither reorders it nor adds
+// waits of its own: the schedule's explicit vmcnt waits cover it.
+__device__ __forceinline__ void copy16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+    // Both values are wave-uniform by construction; readfirstlane states it so
+    // the "s" operands always land in SGPRs (it folds away for SGPR values).
+    rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+    rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+    rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+    rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds_base), "v"(voff), "s"(rsrc)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ i32x4 lds_read128(uint32_t addr) {
+    return *reinterpret_cast<const lds_i32x4 *>(static_cast<uintptr_t>(addr));
+}
+
+__device__ __forceinline__ i32x2 lds_read64_tr(uint32_t addr) {
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_i16x4 *>(static_cast<uintptr_t>(addr)));
+    return __builtin_bit_cast(i32x2, v);
+}
+
+template <bool kBF16>
+__device__ __forceinline__ f32x4 mfma(i32x4 x, i32x4 y, f32x4 c) {
+    if constexpr (kBF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                       __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x),
+                                                      __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
+}
+
+// 32-bit LDS byte address of a __shared__ array.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_address(T *smem) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) char *)smem));
+}
+
+// ---- global -> LDS loader ----------------------------------------------
+//
+// The kWaves waves of a workgroup share every copy: each operand half (16
+// KiB) is sixteen 1-KiB pieces, and wave w moves pieces P*w .. P*w+P-1
+// (P = 16 / kWaves), one buffer_load_dwordx4 ... lds per piece.  A piece of an
+// A half (or of a B half given N x K) is 8 rows x 128 bytes: lane (x, pch)
+// fills physical chunk pch of row x, which holds logical k-chunk pch ^ x, so
+// the copy itself writes the XOR-swizzled layout.  A piece of a B half given
+// K x N is 4 k-rows x 256 bytes, swizzled the same way for the transposing
+// read.
+template <bool kTransB, int kWaves>
+struct Loader {
+    static constexpr int P = 16 / kWaves;   // pieces per wave per half
+    static_assert(P * kWaves == 16, "waves must divide the 16 pieces of a half");
+
+    uint32_t lds0;                   // LDS byte address of buffer 0
+    uint32_t cpA[P], cpB[P];         // copy voffsets
+    int cpAchunk[P];                 // k-chunk (of 8) each A / N x K B copy lane moves
+    int cpBrow[P];                   // k-row each K x N B copy lane moves
+    int wave;
+    const GemmParams &p;
+    int m0, n0;
+    // per-half copy windows (uniform; computed once): first row (A, or B given
+    // N x K) or first column (B given K x N) of the half, the window's bytes
+    // before the k-extent, and whether the half holds any valid row/column
+    const uint16_t *aRow[2], *bBase[2];
+    uint32_t aSpan[2], bSpan[2];
+    bool aLive[2], bLive[2];
+
+    __device__ __forceinline__ Loader(const GemmParams &prm, int tm, int tn) : p(prm) {
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        m0 = tm * kTileM;
+        n0 = tn * kTileN;
+        lds0 = 0;
+        for (int h = 0; h < 2; ++h) {
+            const int rows = min(max(p.M - (m0 + 128 * h), 0), 128);
+            aLive[h] = rows > 0;
+            aRow[h] = p.A + (int64_t)(m0 + 128 * h) * p.lda;
+            aSpan[h] = rows > 0 ? static_cast<uint32_t>((rows - 1) * p.lda * 2) : 0u;
+            const int cols = min(max(p.N - (n0 + 128 * h), 0), 128);
+            bLive[h] = cols > 0;
+            if constexpr (kTransB) {
+                bBase[h] = p.B + (int64_t)(n0 + 128 * h) * p.ldb;
+                bSpan[h] = cols > 0 ? static_cast<uint32_t>((cols - 1) * p.ldb * 2) : 0u;
+            } else {
+                bBase[h] = p.B + n0 + 128 * h;
+                bSpan[h] = static_cast<uint32_t>(cols * 2);
+            }
+        }
+        const int x = lane >> 3, pch = lane & 7;
+        for (int i = 0; i < P; ++i) {
+            const int row = 8 * (P * wave + i) + x;           // row of the half
+            const int c = pch ^ x;                             // logical 16-byte k-chunk (row & 7 = x)
+            cpAchunk[i] = c;
+            cpA[i] = static_cast<uint32_t>(row * p.lda * 2 + c * 16);
+            if constexpr (kTransB)
+                cpB[i] = static_cast<uint32_t>(row * p.ldb * 2 + c * 16);
+        }
+        if constexpr (!kTransB) {
+            const int y = lane >> 4, pc = lane & 15;
+            for (int i = 0; i < P; ++i) {
+                const int krow = 4 * (P * wave + i) + y;
+                const int ch = pc ^ (2 * ((krow & 3) + 4 * ((krow >> 3) & 1)));   // logical n-chunk
+                cpBrow[i] = krow;
+                cpB[i] = static_cast<uint32_t>(krow * p.ldb * 2 + ch * 16);
+            }
+        }
+    }
+
+    // Copy half h of operand A (rows m0+128h..) for K-step s into buffer `buf`.
+    // The window ends at the last valid byte of the half's last valid row, so
+    // rows >= M and every k >= K (steps past the end: an empty window) read 0.
+    // Pieces I0 .. I1-1 of this wave's share (all of them by default).
+    template <int I0 = 0, int I1 = P>
+    __device__ __forceinline__ void copy_a(int s, uint32_t buf, int h) const {
+        const int kv = p.K - s * kTileK;                      // k left (may be <= 0)
+        const uint32_t nrec = (aLive[h] && kv > 0) ? aSpan[h] + 2u * static_cast<uint32_t>(kv) : 0u;
+        const i32x4 rs = make_rsrc(aRow[h] + s * kTileK, nrec);
+        const uint32_t dst = lds0 + buf + kOffA + h * kHalf + P * wave * 1024;
+        for (int i = I0; i < I1; ++i) {
+            const uint32_t v = (cpAchunk[i] * 8 < kv) ? cpA[i] : kOutOfWindow;
+            copy16(rs, dst + i * 1024, v);
+        }
+    }
+
+    // Copy half h of operand B (columns n0+128h..) for K-step s into buffer `buf`.
+    template <int I0 = 0, int I1 = P>
+    __device__ __forceinline__ void copy_b(int s, uint32_t buf, int h) const {
+        const int kv = p.K - s * kTileK;
+        const uint32_t dst = lds0 + buf + kOffB + h * kHalf + P * wave * 1024;
+        if constexpr (kTransB) {
+            const uint32_t nrec = (bLive[h] && kv > 0) ? bSpan[h] + 2u * static_cast<uint32_t>(kv) : 0u;
+            const i32x4 rs = make_rsrc(bBase[h] + s * kTileK, nrec);
+            for (int i = I0; i < I1; ++i) {
+                const uint32_t v = (cpAchunk[i] * 8 < kv) ? cpB[i] : kOutOfWindow;
+                copy16(rs, dst + i * 1024, v);
+            }
+        } else {
+            // k-rows k0 .. k0+rows-1; the window ends at the last valid column
+            // of the last valid k-row
+            const int rows = min(kv, kTileK);
+            const uint32_t nrec = (bLive[h] && kv > 0)
+                ? static_cast<uint32_t>(rows - 1) * static_cast<uint32_t>(p.ldb * 2) + bSpan[h] : 0u;
+            const i32x4 rs = make_rsrc(bBase[h] + (int64_t)s * kTileK * p.ldb, nrec);
+            for (int i = I0; i < I1; ++i) {
+                const uint32_t v = (cpBrow[i] < kv) ? cpB[i] : kOutOfWindow;
+                copy16(rs, dst + i * 1024, v);
+            }
+        }
+    }
+};
+
+// LDS offsets of one lane's MFMA operand fragments within a half.  A fragment
+// (16 rows x 32 k) is one 16-byte chunk per lane: row row0 + (lane & 15),
+// k-chunk 4*ks + (lane >> 4).  For B given K x N the fragment of 16 columns
+// is two transposing 8-byte reads per lane (k-rows 32ks + 8g + r and
+// 32ks + 4 + 8g + r, r = (lane & 15) >> 2), at the per-nt offsets below
+// plus the constant (32*ks + {0, 4}) * 256.
+struct FragOffsets {
+    uint32_t row[2];   // chunk-read offset for rows row0.., ks = 0, 1 (add 2048 per 16 rows)
+    uint32_t tr[4];    // transposing-read offset for columns col0 + 16nt, k-row 8g + r
+
+    __device__ __forceinline__ void rows(int row0, int lane) {
+        const int l16 = lane & 15, lg = lane >> 4;
+        const int swz = lane & 7;                  // = row & 7 for the 16 rows of a read
+        for (int ks = 0; ks < 2; ++ks)
+            row[ks] = (row0 + l16) * 128 + (((4 * ks) | lg) ^ swz) * 16;
+    }
+
+    // col0 a multiple of 64
+    __device__ __forceinline__ void cols_tr(int col0, int lane) {
+        // lane (lg, l16) of a transposed read for (nt, ks, h) loads 8 bytes of
+        // k-row 32ks + 4h + 8lg + (l16 >> 2), columns col0 + 16nt + 4(l16 & 3):
+        // the (ks, h) part of the row is a constant offset, the swizzle only
+        // sees the lane part of the row.
+        const int l16 = lane & 15, lg = lane >> 4;
+        const int fb = 2 * ((l16 >> 2) + 4 * (lg & 1));
+        for (int nt = 0; nt < 4; ++nt) {
+            const int ch = col0 / 8 + 2 * nt + ((l16 & 3) >> 1);
+            tr[nt] = (8 * lg + (l16 >> 2)) * 256 + ((ch ^ fb) * 16) + 8 * (l16 & 1);
+        }
+    }
+};
+
+__device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &tn) {
+    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2);
+    // renumber so each XCD gets a contiguous range of tiles, then walk that
+    // range in groups of group_m tile rows so neighbours share A and B tiles.
+    const int wg = blockIdx.x;
+    const int total = p.tiles_m * p.tiles_n;
+    const int xcd = wg & 7, j = wg >> 3;
+    const int q = total >> 3, r = total & 7;
+    const int tile = xcd * q + min(xcd, r) + j;
+    const int width = p.group_m * p.tiles_n;
+    const int g = tile / width;
+    const int first_m = g * p.group_m;
+    const int gm = min(p.tiles_m - first_m, p.group_m);
+    const int in = tile - g * width;
+    tm = first_m + in % gm;
+    tn = in / gm;
+}
+
+// ---- fused epilogue ------------------------------------------------------
+//
+// Store one lane's part of four neighbouring 16x16 accumulator tiles (columns
+// col0 .. col0+63 of row `row`).  With the B fragment as the first MFMA
+// operand, lane l of tile nt holds columns 16nt + 4(l >> 4) .. +3 of row
+// l & 15.  FP32 output stores those four values (16 bytes).  For a 16-bit
+// output (round to nearest even), lanes l and l^16 trade halves of tiles nt
+// and nt+1 so every lane stores eight consecutive columns (16 bytes).
+// Columns at or past N are not written.
+template <bool kBF16, bool kOutF32>
+__device__ __forceinline__ void store_strip(const GemmParams &p, const f32x4 (&v4)[4], int row,
+                                            int col0, int lane) {
+    const int g = lane >> 4;
+    if constexpr (kOutF32) {
+        for (int nt = 0; nt < 4; ++nt) {
+            const int col = col0 + 16 * nt + 4 * g;
+            const f32x4 v = v4[nt];
+            float *c = reinterpret_cast<float *>(p.C) + (int64_t)row * p.ldc + col;
+            if (col + 4 <= p.N) {
+                *reinterpret_cast<f32x4 *>(c) = v;
+            } else {
+                for (int r = 0; r < 4; ++r)
+                    if (col + r < p.N) c[r] = v[r];
+            }
+        }
+    } else {
+        for (int nt = 0; nt < 4; nt += 2) {
+            i32x2 h0, h1;
+            if constexpr (kBF16) {
+                h0 = __builtin_bit_cast(i32x2, __builtin_convertvector(v4[nt], bf16x4));
+                h1 = __builtin_bit_cast(i32x2, __builtin_convertvector(v4[nt + 1], bf16x4));
+            } else {
+                h0 = __builtin_bit_cast(i32x2, __builtin_convertvector(v4[nt], f16x4));
+                h1 = __builtin_bit_cast(i32x2, __builtin_convertvector(v4[nt + 1], f16x4));
+            }
+            const bool odd = g & 1;
+            const i32x2 send = odd ? h0 : h1;
+            i32x2 recv;
+            recv.x = __shfl_xor(send.x, 16);
+            recv.y = __shfl_xor(send.y, 16);
+            const i32x4 out = odd ? i32x4{recv.x, recv.y, h1.x, h1.y}
+                                  : i32x4{h0.x, h0.y, recv.x, recv.y};
+            const int col = col0 + 16 * nt + (odd ? 16 + 4 * (g - 1) : 4 * g);
+            uint16_t *c = reinterpret_cast<uint16_t *>(p.C) + (int64_t)row * p.ldc + col;
+            if (col + 8 <= p.N) {
+                *reinterpret_cast<i32x4 *>(c) = out;
+            } else {
+                const i16x8 e = __builtin_bit_cast(i16x8, out);
+                for (int r = 0; r < 8; ++r)
+                    if (col + r < p.N) c[r] = static_cast<uint16_t>(e[r]);
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace mcs

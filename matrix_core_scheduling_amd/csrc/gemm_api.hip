@@ -36,7 +36,7 @@ int validate(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t 
     if (dtype != GEMM_DTYPE_F16 && dtype != GEMM_DTYPE_BF16) return GEMM_EINVAL;
     if (trans_b != 0 && trans_b != 1) return GEMM_EINVAL;
     if (out_type != GEMM_OUT_SAME && out_type != GEMM_OUT_F32) return GEMM_EINVAL;
-    if (schedule < GEMM_SCHED_AUTO || schedule > GEMM_SCHED_GENERIC) return GEMM_EINVAL;
+    if (schedule < GEMM_SCHED_AUTO || schedule > GEMM_SCHED_INTERLEAVED) return GEMM_EINVAL;
     if (M < 0 || N < 0 || K < 0) return GEMM_EINVAL;
     if (M > kIntMax || N > kIntMax || K > kIntMax) return GEMM_EUNSUPPORTED;
     if (M == 0 || N == 0) return GEMM_OK;
@@ -86,8 +86,7 @@ extern "C" int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A
 
     const bool fast = pipelined_ok(M, N, K, A, lda, B, ldb, trans_b, C, ldc);
     if (schedule == GEMM_SCHED_AUTO) schedule = fast ? GEMM_SCHED_PIPELINED : GEMM_SCHED_GENERIC;
-    if ((schedule == GEMM_SCHED_PIPELINED || schedule == GEMM_SCHED_IN_PHASE) && !fast)
-        return GEMM_EINVAL;
+    if (schedule != GEMM_SCHED_GENERIC && !fast) return GEMM_EINVAL;
 
     if (schedule == GEMM_SCHED_GENERIC) {
         const int64_t gx = (N + mcs::kGenTile - 1) / mcs::kGenTile;
@@ -106,6 +105,11 @@ extern "C" int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A
     prm.tiles_n = static_cast<int>(tn);
     prm.steps = static_cast<int>(nk < 2 ? 2 : (nk + 1) / 2 * 2);
     prm.group_m = 4;
+    if (schedule == GEMM_SCHED_INTERLEAVED) {
+        prm.steps = static_cast<int>(nk);   // one K-step per loop iteration
+        return launch(mcs::interleaved_kernel(bf16, trans_b != 0, out_f32),
+                      dim3(static_cast<unsigned>(tm * tn)), dim3(mcs::kInterThreads), prm, stream);
+    }
     return launch(mcs::pipelined_kernel(bf16, trans_b != 0, out_f32, schedule == GEMM_SCHED_PIPELINED),
                   dim3(static_cast<unsigned>(tm * tn)), dim3(mcs::kPipeThreads), prm, stream);
 }
@@ -136,6 +140,10 @@ extern "C" int gemm_kernel_info(int dtype, int trans_b, int out_type, int schedu
     if (schedule == GEMM_SCHED_AUTO || schedule == GEMM_SCHED_PIPELINED || schedule == GEMM_SCHED_IN_PHASE) {
         fn = mcs::pipelined_kernel(bf16, trans_b != 0, out_f32, schedule != GEMM_SCHED_IN_PHASE);
         threads = mcs::kPipeThreads;
+        tm = mcs::kTileM; tn = mcs::kTileN; tk = mcs::kTileK;
+    } else if (schedule == GEMM_SCHED_INTERLEAVED) {
+        fn = mcs::interleaved_kernel(bf16, trans_b != 0, out_f32);
+        threads = mcs::kInterThreads;
         tm = mcs::kTileM; tn = mcs::kTileN; tk = mcs::kTileK;
     } else if (schedule == GEMM_SCHED_GENERIC) {
         fn = mcs::generic_kernel(bf16, trans_b != 0, out_f32);

@@ -1,0 +1,226 @@
+// Within-wave interleaved FP16/BF16 GEMM for gfx950: the 4-wave counterpart
+// of the warp-pipelined kernel, built from the same parts (256x256x64 tile,
+// the same global -> LDS loader, LDS layout and swizzle, MFMA instruction,
+// tile order and fused epilogue) so that the two differ only in how the
+// schedule overlaps matrix and memory work.
+//
+// "Two Waves, One Stage Apart: Warp-Pipelining Triton GEMMs on AMD Instinct"
+// compares its 8-wave kernel with a hand-tuned 4-wave kernel on MI355X
+// (section "MI350 Series (gfx950, CDNA 4): Three Overlapping Flows") and notes
+// that the two differ in layout, compiler settings and tooling, so the
+// comparison does not isolate warp-pipelining.  The structure of the 4-wave
+// kernel follows "Porting High-Performance HIP Kernels to FlyDSL" (section
+// "A More Complex Kernel", "Putting it All Together"): each wave owns a
+// 128x128 block of the output as a 2x2 arrangement of 64x64 sub-tiles and
+// computes them in the order c00, c01, c10, c11; while the MFMAs of one
+// sub-tile run, the same wave reads the operand fragment the next sub-tile
+// needs and issues the copy of one operand half of a future K-step (an
+// "interleaved cluster"); a wait plus a workgroup barrier precedes c00 and
+// c10.  That page's kernel is FP8 with a 128-deep K-step; here the K-step is
+// 64 deep (two 16x16x32 MFMA k-slices), as in the 8-wave kernel.
+//
+// One wave per SIMD: wave w = (wm, wn) = (w & 1, w >> 1) owns rows 64wm..+63
+// of both A halves and columns 64wn..+63 of both B halves, i.e. one 64x64 block
+// of every 128x128 quadrant; its 256 FP32 accumulators live in the
+// accumulation registers.  Fragments: a0/a1 = the wave's 64 rows of A half 0/1,
+// b0/b1 = its 64 columns of B half 0/1 (4 tiles x 2 k-slices, 32 VGPRs each).
+//
+// Schedule of K-step s (cur = buffer of s, nxt = buffer of s+1):
+//     [wait, barrier]
+//     c00 += a0.b0   read b1 <- B1[cur]   copy A0[cur] <- s+2
+//     c01 += a0.b1   read a1 <- A1[cur]   copy B0[cur] <- s+2
+//     [wait, barrier]
+//     c10 += a1.b0   read a0 <- A0[nxt]   copy B1[cur] <- s+2
+//     c11 += a1.b1   read b0 <- B0[nxt]   copy A1[cur] <- s+2
+// Waits (derived the same way as for the 8-wave kernel):
+//   * read -> refill: each half is refilled only after a barrier that follows
+//     the cluster that last read it (A0/B0 of cur were read in c10/c11 of
+//     step s-1, B1/A1 in c00/c01 of step s), and every barrier is preceded
+//     by lgkmcnt(0).
+//   * copy -> read: each wave issues four copies per cluster.  The halves read
+//     after the first barrier (B1, A1 of cur) were copied in c10/c11 of step
+//     s-2 and the halves read after the second (A0, B0 of nxt) in c00/c01 of
+//     step s-1; in both cases at least sixteen copies of this wave follow, so
+//     both barriers are preceded by vmcnt(16): every copy has about one
+//     K-step to land.
+// Inside a cluster the 32 MFMAs run in eight groups of four (one k-slice and
+// one 16-row tile of A against four 16-column tiles of B); the eight reads of
+// the next fragment go out two per group in groups 0-3 (so they are complete
+// well before the barrier that ends the cluster pair) and the four copies one
+// per group in groups 4-7, with a scheduling wall after each group so the
+// compiler keeps the interleaving.  Per K-step each wave reads 32 KiB of LDS
+// (the 8-wave kernel: 24 KiB for each of 8 waves) and waits at two barriers.
+#include "device.h"
+
+namespace mcs {
+namespace {
+
+constexpr int kWaves = kInterThreads / 64;
+constexpr int kCopyWait = 16;              // vmcnt before each barrier
+
+template <bool kTransB>
+struct Interleave : Loader<kTransB, kWaves> {
+    using Loader<kTransB, kWaves>::lds0;
+    FragOffsets fa, fb;
+
+    __device__ __forceinline__ Interleave(const GemmParams &prm, int tm, int tn)
+        : Loader<kTransB, kWaves>(prm, tm, tn) {
+        const int lane = threadIdx.x & 63;
+        const int wm = this->wave & 1, wn = this->wave >> 1;
+        fa.rows(64 * wm, lane);
+        if constexpr (kTransB)
+            fb.rows(64 * wn, lane);
+        else
+            fb.cols_tr(64 * wn, lane);
+    }
+
+    // Piece j (k-slice j >> 2, 16-row tile j & 3) of a fragment of A half h.
+    __device__ __forceinline__ i32x4 read_a(uint32_t buf, int h, int j) const {
+        return lds_read128(lds0 + buf + kOffA + h * kHalf + fa.row[j >> 2] + (j & 3) * 2048);
+    }
+
+    // Piece j (k-slice j >> 2, 16-column tile j & 3) of a fragment of B half h.
+    __device__ __forceinline__ i32x4 read_b(uint32_t buf, int h, int j) const {
+        const uint32_t base = lds0 + buf + kOffB + h * kHalf;
+        const int ks = j >> 2, nt = j & 3;
+        if constexpr (kTransB) {
+            return lds_read128(base + fb.row[ks] + nt * 2048);
+        } else {
+            const i32x2 lo = lds_read64_tr(base + fb.tr[nt] + (32 * ks + 0) * 256);
+            const i32x2 hi = lds_read64_tr(base + fb.tr[nt] + (32 * ks + 4) * 256);
+            return i32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+    }
+
+    // One cluster: acc += a . b over the K-step while fragment `nf` (operand
+    // kind kReadB ? B : A, half rh, buffer rbuf) is read and half ch of operand
+    // kCopyB ? B : A is copied for K-step cs into buffer cbuf.
+    template <bool kBF16, bool kReadB, bool kCopyB>
+    __device__ __forceinline__ void cluster(f32x4 (&acc)[4][4], const i32x4 (&a)[4][2],
+                                            const i32x4 (&b)[4][2], i32x4 (&nf)[4][2],
+                                            uint32_t rbuf, int rh, int cs, uint32_t cbuf,
+                                            int ch) const {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            if (g < 4) {
+#pragma unroll
+                for (int j = 2 * g; j < 2 * g + 2; ++j)
+                    nf[j & 3][j >> 2] = kReadB ? read_b(rbuf, rh, j) : read_a(rbuf, rh, j);
+            } else {
+                if constexpr (kCopyB) {
+                    if (g == 4) this->template copy_b<0, 1>(cs, cbuf, ch);
+                    if (g == 5) this->template copy_b<1, 2>(cs, cbuf, ch);
+                    if (g == 6) this->template copy_b<2, 3>(cs, cbuf, ch);
+                    if (g == 7) this->template copy_b<3, 4>(cs, cbuf, ch);
+                } else {
+                    if (g == 4) this->template copy_a<0, 1>(cs, cbuf, ch);
+                    if (g == 5) this->template copy_a<1, 2>(cs, cbuf, ch);
+                    if (g == 6) this->template copy_a<2, 3>(cs, cbuf, ch);
+                    if (g == 7) this->template copy_a<3, 4>(cs, cbuf, ch);
+                }
+            }
+            const int ks = g >> 2, mt = g & 3;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                acc[mt][nt] = mfma<kBF16>(b[nt][ks], a[mt][ks], acc[mt][nt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
+// This wave's copies for the reads after the barrier have landed, and its own
+// LDS reads are complete (their halves are refilled after the barrier).
+__device__ __forceinline__ void wait_and_rendezvous() {
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<kCopyWait>();
+    wait_lgkmcnt<0>();
+    rendezvous();
+}
+
+template <bool kBF16, bool kTransB, bool kOutF32>
+__global__ void __launch_bounds__(kInterThreads)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_interleaved_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[2 * kBuf];
+
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    Interleave<kTransB> il(p, tm, tn);
+    il.lds0 = lds_address(smem);
+    const int wave = il.wave;
+
+    f32x4 acc[2][2][4][4];
+    for (int qa = 0; qa < 2; ++qa)
+        for (int qb = 0; qb < 2; ++qb)
+            for (int mt = 0; mt < 4; ++mt)
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[qa][qb][mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x4 a0[4][2], a1[4][2], b0[4][2], b1[4][2];
+
+    // ---- prologue: the copy stream of steps 0 and 1 in steady-state order
+    // (A0 B0 B1 A1 per step), then the fragments c00 of step 0 needs.
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t buf = s ? kBuf : 0u;
+        il.copy_a(s, buf, 0);
+        il.copy_b(s, buf, 0);
+        il.copy_b(s, buf, 1);
+        il.copy_a(s, buf, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<24>();                   // A0(0) and B0(0) landed (this wave's part)
+    rendezvous();                       // ... and every wave's part
+    for (int j = 0; j < 8; ++j) {
+        a0[j & 3][j >> 2] = il.read_a(0, 0, j);
+        b0[j & 3][j >> 2] = il.read_b(0, 0, j);
+    }
+
+    // ---- steady state, one K-step per iteration.  (Unrolling two K-steps so
+    // the buffers are addressed statically, as the 8-wave kernel does, makes
+    // the register allocator rotate the 256 accumulators through copies; the
+    // buffer offset costs one scalar select instead.)
+#pragma unroll 1
+    for (int s = 0; s < p.steps; ++s) {
+        const uint32_t cur = (s & 1) ? kBuf : 0u, nxt = kBuf - cur;
+        wait_and_rendezvous();
+        il.template cluster<kBF16, true, false>(acc[0][0], a0, b0, b1, cur, 1, s + 2, cur, 0);
+        il.template cluster<kBF16, false, true>(acc[0][1], a0, b1, a1, cur, 1, s + 2, cur, 0);
+        wait_and_rendezvous();
+        il.template cluster<kBF16, false, true>(acc[1][0], a1, b0, a0, nxt, 0, s + 2, cur, 1);
+        il.template cluster<kBF16, true, false>(acc[1][1], a1, b1, b0, nxt, 0, s + 2, cur, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();   // the zero-window copies of steps past the end, before LDS is released
+
+    // ---- epilogue (fully unrolled: the accumulators are only ever indexed
+    // by constants, so they stay in registers)
+    const int lane = __lane_id();
+    const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+    for (int qa = 0; qa < 2; ++qa)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int row = il.m0 + 128 * qa + 64 * wm + 16 * mt + (lane & 15);
+            if (row >= p.M) continue;
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                store_strip<kBF16, kOutF32>(p, acc[qa][qb][mt], row, il.n0 + 128 * qb + 64 * wn, lane);
+        }
+}
+
+}  // namespace
+
+const void *interleaved_kernel(bool bf16, bool trans_b, bool out_f32) {
+#define MCS_PICK(B, T, O)                                                            \
+    if (bf16 == B && trans_b == T && out_f32 == O)                                  \
+        return reinterpret_cast<const void *>(&gemm_interleaved_kernel<B, T, O>);
+#define MCS_PICK_O(B, T) MCS_PICK(B, T, false) MCS_PICK(B, T, true)
+    MCS_PICK_O(false, false)
+    MCS_PICK_O(false, true)
+    MCS_PICK_O(true, false)
+    MCS_PICK_O(true, true)
+#undef MCS_PICK_O
+#undef MCS_PICK
+    return nullptr;
+}
+
+}  // namespace mcs

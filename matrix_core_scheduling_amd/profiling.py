@@ -3,7 +3,8 @@
     python -m matrix_core_scheduling_amd.profiling stats DIR [--kernel SUBSTR]
     python -m matrix_core_scheduling_amd.profiling counters DIR [DIR ...] [--kernel SUBSTR]
     python -m matrix_core_scheduling_amd.profiling traffic --fetch DIR --write DIR
-           --copy-fetch DIR --copy-write DIR --copy-mib N --workload NAME [--update FILE]
+           --copy-fetch DIR --copy-write DIR --copy-mib N --workload NAME
+           [--schedule pipelined|interleaved] [--update FILE]
 
 DIR is a rocprofv3 output directory written with --output-format csv.
 Counter rows come one per hardware instance; they are summed per dispatch
@@ -26,7 +27,12 @@ import json
 import os
 import sys
 
-KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", "gemm_pipelined.hip")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+# Source files that determine each timed kernel's code.
+KERNEL_SOURCES = {
+    "pipelined": ("gemm_pipelined.hip", "device.h", "internal.h"),
+    "interleaved": ("gemm_interleaved.hip", "device.h", "internal.h"),
+}
 
 
 def _one(d: str, pattern: str) -> str:
@@ -96,13 +102,21 @@ def derived(c: dict, n_xcc: int, simds: int) -> dict:
     return out
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_source_hash(schedule: str = "pipelined") -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[schedule]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, kernel="gemm_pipelined",
+def traffic_key(workload: str, schedule: str = "pipelined") -> str:
+    return workload if schedule == "pipelined" else f"{workload}@{schedule}"
+
+
+def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, schedule="pipelined",
             copy_kernel="copyBuffer") -> dict:
+    kernel = "gemm_" + schedule
     copy_bytes = copy_mib * 2 ** 20
     cf = counters([copy_fetch_dir], copy_kernel)
     cw = counters([copy_write_dir], copy_kernel)
@@ -119,7 +133,7 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, kern
     return {"fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
             "hbm_bytes_per_launch": round(fetch + write), "fetch_scale": round(f_scale, 5),
             "write_scale": round(w_scale, 5), "copy_calibration_mib": copy_mib,
-            "kernel_source_sha256": kernel_source_hash()}
+            "kernel_source_sha256": kernel_source_hash(schedule)}
 
 
 def main(argv=None) -> int:
@@ -136,6 +150,7 @@ def main(argv=None) -> int:
         t.add_argument("--" + f.replace("_", "-"), required=True)
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--workload", required=True)
+    t.add_argument("--schedule", default="pipelined", choices=sorted(KERNEL_SOURCES))
     t.add_argument("--update", default=None, help="JSON file to add the result to")
     a = ap.parse_args(argv)
 
@@ -158,13 +173,13 @@ def main(argv=None) -> int:
                 print(f"| (derived) {n} | {v:.6g} |")
             print()
     elif a.cmd == "traffic":
-        r = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib)
+        r = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.schedule)
         print(json.dumps(r, indent=1))
         if a.update:
             data = {}
             if os.path.exists(a.update):
                 data = json.load(open(a.update))
-            data[a.workload] = r
+            data[traffic_key(a.workload, a.schedule)] = r
             with open(a.update, "w") as f:
                 json.dump(data, f, indent=1, sort_keys=True)
                 f.write("\n")

@@ -78,8 +78,10 @@ def test_pipelined_schedule_refuses_unaligned_operands(lib):
     args = (256, 256, 64, P + 2, 64, P, 64, 1, P, 256, 0)
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_IN_PHASE, 0) == mcs.GEMM_EINVAL
+    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
     args = (256, 256, 60, P, 64, P, 64, 1, P, 256, 0)             # K % 8 != 0
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
+    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

@@ -15,7 +15,7 @@ from tests.gpu_util import assert_bit_exact, assert_within_tolerance, run
 pytestmark = pytest.mark.gpu
 
 SCHEDS = {"pipelined": mcs.GEMM_SCHED_PIPELINED, "in_phase": mcs.GEMM_SCHED_IN_PHASE,
-          "generic": mcs.GEMM_SCHED_GENERIC}
+          "interleaved": mcs.GEMM_SCHED_INTERLEAVED, "generic": mcs.GEMM_SCHED_GENERIC}
 
 
 def operands(elem, dist, M, N, K, trans_b, seed, lda=None, ldb=None, nan_pad=False):
@@ -54,7 +54,7 @@ def pipelined_eligible(N, K, trans_b):
     return K % 8 == 0 and (trans_b or N % 2 == 0)
 
 
-@pytest.mark.parametrize("sched", ["pipelined", "in_phase"])
+@pytest.mark.parametrize("sched", ["pipelined", "in_phase", "interleaved"])
 @pytest.mark.parametrize("out", ["same", "f32"])
 @pytest.mark.parametrize("trans_b", [0, 1])
 @pytest.mark.parametrize("elem", ["f16", "bf16"])
@@ -98,16 +98,17 @@ def test_generic_kernel_every_element(elem, trans_b):
 INT_SHAPES = [(256, 256, 32), (512, 256, 64), (256, 512, 192), (512, 512, 448), (1024, 1024, 512)]
 
 
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved"])
 @pytest.mark.parametrize("out", ["same", "f32"])
 @pytest.mark.parametrize("trans_b", [0, 1])
 @pytest.mark.parametrize("elem", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", INT_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_integer_regime_bit_exact(shape, elem, trans_b, out):
+def test_integer_regime_bit_exact(shape, elem, trans_b, out, sched):
     M, N, K = shape
     a, b = operands(elem, "int5", M, N, K, trans_b, seed=7 + K)
     cref = oracle.gemm(a, b, elem, trans_b, with_sabs=False)
-    _, bits = run(elem, M, N, K, a, b, trans_b, out=out, schedule=mcs.GEMM_SCHED_PIPELINED)
-    assert_bit_exact(bits, cref, elem, out, f"int {shape} {elem} tb={trans_b} {out}")
+    _, bits = run(elem, M, N, K, a, b, trans_b, out=out, schedule=SCHEDS[sched])
+    assert_bit_exact(bits, cref, elem, out, f"int {shape} {elem} tb={trans_b} {out} {sched}")
 
 
 # ---- closed forms ---------------------------------------------------------------
@@ -201,6 +202,35 @@ def test_deterministic_and_schedules_agree_bitwise():
     assert np.array_equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("out", ["same", "f32"])
+@pytest.mark.parametrize("trans_b", [0, 1])
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+def test_interleaved_matches_pipelined_bitwise(elem, trans_b, out):
+    """Both 256x256x64 kernels give every output element the same sequence of
+    MFMAs (K-steps in order, two k-slices each, same operand roles), so their
+    results agree bit for bit, ragged edges and K tail included."""
+    for (M, N, K) in [(1024, 768, 2048), (300, 520, 200), (513, 264, 1000)]:
+        a, b = operands(elem, "normal", M, N, K, trans_b, seed=M + K)
+        p = run(elem, M, N, K, a, b, trans_b, out=out, schedule=mcs.GEMM_SCHED_PIPELINED)[1]
+        i = run(elem, M, N, K, a, b, trans_b, out=out, schedule=mcs.GEMM_SCHED_INTERLEAVED)[1]
+        assert np.array_equal(p, i), (M, N, K)
+
+
+@pytest.mark.parametrize("name", [n for n, w in si.WORKLOADS.items() if w.M * w.N >= 4096 * 4096])
+def test_workload_interleaved(name):
+    """Full-size workloads through the 4-wave kernel: sampled oracle parity and
+    bitwise agreement with the 8-wave kernel at every element."""
+    w = si.WORKLOADS[name]
+    a, b = w.operands(0)
+    c, bits = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, schedule=mcs.GEMM_SCHED_INTERLEAVED)
+    ii, jj = sample_points(w.M, w.N, 3000, seed=w.seed + 1)
+    cref, sabs = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
+    assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name,
+                            out=w.dtype if w.out == "same" else "f32")
+    _, bits_p = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, schedule=mcs.GEMM_SCHED_PIPELINED)
+    assert np.array_equal(bits, bits_p)
+
+
 def test_repeated_runs_are_bitwise_identical():
     M, N, K = 2048, 2048, 4096
     a, b = operands("bf16", "normal", M, N, K, 1, seed=99)
@@ -256,7 +286,9 @@ def test_misaligned_operand_takes_generic_path_and_is_correct():
 def test_kernels_have_no_spills():
     for dt in (mcs.GEMM_DTYPE_F16, mcs.GEMM_DTYPE_BF16):
         for out in (mcs.GEMM_OUT_SAME, mcs.GEMM_OUT_F32):
-            info = mcs.gemm_kernel_info(dt, 1, out, mcs.GEMM_SCHED_PIPELINED)
-            assert info["local_bytes"] == 0, info
-            assert info["shared_bytes"] == 128 * 1024, info
-            assert info["block_threads"] == 512
+            for tb in (0, 1):
+                for sched, threads in ((mcs.GEMM_SCHED_PIPELINED, 512), (mcs.GEMM_SCHED_INTERLEAVED, 256)):
+                    info = mcs.gemm_kernel_info(dt, tb, out, sched)
+                    assert info["local_bytes"] == 0, info
+                    assert info["shared_bytes"] == 128 * 1024, info
+                    assert info["block_threads"] == threads
