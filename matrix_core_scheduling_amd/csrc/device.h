@@ -7,6 +7,8 @@
 
 #include "internal.h"
 
+#include <type_traits>
+
 namespace mcs {
 namespace {
 
@@ -67,9 +69,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_record
 }
 
 // One 16-byte-per-lane copy global -> LDS.  The lane's 16 bytes land at
-// lds_base + 16*lane; voff selects the global bytes (>= num_records reads 0).
-// Issued from inline assembly so the compiler neither reorders it nor adds
-// waits of its own: the schedule's explicit vmcnt waits cover it.
+// lds_base + kOff + 16*lane; voff selects the global bytes (>= num_records
+// reads 0).  Issued from inline assembly so the compiler neither reorders it
+// nor adds waits of its own: the schedule's explicit vmcnt waits cover it.
+// M0 (the LDS destination) needs one wait state before the load reads it.
+template <uint32_t kOff>
 __device__ __forceinline__ void copy16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
     // Both values are wave-uniform by construction; readfirstlane states it so
     // the "s" operands always land in SGPRs (it folds away for SGPR values).
@@ -79,12 +83,21 @@ __device__ __forceinline__ void copy16(i32x4 rsrc, uint32_t lds_base, uint32_t v
     rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
     lds_base = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
+        "s_add_u32 m0, %0, %3\n\t"
         "s_nop 0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
         :
-        : "s"(lds_base), "v"(voff), "s"(rsrc)
-        : "memory", "m0");
+        : "s"(lds_base), "v"(voff), "s"(rsrc), "n"(kOff)
+        : "memory", "m0", "scc");
+}
+
+// Calls f(std::integral_constant<int, I>) for I = I0 .. I1-1.
+template <int I0, int I1, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I0 < I1) {
+        f(std::integral_constant<int, I0>{});
+        static_for<I0 + 1, I1>(f);
+    }
 }
 
 __device__ __forceinline__ i32x4 lds_read128(uint32_t addr) {
@@ -132,16 +145,21 @@ struct Loader {
     uint32_t lds0;                   // LDS byte address of buffer 0
     uint32_t cpA[P], cpB[P];         // copy voffsets
     int cpAchunk[P];                 // k-chunk (of 8) each A / N x K B copy lane moves
-    int cpBrow[P];                   // k-row each K x N B copy lane moves
     int wave;
     const GemmParams &p;
     int m0, n0;
-    // per-half copy windows (uniform; computed once): first row (A, or B given
-    // N x K) or first column (B given K x N) of the half, the window's bytes
-    // before the k-extent, and whether the half holds any valid row/column
-    const uint16_t *aRow[2], *bBase[2];
-    uint32_t aSpan[2], bSpan[2];
-    bool aLive[2], bLive[2];
+    // Per-half copy windows (uniform, computed once) of A and of B given N x
+    // K: byte address of the half's first row at k = 0, the window's extent at
+    // k = 0 (start of the last valid row + 2K bytes), and 2K, or 0 when the
+    // half holds no valid row.  At K-step s the window starts 128*s bytes on
+    // and holds data while 128*s < 2K.
+    uint64_t aAddr[2], bAddr[2];
+    uint32_t aEnd[2], bEnd[2], aK2[2], bK2[2];
+    // B given K x N: first column of the half, bytes of one k-row's valid
+    // columns, and whether the half holds any valid column
+    const uint16_t *bBase[2];
+    uint32_t bSpan[2];
+    bool bLive[2];
 
     __device__ __forceinline__ Loader(const GemmParams &prm, int tm, int tn) : p(prm) {
         const int tid = threadIdx.x;
@@ -150,17 +168,19 @@ struct Loader {
         m0 = tm * kTileM;
         n0 = tn * kTileN;
         lds0 = 0;
+        const uint32_t k2 = 2u * static_cast<uint32_t>(p.K);
         for (int h = 0; h < 2; ++h) {
             const int rows = min(max(p.M - (m0 + 128 * h), 0), 128);
-            aLive[h] = rows > 0;
-            aRow[h] = p.A + (int64_t)(m0 + 128 * h) * p.lda;
-            aSpan[h] = rows > 0 ? static_cast<uint32_t>((rows - 1) * p.lda * 2) : 0u;
+            aAddr[h] = reinterpret_cast<uint64_t>(p.A + (int64_t)(m0 + 128 * h) * p.lda);
+            aEnd[h] = rows > 0 ? static_cast<uint32_t>((rows - 1) * p.lda * 2) + k2 : 0u;
+            aK2[h] = rows > 0 ? k2 : 0u;
             const int cols = min(max(p.N - (n0 + 128 * h), 0), 128);
-            bLive[h] = cols > 0;
             if constexpr (kTransB) {
-                bBase[h] = p.B + (int64_t)(n0 + 128 * h) * p.ldb;
-                bSpan[h] = cols > 0 ? static_cast<uint32_t>((cols - 1) * p.ldb * 2) : 0u;
+                bAddr[h] = reinterpret_cast<uint64_t>(p.B + (int64_t)(n0 + 128 * h) * p.ldb);
+                bEnd[h] = cols > 0 ? static_cast<uint32_t>((cols - 1) * p.ldb * 2) + k2 : 0u;
+                bK2[h] = cols > 0 ? k2 : 0u;
             } else {
+                bLive[h] = cols > 0;
                 bBase[h] = p.B + n0 + 128 * h;
                 bSpan[h] = static_cast<uint32_t>(cols * 2);
             }
@@ -179,51 +199,59 @@ struct Loader {
             for (int i = 0; i < P; ++i) {
                 const int krow = 4 * (P * wave + i) + y;
                 const int ch = pc ^ (2 * ((krow & 3) + 4 * ((krow >> 3) & 1)));   // logical n-chunk
-                cpBrow[i] = krow;
                 cpB[i] = static_cast<uint32_t>(krow * p.ldb * 2 + ch * 16);
             }
         }
     }
 
+    // Buffer resource of a row-major (k contiguous) half at K-step s.
+    static __device__ __forceinline__ i32x4 step_rsrc(uint64_t addr, uint32_t end, uint32_t k2, int s) {
+        const uint32_t koff = static_cast<uint32_t>(s) * (2 * kTileK);
+        const uint64_t a = addr + koff;
+        i32x4 r;
+        r.x = static_cast<int>(static_cast<uint32_t>(a));
+        r.y = static_cast<int>(static_cast<uint32_t>(a >> 32));   // < 2^16: stride 0
+        r.z = static_cast<int>(koff < k2 ? end - koff : 0u);
+        r.w = 0x00020000;
+        return r;
+    }
+
     // Copy half h of operand A (rows m0+128h..) for K-step s into buffer `buf`.
     // The window ends at the last valid byte of the half's last valid row, so
     // rows >= M and every k >= K (steps past the end: an empty window) read 0.
-    // Pieces I0 .. I1-1 of this wave's share (all of them by default).
-    template <int I0 = 0, int I1 = P>
+    // Pieces I0 .. I1-1 of this wave's share (all of them by default).  kMask
+    // = false skips the per-lane k-chunk mask: allowed when the step is
+    // either whole (64 k left) or wholly past the end.
+    template <bool kMask = true, int I0 = 0, int I1 = P>
     __device__ __forceinline__ void copy_a(int s, uint32_t buf, int h) const {
         const int kv = p.K - s * kTileK;                      // k left (may be <= 0)
-        const uint32_t nrec = (aLive[h] && kv > 0) ? aSpan[h] + 2u * static_cast<uint32_t>(kv) : 0u;
-        const i32x4 rs = make_rsrc(aRow[h] + s * kTileK, nrec);
+        const i32x4 rs = step_rsrc(aAddr[h], aEnd[h], aK2[h], s);
         const uint32_t dst = lds0 + buf + kOffA + h * kHalf + P * wave * 1024;
-        for (int i = I0; i < I1; ++i) {
-            const uint32_t v = (cpAchunk[i] * 8 < kv) ? cpA[i] : kOutOfWindow;
-            copy16(rs, dst + i * 1024, v);
-        }
+        static_for<I0, I1>([&](auto i) {
+            const uint32_t v = (!kMask || cpAchunk[i] * 8 < kv) ? cpA[i] : kOutOfWindow;
+            copy16<i * 1024>(rs, dst, v);
+        });
     }
 
     // Copy half h of operand B (columns n0+128h..) for K-step s into buffer `buf`.
-    template <int I0 = 0, int I1 = P>
+    template <bool kMask = true, int I0 = 0, int I1 = P>
     __device__ __forceinline__ void copy_b(int s, uint32_t buf, int h) const {
         const int kv = p.K - s * kTileK;
         const uint32_t dst = lds0 + buf + kOffB + h * kHalf + P * wave * 1024;
         if constexpr (kTransB) {
-            const uint32_t nrec = (bLive[h] && kv > 0) ? bSpan[h] + 2u * static_cast<uint32_t>(kv) : 0u;
-            const i32x4 rs = make_rsrc(bBase[h] + s * kTileK, nrec);
-            for (int i = I0; i < I1; ++i) {
-                const uint32_t v = (cpAchunk[i] * 8 < kv) ? cpB[i] : kOutOfWindow;
-                copy16(rs, dst + i * 1024, v);
-            }
+            const i32x4 rs = step_rsrc(bAddr[h], bEnd[h], bK2[h], s);
+            static_for<I0, I1>([&](auto i) {
+                const uint32_t v = (!kMask || cpAchunk[i] * 8 < kv) ? cpB[i] : kOutOfWindow;
+                copy16<i * 1024>(rs, dst, v);
+            });
         } else {
             // k-rows k0 .. k0+rows-1; the window ends at the last valid column
-            // of the last valid k-row
+            // of the last valid k-row, so k-rows >= K read 0 without a mask
             const int rows = min(kv, kTileK);
             const uint32_t nrec = (bLive[h] && kv > 0)
                 ? static_cast<uint32_t>(rows - 1) * static_cast<uint32_t>(p.ldb * 2) + bSpan[h] : 0u;
             const i32x4 rs = make_rsrc(bBase[h] + (int64_t)s * kTileK * p.ldb, nrec);
-            for (int i = I0; i < I1; ++i) {
-                const uint32_t v = (cpBrow[i] < kv) ? cpB[i] : kOutOfWindow;
-                copy16(rs, dst + i * 1024, v);
-            }
+            static_for<I0, I1>([&](auto i) { copy16<i * 1024>(rs, dst, cpB[i]); });
         }
     }
 };
@@ -294,7 +322,8 @@ __device__ __forceinline__ void store_strip(const GemmParams &p, const f32x4 (&v
     if constexpr (kOutF32) {
         for (int nt = 0; nt < 4; ++nt) {
             const int col = col0 + 16 * nt + 4 * g;
-            const f32x4 v = v4[nt];
+            f32x4 v = v4[nt];
+            asm volatile("" : "+v"(v));   // stage through VGPRs: keeps the accumulators' allocation free
             float *c = reinterpret_cast<float *>(p.C) + (int64_t)row * p.ldc + col;
             if (col + 4 <= p.N) {
                 *reinterpret_cast<f32x4 *>(c) = v;

@@ -44,12 +44,19 @@
 //     both barriers are preceded by vmcnt(16): every copy has about one
 //     K-step to land.
 // Inside a cluster the 32 MFMAs run in eight groups of four (one k-slice and
-// one 16-row tile of A against four 16-column tiles of B); the eight reads of
-// the next fragment go out two per group in groups 0-3 (so they are complete
-// well before the barrier that ends the cluster pair) and the four copies one
-// per group in groups 4-7, with a scheduling wall after each group so the
-// compiler keeps the interleaving.  Per K-step each wave reads 32 KiB of LDS
-// (the 8-wave kernel: 24 KiB for each of 8 waves) and waits at two barriers.
+// one 16-row tile of A against four 16-column tiles of B); group g also
+// issues piece g of the next fragment and, for odd g, one copy, with a
+// scheduling wall after each group so the compiler keeps the interleaving.
+// With one wave per SIMD nothing else issues while this wave spends issue
+// slots on address, descriptor or wait instructions: measured on MI355X, a
+// lone wave keeps the matrix pipe full with about three other instructions
+// per 16x16x32 MFMA (fewer if they are vector ALU), so the memory work is
+// kept lean: each K-step computes its LDS read bases once (every read is a
+// base plus an immediate offset), the copies take their LDS destination as
+// an immediate on M0, and the per-lane k mask of the copies is compiled out
+// of every K-step except the partial last one.  Per K-step each wave reads
+// 32 KiB of LDS (the 8-wave kernel: 24 KiB for each of 8 waves) and waits at
+// two barriers.
 #include "device.h"
 
 namespace mcs {
@@ -74,57 +81,72 @@ struct Interleave : Loader<kTransB, kWaves> {
             fb.cols_tr(64 * wn, lane);
     }
 
+    // LDS read bases of one K-step, VGPRs kept opaque to the compiler so
+    // that every fragment read is the base plus an immediate offset.
+    struct Bases {
+        uint32_t a[2][2];    // [buffer cur/nxt][ks]: A fragment rows, A half 0
+        uint32_t b[2][2];    // [buffer][ks]: B fragment rows (B given N x K), B half 0
+        uint32_t buf[2];     // LDS byte address of buffer cur / nxt (uniform)
+    };
+
+    __device__ __forceinline__ Bases bases(uint32_t cur, uint32_t nxt) const {
+        Bases r;
+        for (int u = 0; u < 2; ++u) {
+            r.buf[u] = lds0 + (u ? nxt : cur);
+            for (int ks = 0; ks < 2; ++ks) {
+                r.a[u][ks] = r.buf[u] + kOffA + fa.row[ks];
+                asm volatile("" : "+v"(r.a[u][ks]));
+                if constexpr (kTransB) {
+                    r.b[u][ks] = r.buf[u] + kOffB + fb.row[ks];
+                    asm volatile("" : "+v"(r.b[u][ks]));
+                }
+            }
+        }
+        return r;
+    }
+
     // Piece j (k-slice j >> 2, 16-row tile j & 3) of a fragment of A half h.
-    __device__ __forceinline__ i32x4 read_a(uint32_t buf, int h, int j) const {
-        return lds_read128(lds0 + buf + kOffA + h * kHalf + fa.row[j >> 2] + (j & 3) * 2048);
+    __device__ __forceinline__ i32x4 read_a(const Bases &bs, int u, int h, int j) const {
+        return lds_read128(bs.a[u][j >> 2] + h * kHalf + (j & 3) * 2048);
     }
 
     // Piece j (k-slice j >> 2, 16-column tile j & 3) of a fragment of B half h.
-    __device__ __forceinline__ i32x4 read_b(uint32_t buf, int h, int j) const {
-        const uint32_t base = lds0 + buf + kOffB + h * kHalf;
+    __device__ __forceinline__ i32x4 read_b(const Bases &bs, int u, int h, int j) const {
         const int ks = j >> 2, nt = j & 3;
         if constexpr (kTransB) {
-            return lds_read128(base + fb.row[ks] + nt * 2048);
+            return lds_read128(bs.b[u][ks] + h * kHalf + nt * 2048);
         } else {
-            const i32x2 lo = lds_read64_tr(base + fb.tr[nt] + (32 * ks + 0) * 256);
-            const i32x2 hi = lds_read64_tr(base + fb.tr[nt] + (32 * ks + 4) * 256);
+            // one address add per piece; the k-row offsets are immediates
+            uint32_t base = bs.buf[u] + kOffB + h * kHalf + fb.tr[nt];
+            asm volatile("" : "+v"(base));
+            const i32x2 lo = lds_read64_tr(base + (32 * ks + 0) * 256);
+            const i32x2 hi = lds_read64_tr(base + (32 * ks + 4) * 256);
             return i32x4{lo.x, lo.y, hi.x, hi.y};
         }
     }
 
     // One cluster: acc += a . b over the K-step while fragment `nf` (operand
-    // kind kReadB ? B : A, half rh, buffer rbuf) is read and half ch of operand
-    // kCopyB ? B : A is copied for K-step cs into buffer cbuf.
-    template <bool kBF16, bool kReadB, bool kCopyB>
+    // kind kReadB ? B : A, half rh, buffer u of bs) is read and half ch of
+    // operand kCopyB ? B : A is copied for K-step cs into buffer cbuf.  Group
+    // g issues fragment piece g and, for odd g, one copy.
+    template <bool kBF16, bool kReadB, bool kCopyB, bool kMask>
     __device__ __forceinline__ void cluster(f32x4 (&acc)[4][4], const i32x4 (&a)[4][2],
                                             const i32x4 (&b)[4][2], i32x4 (&nf)[4][2],
-                                            uint32_t rbuf, int rh, int cs, uint32_t cbuf,
+                                            const Bases &bs, int u, int rh, int cs, uint32_t cbuf,
                                             int ch) const {
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            if (g < 4) {
-#pragma unroll
-                for (int j = 2 * g; j < 2 * g + 2; ++j)
-                    nf[j & 3][j >> 2] = kReadB ? read_b(rbuf, rh, j) : read_a(rbuf, rh, j);
-            } else {
-                if constexpr (kCopyB) {
-                    if (g == 4) this->template copy_b<0, 1>(cs, cbuf, ch);
-                    if (g == 5) this->template copy_b<1, 2>(cs, cbuf, ch);
-                    if (g == 6) this->template copy_b<2, 3>(cs, cbuf, ch);
-                    if (g == 7) this->template copy_b<3, 4>(cs, cbuf, ch);
-                } else {
-                    if (g == 4) this->template copy_a<0, 1>(cs, cbuf, ch);
-                    if (g == 5) this->template copy_a<1, 2>(cs, cbuf, ch);
-                    if (g == 6) this->template copy_a<2, 3>(cs, cbuf, ch);
-                    if (g == 7) this->template copy_a<3, 4>(cs, cbuf, ch);
-                }
+        static_for<0, 8>([&](auto g) {
+            nf[g & 3][g >> 2] = kReadB ? read_b(bs, u, rh, g) : read_a(bs, u, rh, g);
+            if constexpr (g & 1) {
+                if constexpr (kCopyB)
+                    this->template copy_b<kMask, g / 2, g / 2 + 1>(cs, cbuf, ch);
+                else
+                    this->template copy_a<kMask, g / 2, g / 2 + 1>(cs, cbuf, ch);
             }
-            const int ks = g >> 2, mt = g & 3;
-#pragma unroll
+            constexpr int ks = g >> 2, mt = g & 3;
             for (int nt = 0; nt < 4; ++nt)
                 acc[mt][nt] = mfma<kBF16>(b[nt][ks], a[mt][ks], acc[mt][nt]);
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     }
 };
 
@@ -169,25 +191,39 @@ gemm_interleaved_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<24>();                   // A0(0) and B0(0) landed (this wave's part)
     rendezvous();                       // ... and every wave's part
-    for (int j = 0; j < 8; ++j) {
-        a0[j & 3][j >> 2] = il.read_a(0, 0, j);
-        b0[j & 3][j >> 2] = il.read_b(0, 0, j);
+    {
+        const auto bs = il.bases(0, kBuf);
+        for (int j = 0; j < 8; ++j) {
+            a0[j & 3][j >> 2] = il.read_a(bs, 0, 0, j);
+            b0[j & 3][j >> 2] = il.read_b(bs, 0, 0, j);
+        }
     }
 
     // ---- steady state, one K-step per iteration.  (Unrolling two K-steps so
     // the buffers are addressed statically, as the 8-wave kernel does, makes
-    // the register allocator rotate the 256 accumulators through copies; the
-    // buffer offset costs one scalar select instead.)
-#pragma unroll 1
-    for (int s = 0; s < p.steps; ++s) {
+    // the register allocator rotate the 256 accumulators through copies.)
+    // The copies of K-step s+2 need the per-lane k mask only when that step
+    // is the partial last one.
+    const int tail = (p.K % kTileK) ? p.steps - 1 : -1;
+    auto kstep = [&](int s, auto mask) {
+        constexpr bool kMask = decltype(mask)::value;
         const uint32_t cur = (s & 1) ? kBuf : 0u, nxt = kBuf - cur;
+        const auto bs = il.bases(cur, nxt);
         wait_and_rendezvous();
-        il.template cluster<kBF16, true, false>(acc[0][0], a0, b0, b1, cur, 1, s + 2, cur, 0);
-        il.template cluster<kBF16, false, true>(acc[0][1], a0, b1, a1, cur, 1, s + 2, cur, 0);
+        il.template cluster<kBF16, true, false, kMask>(acc[0][0], a0, b0, b1, bs, 0, 1, s + 2, cur, 0);
+        il.template cluster<kBF16, false, true, kMask>(acc[0][1], a0, b1, a1, bs, 0, 1, s + 2, cur, 0);
         wait_and_rendezvous();
-        il.template cluster<kBF16, false, true>(acc[1][0], a1, b0, a0, nxt, 0, s + 2, cur, 1);
-        il.template cluster<kBF16, true, false>(acc[1][1], a1, b1, b0, nxt, 0, s + 2, cur, 1);
+        il.template cluster<kBF16, false, true, kMask>(acc[1][0], a1, b0, a0, bs, 1, 0, s + 2, cur, 1);
+        il.template cluster<kBF16, true, false, kMask>(acc[1][1], a1, b1, b0, bs, 1, 0, s + 2, cur, 1);
+    };
+    int s = 0;
+    if constexpr (kTransB) {
+        const int plain = tail >= 2 ? tail - 2 : (tail < 0 ? p.steps : 0);
+#pragma unroll 1
+        for (; s < plain; ++s) kstep(s, std::false_type{});
     }
+#pragma unroll 1
+    for (; s < p.steps; ++s) kstep(s, std::true_type{});
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();   // the zero-window copies of steps past the end, before LDS is released
 
