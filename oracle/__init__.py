@@ -1,16 +1,18 @@
-"""CPU oracle for the FP16/BF16 GEMM -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the FP16/BF16/FP8 GEMM -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The GPU library never calls it, and it
 imports nothing from the GPU package.
 
 The arithmetic lives in ``gemm_oracle.c`` (a plain binary64 triple loop with
-hand-written binary16/bfloat16 decoders and round-to-nearest-even encoders);
+hand-written binary16/bfloat16/FP8-E4M3 decoders and round-to-nearest-even
+encoders for the 16-bit outputs);
 this file compiles it with gcc on first use and marshals numpy arrays.
 
 Pins (the tests that tie the oracle to something other than itself):
   * decoders: exhaustive over all 65536 bit patterns against numpy (binary16)
-    and torch (bfloat16) widening;
+    and torch (bfloat16) widening, and over all 256 FP8 E4M3 patterns against
+    torch's float8_e4m3fn widening;
   * encoders: against numpy's float64->float16 rounding on random and edge
     values, and bfloat16 ties worked by hand;
   * product: exact rational brute force (fractions.Fraction) on tiny shapes,
@@ -32,7 +34,9 @@ _LIB = os.path.join(_HERE, "libgemm_oracle.so")
 _lock = threading.Lock()
 _lib = None
 
-ELEM = {"f16": 0, "bf16": 1}
+ELEM = {"f16": 0, "bf16": 1, "fp8": 2}
+# numpy dtype of an operand's bit patterns
+BITS = {"f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
 
 
 def build(force: bool = False, src: str = _SRC, out: str = _LIB, defines=()) -> str:
@@ -48,15 +52,16 @@ def build(force: bool = False, src: str = _SRC, out: str = _LIB, defines=()) -> 
 
 def _bind(path: str):
     lib = ctypes.CDLL(path)
-    i64, u16p, f64p, i64p = (ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
-                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64))
-    lib.oracle_gemm_rows.argtypes = [ctypes.c_int, i64, i64, i64, u16p, i64, u16p, i64,
+    i64, u16p, f64p, i64p, vp = (ctypes.c_int64, ctypes.POINTER(ctypes.c_uint16),
+                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                 ctypes.c_void_p)
+    lib.oracle_gemm_rows.argtypes = [ctypes.c_int, i64, i64, i64, vp, i64, vp, i64,
                                      ctypes.c_int, i64, i64, f64p, f64p, ctypes.c_int]
     lib.oracle_gemm_rows.restype = ctypes.c_int
-    lib.oracle_gemm_points.argtypes = [ctypes.c_int, i64, i64, i64, u16p, i64, u16p, i64,
+    lib.oracle_gemm_points.argtypes = [ctypes.c_int, i64, i64, i64, vp, i64, vp, i64,
                                        ctypes.c_int, i64, i64p, i64p, f64p, f64p]
     lib.oracle_gemm_points.restype = ctypes.c_int
-    lib.oracle_decode.argtypes = [ctypes.c_int, i64, u16p, f64p]
+    lib.oracle_decode.argtypes = [ctypes.c_int, i64, vp, f64p]
     lib.oracle_decode.restype = None
     lib.oracle_round.argtypes = [ctypes.c_int, i64, f64p, u16p]
     lib.oracle_round.restype = None
@@ -67,16 +72,16 @@ def _ptr(a: np.ndarray, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
-def _u16(a) -> np.ndarray:
+def _bits(a, elem: str) -> np.ndarray:
     a = np.asarray(a)
-    if a.dtype != np.uint16:
-        raise TypeError("operands are passed as uint16 bit patterns")
+    if a.dtype != BITS[elem]:
+        raise TypeError(f"{elem} operands are passed as {np.dtype(BITS[elem]).name} bit patterns")
     return a
 
 
-def _shape_args(A, B, trans_b, K=None):
-    A = _u16(A)
-    B = _u16(B)
+def _shape_args(A, B, trans_b, elem, K=None):
+    A = _bits(A, elem)
+    B = _bits(B, elem)
     if A.ndim != 2 or B.ndim != 2 or not A.flags.c_contiguous or not B.flags.c_contiguous:
         raise ValueError("A and B must be 2-D C-contiguous arrays (row stride = shape[1])")
     M, lda = A.shape
@@ -99,14 +104,16 @@ class Oracle:
         self.lib = _bind(path)
 
     def decode(self, bits, elem: str) -> np.ndarray:
-        """Exact float64 values of FP16/BF16 bit patterns."""
-        b = np.ascontiguousarray(_u16(bits))
+        """Exact float64 values of FP16/BF16 (uint16) or FP8 E4M3 (uint8) bit patterns."""
+        b = np.ascontiguousarray(_bits(bits, elem))
         out = np.empty(b.shape, dtype=np.float64)
-        self.lib.oracle_decode(ELEM[elem], b.size, _ptr(b, ctypes.c_uint16), _ptr(out, ctypes.c_double))
+        self.lib.oracle_decode(ELEM[elem], b.size, b.ctypes.data, _ptr(out, ctypes.c_double))
         return out
 
     def round_to(self, values, elem: str) -> np.ndarray:
         """Round-to-nearest-even of float64 values into FP16/BF16 bit patterns."""
+        if elem not in ("f16", "bf16"):
+            raise ValueError("results round to f16 or bf16")
         v = np.ascontiguousarray(values, dtype=np.float64)
         out = np.empty(v.shape, dtype=np.uint16)
         self.lib.oracle_round(ELEM[elem], v.size, _ptr(v, ctypes.c_double), _ptr(out, ctypes.c_uint16))
@@ -116,16 +123,17 @@ class Oracle:
              rows: tuple[int, int] | None = None, nthreads: int | None = None, with_sabs: bool = True):
         """Cref (and Sabs) = rows of A.B in float64.
 
-        A: M x lda uint16 (first K columns used); B: K x ldb (trans_b=0, first N
-        columns used) or N x ldb (trans_b=1, first K columns used)."""
-        A, B, M, Nb, K, lda, ldb = _shape_args(A, B, trans_b, K)
+        A: M x lda bit patterns (uint16, or uint8 for fp8; first K columns
+        used); B: K x ldb (trans_b=0, first N columns used) or N x ldb
+        (trans_b=1, first K columns used)."""
+        A, B, M, Nb, K, lda, ldb = _shape_args(A, B, trans_b, elem, K)
         N = Nb if N is None else N
         r0, r1 = (0, M) if rows is None else rows
         nthreads = nthreads or min(os.cpu_count() or 1, 16)
         C = np.empty((r1 - r0, N), dtype=np.float64)
         S = np.empty((r1 - r0, N), dtype=np.float64) if with_sabs else None
-        rc = self.lib.oracle_gemm_rows(ELEM[elem], M, N, K, _ptr(A, ctypes.c_uint16), lda,
-                                       _ptr(B, ctypes.c_uint16), ldb, int(trans_b), r0, r1,
+        rc = self.lib.oracle_gemm_rows(ELEM[elem], M, N, K, A.ctypes.data, lda,
+                                       B.ctypes.data, ldb, int(trans_b), r0, r1,
                                        _ptr(C, ctypes.c_double),
                                        _ptr(S, ctypes.c_double) if S is not None else None, nthreads)
         if rc != 0:
@@ -135,14 +143,14 @@ class Oracle:
     def gemm_points(self, A, B, elem: str, trans_b: int, ii, jj, K: int | None = None,
                     N: int | None = None):
         """Cref and Sabs at the points (ii[p], jj[p])."""
-        A, B, M, Nb, K, lda, ldb = _shape_args(A, B, trans_b, K)
+        A, B, M, Nb, K, lda, ldb = _shape_args(A, B, trans_b, elem, K)
         N = Nb if N is None else N
         ii = np.ascontiguousarray(ii, dtype=np.int64)
         jj = np.ascontiguousarray(jj, dtype=np.int64)
         C = np.empty(ii.shape, dtype=np.float64)
         S = np.empty(ii.shape, dtype=np.float64)
-        rc = self.lib.oracle_gemm_points(ELEM[elem], M, N, K, _ptr(A, ctypes.c_uint16), lda,
-                                         _ptr(B, ctypes.c_uint16), ldb, int(trans_b), ii.size,
+        rc = self.lib.oracle_gemm_points(ELEM[elem], M, N, K, A.ctypes.data, lda,
+                                         B.ctypes.data, ldb, int(trans_b), ii.size,
                                          _ptr(ii, ctypes.c_int64), _ptr(jj, ctypes.c_int64),
                                          _ptr(C, ctypes.c_double), _ptr(S, ctypes.c_double))
         if rc != 0:

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for C = A . B with FP16 or BF16 operands  -- TEST INFRASTRUCTURE.
+ * CPU oracle for C = A . B with FP16, BF16 or FP8 (E4M3) operands
+ * -- TEST INFRASTRUCTURE.
  *
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
  * load this file's library.  It shares no code, header or table with the GPU
@@ -18,10 +19,10 @@
  *   b(k,j) = B[k*ldb + j]   if trans_b == 0   (B stored K x N, row-major)
  *          = B[j*ldb + k]   if trans_b == 1   (B stored N x K, row-major)
  *
- * Every operand is widened exactly to double (binary16 and bfloat16 values are
- * all representable in binary64), products are exact in binary64 (at most
- * 2 x 11 significant bits), and the sum runs over increasing k from +0.0 in
- * binary64.  Rows of C are split across threads; each element is one thread's
+ * Every operand is widened exactly to double (binary16, bfloat16 and FP8 E4M3
+ * values are all representable in binary64), products are exact in binary64
+ * (at most 2 x 11 significant bits), and the sum runs over increasing k from
+ * +0.0 in binary64.  FP8 operands are one byte per element, the others two.  Rows of C are split across threads; each element is one thread's
  * plain loop, so the result does not depend on the thread count.
  *
  * The output-rounding helpers implement round-to-nearest-even from the
@@ -68,6 +69,35 @@ double oracle_bf16_to_f64(uint16_t b)
     else
         v = ldexp((double)(128 + f), e - 134);   /* (1 + f/2^7) * 2^(e-127) */
     return sign ? -v : v;
+}
+
+/* FP8 E4M3 (the OCP 8-bit "E4M3" format with no infinities, as the FP8 MFMA
+ * of "Porting High-Performance HIP Kernels to FlyDSL", section "MFMA in
+ * FlyDSL", takes it): 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits;
+ * exponent field 15 with fraction 7 is NaN, every other pattern is finite
+ * (largest 448). */
+double oracle_fp8e4m3_to_f64(uint8_t x)
+{
+    int sign = (x >> 7) & 1;
+    int e = (x >> 3) & 0xF;
+    int f = x & 0x7;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -9);                /* f/8 * 2^(1-7) */
+    else if (e == 15 && f == 7)
+        v = NAN;
+    else
+        v = ldexp((double)(8 + f), e - 10);      /* (1 + f/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Element idx of an operand array of type elem (0 FP16, 1 BF16, 2 FP8 E4M3). */
+static double load(int elem, const void *p, int64_t idx)
+{
+    if (elem == 2)
+        return oracle_fp8e4m3_to_f64(((const uint8_t *)p)[idx]);
+    uint16_t h = ((const uint16_t *)p)[idx];
+    return elem == 0 ? oracle_f16_to_f64(h) : oracle_bf16_to_f64(h);
 }
 
 /* ---- output rounding (round to nearest, ties to even) ------------------- */
@@ -140,12 +170,10 @@ uint16_t oracle_f64_to_bf16_rne(double x)
 
 /* ---- the product -------------------------------------------------------- */
 
-typedef double (*decode_fn)(uint16_t);
-
 struct job {
-    decode_fn dec;
+    int elem;
     int64_t K, N;
-    const uint16_t *A;
+    const void *A;
     int64_t lda;
     const double *bt;      /* b(k,j) widened, stored at bt[j*K + k] */
     int64_t row0, row1;    /* rows of C computed by the whole call */
@@ -159,7 +187,7 @@ static void *rows_worker(void *p)
     double *arow = (double *)malloc(sizeof(double) * (size_t)(jb->K > 0 ? jb->K : 1));
     for (int64_t i = jb->row0 + jb->tid; i < jb->row1; i += jb->nthreads) {
         for (int64_t k = 0; k < jb->K; ++k)
-            arow[k] = jb->dec(jb->A[i * jb->lda + k]);
+            arow[k] = load(jb->elem, jb->A, i * jb->lda + k);
         for (int64_t j = 0; j < jb->N; ++j) {
             const double *bcol = jb->bt + j * jb->K;
             double s = 0.0, sa = 0.0;
@@ -179,22 +207,22 @@ static void *rows_worker(void *p)
 
 /*
  * Rows row0..row1-1 of Cref (and Sabs if S != NULL), each (row1-row0) x N
- * row-major.  elem: 0 = FP16 operands, 1 = BF16 operands.
+ * row-major.  elem: 0 = FP16 operands, 1 = BF16, 2 = FP8 E4M3 (one byte per
+ * element; leading dimensions are in elements).
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
 int oracle_gemm_rows(int elem, int64_t M, int64_t N, int64_t K,
-                     const uint16_t *A, int64_t lda,
-                     const uint16_t *B, int64_t ldb, int trans_b,
+                     const void *A, int64_t lda,
+                     const void *B, int64_t ldb, int trans_b,
                      int64_t row0, int64_t row1,
                      double *C, double *S, int nthreads)
 {
-    if (elem != 0 && elem != 1)
+    if (elem < 0 || elem > 2)
         return -1;
     if (M < 0 || N < 0 || K < 0 || row0 < 0 || row1 > M || row0 > row1)
         return -1;
     if (trans_b != 0 && trans_b != 1)
         return -1;
-    decode_fn dec = elem == 0 ? oracle_f16_to_f64 : oracle_bf16_to_f64;
     if (nthreads < 1)
         nthreads = 1;
 
@@ -203,12 +231,12 @@ int oracle_gemm_rows(int elem, int64_t M, int64_t N, int64_t K,
         return -1;
     for (int64_t k = 0; k < K; ++k)
         for (int64_t j = 0; j < N; ++j)
-            bt[j * K + k] = dec(trans_b ? B[j * ldb + k] : B[k * ldb + j]);
+            bt[j * K + k] = load(elem, B, trans_b ? j * ldb + k : k * ldb + j);
 
     pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
     struct job *jobs = (struct job *)malloc(sizeof(struct job) * (size_t)nthreads);
     for (int t = 0; t < nthreads; ++t) {
-        jobs[t] = (struct job){dec, K, N, A, lda, bt, row0, row1, C, S, t, nthreads};
+        jobs[t] = (struct job){elem, K, N, A, lda, bt, row0, row1, C, S, t, nthreads};
         if (nthreads == 1)
             rows_worker(&jobs[t]);
         else
@@ -228,24 +256,23 @@ int oracle_gemm_rows(int elem, int64_t M, int64_t N, int64_t K,
  * each point one plain k-loop.  Used for sampled checks of large products.
  */
 int oracle_gemm_points(int elem, int64_t M, int64_t N, int64_t K,
-                       const uint16_t *A, int64_t lda,
-                       const uint16_t *B, int64_t ldb, int trans_b,
+                       const void *A, int64_t lda,
+                       const void *B, int64_t ldb, int trans_b,
                        int64_t n, const int64_t *ii, const int64_t *jj,
                        double *C, double *S)
 {
-    if (elem != 0 && elem != 1)
+    if (elem < 0 || elem > 2)
         return -1;
     if (trans_b != 0 && trans_b != 1)
         return -1;
-    decode_fn dec = elem == 0 ? oracle_f16_to_f64 : oracle_bf16_to_f64;
     for (int64_t p = 0; p < n; ++p) {
         int64_t i = ii[p], j = jj[p];
         if (i < 0 || i >= M || j < 0 || j >= N)
             return -1;
         double s = 0.0, sa = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double a = dec(A[i * lda + k]);
-            double b = dec(trans_b ? B[j * ldb + k] : B[k * ldb + j]);
+            double a = load(elem, A, i * lda + k);
+            double b = load(elem, B, trans_b ? j * ldb + k : k * ldb + j);
             s += a * b;
             sa += fabs(a * b);
         }
@@ -257,10 +284,10 @@ int oracle_gemm_points(int elem, int64_t M, int64_t N, int64_t K,
 }
 
 /* Vectorised conveniences over n values (bit patterns in / out). */
-void oracle_decode(int elem, int64_t n, const uint16_t *in, double *out)
+void oracle_decode(int elem, int64_t n, const void *in, double *out)
 {
     for (int64_t p = 0; p < n; ++p)
-        out[p] = elem == 0 ? oracle_f16_to_f64(in[p]) : oracle_bf16_to_f64(in[p]);
+        out[p] = load(elem, in, p);
 }
 
 void oracle_round(int elem, int64_t n, const double *in, uint16_t *out)

@@ -1,4 +1,4 @@
-"""Seeded synthetic operands for the FP16/BF16 GEMM and for its CPU oracle.
+"""Seeded synthetic operands for the FP16/BF16/FP8 GEMM and for its CPU oracle.
 
 This module is the only code shared by the GPU path's tests/bench and the
 oracle.  It produces *input bit patterns* and the workload table; it holds
@@ -24,7 +24,9 @@ row stride in elements; padding elements get values too):
 
 The double v is rounded once to the operand type: FP16 by numpy's
 float64->float16 cast (round to nearest even), BF16 by float64->float32
-(numpy) then float32->bfloat16 (torch), both round-to-nearest-even.
+(numpy) then float32->bfloat16 (torch), FP8 E4M3 by float64->float32 then
+float32->float8_e4m3fn (torch), all round-to-nearest-even.  FP16/BF16 bit
+patterns are uint16, FP8 bit patterns uint8.
 Stream 2r holds A and 2r+1 holds B of rotation set r (r = 0 is the set
 that is checked).
 """
@@ -142,20 +144,24 @@ def values(dist: str, seed: int, stream: int, count: int, start: int = 0) -> np.
 
 
 def to_bits(v: np.ndarray, dtype: str) -> np.ndarray:
-    """Round float64 values once to FP16/BF16 and return their uint16 bit patterns."""
+    """Round float64 values once to FP16/BF16 (uint16 bit patterns) or FP8 E4M3
+    (uint8 bit patterns)."""
     if dtype == "f16":
         return v.astype(np.float16).view(np.uint16)
-    if dtype == "bf16":
+    if dtype in ("bf16", "fp8"):
         import torch
 
         f32 = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32))
-        return f32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        if dtype == "bf16":
+            return f32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        return f32.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     raise ValueError(f"unknown operand type {dtype!r}")
 
 
 def matrix_bits(dtype: str, dist: str, rows: int, cols: int, ld: int | None = None,
                 seed: int = 1, stream: int = 0, scale: float = 1.0) -> np.ndarray:
-    """A rows x ld uint16 array (row-major, row stride ld) of seeded operand bits.
+    """A rows x ld array (row-major, row stride ld) of seeded operand bits
+    (uint16 for f16/bf16, uint8 for fp8).
 
     Only the first ``cols`` columns are meant to be read; the padding columns
     hold draws too (they must never influence a result)."""
@@ -167,12 +173,12 @@ def matrix_bits(dtype: str, dist: str, rows: int, cols: int, ld: int | None = No
         out = np.empty(n, dtype=np.float16)
         _values_into(dist, seed, stream, 0, out, scale)
         return out.view(np.uint16).reshape(rows, ld)
-    out = np.empty(n, dtype=np.uint16)
+    out = np.empty(n, dtype=np.uint8 if dtype == "fp8" else np.uint16)
     buf = np.empty(min(n, _CHUNK), dtype=np.float32)
     for c0 in range(0, n, _CHUNK):
         m = min(_CHUNK, n - c0)
         _values_into(dist, seed, stream, c0, buf[:m], scale)
-        out[c0:c0 + m] = to_bits(buf[:m], "bf16")
+        out[c0:c0 + m] = to_bits(buf[:m], dtype)
     return out.reshape(rows, ld)
 
 
@@ -180,22 +186,31 @@ def matrix_bits(dtype: str, dist: str, rows: int, cols: int, ld: int | None = No
 class Workload:
     """One synthetic GEMM workload: C (MxN) = A (MxK) . B, B given KxN (trans_b=0) or NxK (trans_b=1)."""
     name: str
-    dtype: str          # "f16" | "bf16" operands
+    dtype: str          # "f16" | "bf16" | "fp8" (E4M3) operands
     M: int
     N: int
     K: int
     trans_b: int
     dist: str           # "uniform" | "normal" | "normal_scaled" (normal / sqrt(K))
-    out: str            # "same" | "f32"
+    out: str            # "same" | "f32" | "bf16" (fp8 operands: "f32" or "bf16")
     seed: int
 
     @property
     def flops(self) -> int:
         return 2 * self.M * self.N * self.K
 
+    @property
+    def elem_bytes(self) -> int:
+        return 1 if self.dtype == "fp8" else 2
+
+    @property
+    def out_type(self) -> str:
+        """Element type of C: "f16", "bf16" or "f32"."""
+        return self.dtype if self.out == "same" else self.out
+
     def algorithmic_bytes(self) -> int:
-        out_bytes = 4 if self.out == "f32" else 2
-        return 2 * (self.M * self.K + self.K * self.N) + out_bytes * self.M * self.N
+        out_bytes = 4 if self.out_type == "f32" else 2
+        return self.elem_bytes * (self.M * self.K + self.K * self.N) + out_bytes * self.M * self.N
 
     def operands(self, rotation: int = 0):
         """(A bits MxK, B bits) for rotation set ``rotation``."""
@@ -213,10 +228,11 @@ class Workload:
         return a, b
 
 
-# The five workloads: a 256^3 case the oracle finishes in seconds, a 1024^3
-# case with B given transposed, the 4096x4096x8192 FP16 compute-bound shape the
-# MI355X figures are quoted on, an 8192^3 BF16 case and a tall-skinny
-# 16384x2048x8192 case with FP32 output.
+# The workloads: a 256^3 case the oracle finishes in seconds, a 1024^3 case
+# with B given transposed, the 4096x4096x8192 FP16 compute-bound shape the
+# MI355X figures are quoted on, an 8192^3 BF16 case, a tall-skinny
+# 16384x2048x8192 case with FP32 output, and the 8192^3 FP8 E4M3 shape (B given
+# N x K, normally distributed values) an MI355X FP8 figure is quoted on.
 WORKLOADS = {
     "f16_256": Workload("f16_256", "f16", 256, 256, 256, 0, "uniform", "same", 1001),
     "f16_1024_bt": Workload("f16_1024_bt", "f16", 1024, 1024, 1024, 1, "normal_scaled", "same", 1002),
@@ -224,5 +240,6 @@ WORKLOADS = {
     "bf16_8192": Workload("bf16_8192", "bf16", 8192, 8192, 8192, 1, "normal", "same", 1004),
     "f16_16384x2048x8192_f32out": Workload("f16_16384x2048x8192_f32out", "f16", 16384, 2048, 8192, 0,
                                            "uniform", "f32", 1005),
+    "fp8_8192": Workload("fp8_8192", "fp8", 8192, 8192, 8192, 1, "normal", "bf16", 1006),
 }
 HEADLINE = "f16_4096x4096x8192"

@@ -5,7 +5,8 @@ the same checks run against the real oracle (tests/test_oracle_pins.py) and
 against deliberately broken builds of it (tests/test_oracle_mutants.py).
 
 Sources of truth used here, none of which is the oracle's own code:
-  * numpy's binary16 <-> float64 conversions and torch's bfloat16 widening;
+  * numpy's binary16 <-> float64 conversions and torch's bfloat16 and
+    float8_e4m3fn widening;
   * exact rational arithmetic (fractions.Fraction);
   * numpy.matmul in float64 and int64;
   * closed forms of special matrices (identity, permutation, all-ones,
@@ -46,15 +47,35 @@ def check_bf16_decode_exhaustive(o):
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
 
 
+def check_fp8_decode_exhaustive(o):
+    import torch
+
+    bits = np.arange(256, dtype=np.uint32).astype(np.uint8)
+    got = o.decode(bits, "fp8")
+    ref = torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2                                 # 0x7F and 0xFF only: no infinities
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
 def check_decode_worked_values(o):
     # IEEE 754 binary16 / bfloat16 encodings of a few textbook values.
     f16 = {0x3C00: 1.0, 0xC000: -2.0, 0x7BFF: 65504.0, 0x0400: 2.0 ** -14, 0x0001: 2.0 ** -24,
            0x3555: 0.333251953125, 0x8000: -0.0}
     bf16 = {0x3F80: 1.0, 0xC000: -2.0, 0x4380: 256.0, 0x4382: 260.0, 0x0080: 2.0 ** -126,
             0x0001: 2.0 ** -133, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127}
-    for elem, table in (("f16", f16), ("bf16", bf16)):
-        k = np.array(list(table), dtype=np.uint16)
-        assert np.array_equal(o.decode(k, elem), np.array(list(table.values())))
+    # FP8 E4M3 (bias 7, 3 fraction bits, no infinities): 1.0, -2.0, the
+    # largest value 448 = 1.75 * 2^8, the smallest normal 2^-6, the smallest
+    # subnormal 2^-9, 13/16 and -0.
+    fp8 = {0x38: 1.0, 0xC0: -2.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x35: 0.8125,
+           0x80: -0.0}
+    for elem, table in (("f16", f16), ("bf16", bf16), ("fp8", fp8)):
+        k = np.array(list(table), dtype=np.uint8 if elem == "fp8" else np.uint16)
+        got = o.decode(k, elem)
+        assert np.array_equal(got, np.array(list(table.values())))
+        assert np.array_equal(np.signbit(got), np.signbit(np.array(list(table.values()))))
 
 
 # ---------------------------------------------------------------- encoders
@@ -117,6 +138,8 @@ def _decode_ref(bits, elem):
     if elem == "f16":
         return bits.view(np.float16).astype(np.float64)
     import torch
+    if elem == "fp8":
+        return torch.from_numpy(bits.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
 
 
@@ -127,7 +150,7 @@ def _bhat(b, trans_b, K, N):
 
 def check_bruteforce_fraction(o):
     rng_shapes = [(1, 1, 1), (2, 3, 7), (3, 7, 2), (7, 2, 33), (16, 3, 16), (3, 33, 16), (33, 16, 3)]
-    for elem in ("f16", "bf16"):
+    for elem in ("f16", "bf16", "fp8"):
         for trans_b in (0, 1):
             for s, (M, N, K) in enumerate(rng_shapes):
                 a = matrix_bits(elem, "uniform", M, K, ld=K + 3, seed=11 + s, stream=0)
@@ -146,7 +169,7 @@ def check_bruteforce_fraction(o):
 
 
 def check_numpy_matmul(o):
-    for elem in ("f16", "bf16"):
+    for elem in ("f16", "bf16", "fp8"):
         for trans_b in (0, 1):
             M, N, K = 67, 45, 301
             a = matrix_bits(elem, "normal", M, K, ld=K + 11, seed=5, stream=0)
@@ -219,7 +242,7 @@ def check_rank_one(o):
 
 
 def check_integer_regime(o):
-    for elem in ("f16", "bf16"):
+    for elem in ("f16", "bf16", "fp8"):
         for trans_b in (0, 1):
             M, N, K = 40, 33, 512
             a = matrix_bits(elem, "int5", M, K, seed=21, stream=0)
@@ -244,7 +267,8 @@ def check_layouts_agree(o):
     assert np.array_equal(Cp, C0[ii, jj])
 
 
-ALL_CHECKS = [check_f16_decode_exhaustive, check_bf16_decode_exhaustive, check_decode_worked_values,
+ALL_CHECKS = [check_f16_decode_exhaustive, check_bf16_decode_exhaustive, check_fp8_decode_exhaustive,
+              check_decode_worked_values,
               check_f16_round_vs_numpy, check_round_worked_ties, check_bf16_round_ties,
               check_bruteforce_fraction, check_numpy_matmul, check_identity_and_permutation,
               check_all_ones, check_rank_one, check_integer_regime, check_layouts_agree]

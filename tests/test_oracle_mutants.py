@@ -13,10 +13,10 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "gemm_oracle.c")
 MUTANTS = [
     ("dropped_last_term", "double p = arow[k] * bcol[k];",
      "double p = (k == jb->K - 1) ? 0.0 : arow[k] * bcol[k];"),
-    ("transposed_B_operand", "bt[j * K + k] = dec(trans_b ? B[j * ldb + k] : B[k * ldb + j]);",
-     "bt[j * K + k] = dec(trans_b ? B[k * ldb + j] : B[j * ldb + k]);"),
-    ("ignores_lda_padding", "arow[k] = jb->dec(jb->A[i * jb->lda + k]);",
-     "arow[k] = jb->dec(jb->A[i * jb->K + k]);"),
+    ("transposed_B_operand", "bt[j * K + k] = load(elem, B, trans_b ? j * ldb + k : k * ldb + j);",
+     "bt[j * K + k] = load(elem, B, trans_b ? k * ldb + j : j * ldb + k);"),
+    ("ignores_lda_padding", "arow[k] = load(jb->elem, jb->A, i * jb->lda + k);",
+     "arow[k] = load(jb->elem, jb->A, i * jb->K + k);"),
     ("f16_exponent_bias_off_by_one", "v = ldexp((double)(1024 + f), e - 25);",
      "v = ldexp((double)(1024 + f), e - 24);"),
     ("bf16_sign_dropped", "        v = ldexp((double)(128 + f), e - 134);   /* (1 + f/2^7) * 2^(e-127) */\n    return sign ? -v : v;",
@@ -25,7 +25,11 @@ MUTANTS = [
      "if (rem >= 0.5)"),
     ("sabs_without_abs", "sa += fabs(p);", "sa += p;"),
     ("f16_subnormal_scale", "v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
-    ("points_wrong_row", "double a = dec(A[i * lda + k]);", "double a = dec(A[j * lda + k]);"),
+    ("points_wrong_row", "double a = load(elem, A, i * lda + k);", "double a = load(elem, A, j * lda + k);"),
+    ("fp8_exponent_bias_off_by_one", "v = ldexp((double)(8 + f), e - 10);", "v = ldexp((double)(8 + f), e - 11);"),
+    ("fp8_top_binade_as_nan", "else if (e == 15 && f == 7)", "else if (e == 15)"),
+    ("fp8_read_as_two_bytes", "if (elem == 2)\n        return oracle_fp8e4m3_to_f64(((const uint8_t *)p)[idx]);",
+     "if (elem == 2)\n        return oracle_fp8e4m3_to_f64(((const uint8_t *)p)[2 * idx]);"),
 ]
 
 
