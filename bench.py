@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the gfx950 warp-pipelined GEMM; prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--schedule S] [--gpus 1]
 
-A step is one C = A.B launch of the whole product (FP16 operands, FP32
-accumulation, FP16 output) on the compute-bound 4096x4096x8192 shape, on
-inputs already resident in HBM.  Inputs are seeded synthetic matrices (A and
+A step is one C = A.B launch of the whole product (by default FP16 operands,
+FP32 accumulation, FP16 output on the compute-bound 4096x4096x8192 shape; the
+other workloads include 8192^3 BF16 and 8192^3 FP8 E4M3), on inputs already
+resident in HBM.  Inputs are seeded synthetic matrices (A and
 B uniform in [-1, 1), B given N x K); enough rotating input sets are kept on
 the device that one pass over them exceeds the 256 MB last-level cache, and
 consecutive steps use consecutive sets.  Warm-up launches are untimed; the K
@@ -31,13 +32,16 @@ sys.path.insert(0, ROOT)
 import seeded_inputs as si  # noqa: E402
 
 METRIC = "FP16 GEMM TFLOP/s at M=N=4096,K=8192 and % of MI355X MFMA peak"
-# Published MI355X dense MFMA peak for FP16/BF16 (TFLOP/s).
-PEAK_TFLOPS = 2500.0
-# 256 CUs x 4 SIMDs x 1024 FLOP/clk x 2.4 GHz, the same peak from the unit counts.
-PEAK_TFLOPS_UNITS = 256 * 4 * 1024 * 2.4e9 / 1e12
-# The pages' MI355X figure for this exact metric and shape (8-wave warp-pipelined
-# Triton kernel, FP16, M=N=4096, K=8192): context for vs_baseline.
-PAGES_TFLOPS = {"f16_4096x4096x8192": 1437.0}
+# Published MI355X dense MFMA peaks (TFLOP/s) per operand type.
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}
+# 256 CUs x 4 SIMDs x FLOP/clk (1024 FP16/BF16, 2048 FP8) x 2.4 GHz: the same
+# peaks from the unit counts.
+PEAK_TFLOPS_UNITS = {"f16": 256 * 4 * 1024 * 2.4e9 / 1e12, "bf16": 256 * 4 * 1024 * 2.4e9 / 1e12,
+                     "fp8": 256 * 4 * 2048 * 2.4e9 / 1e12}
+# The pages' MI355X figures for these exact shapes: the 8-wave warp-pipelined
+# Triton kernel (FP16, M=N=4096, K=8192) and the hand-written 4-wave HIP C++
+# FP8 kernel at matrix size 8192.  Context for vs_baseline.
+PAGES_TFLOPS = {"f16_4096x4096x8192": 1437.0, "fp8_8192": 3292.0}
 MALL_BYTES = 256 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def traffic_for(workload: str, schedule: str):
@@ -127,14 +131,16 @@ def main(argv=None) -> int:
     mcs.load()
 
     w = si.WORKLOADS[a.workload]
-    tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
-    set_bytes = 2 * (w.M * w.K + w.K * w.N)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]
+    set_bytes = w.elem_bytes * (w.M * w.K + w.K * w.N)
     nrot = max(1, math.ceil(2 * MALL_BYTES / set_bytes))
     dev = torch.device("cuda:0")
     print(f"[bench] workload {w.name}: generating {nrot} rotating input sets", file=sys.stderr, flush=True)
 
     def to_dev(bits):
-        return torch.from_numpy(bits.reshape(-1).view(np.int16)).to(dev).view(tdt)
+        raw = bits.reshape(-1)
+        raw = raw if w.dtype == "fp8" else raw.view(np.int16)
+        return torch.from_numpy(raw).to(dev).view(tdt)
 
     host0 = None
     sets = []
@@ -144,17 +150,17 @@ def main(argv=None) -> int:
             host0 = (ab, bb)
         sets.append((to_dev(ab), to_dev(bb)))
         del ab, bb
-    cdt = torch.float32 if w.out == "f32" else tdt
+    cdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[w.out_type]
     outs = [torch.empty(w.M * w.N, dtype=cdt, device=dev) for _ in range(nrot)]
-    out_type = mcs.GEMM_OUT_F32 if w.out == "f32" else mcs.GEMM_OUT_SAME
-    dtype = mcs.GEMM_DTYPE_F16 if w.dtype == "f16" else mcs.GEMM_DTYPE_BF16
+    out_type = {"same": mcs.GEMM_OUT_SAME, "f32": mcs.GEMM_OUT_F32, "bf16": mcs.GEMM_OUT_BF16}[w.out]
+    dtype = {"f16": mcs.GEMM_DTYPE_F16, "bf16": mcs.GEMM_DTYPE_BF16, "fp8": mcs.GEMM_DTYPE_FP8_E4M3}[w.dtype]
     sched = {"auto": mcs.GEMM_SCHED_AUTO, "pipelined": mcs.GEMM_SCHED_PIPELINED,
              "in_phase": mcs.GEMM_SCHED_IN_PHASE, "interleaved": mcs.GEMM_SCHED_INTERLEAVED,
              "generic": mcs.GEMM_SCHED_GENERIC}[a.schedule]
     lda, ldb, ldc = w.K, (w.K if w.trans_b else w.N), w.N
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
-    fn = mcs.load().gemm_f16 if w.dtype == "f16" else mcs.load().gemm_bf16
+    fn = {"f16": mcs.load().gemm_f16, "bf16": mcs.load().gemm_bf16, "fp8": mcs.load().gemm_fp8}[w.dtype]
 
     def launch(i):
         A, B = sets[i % nrot]
@@ -236,19 +242,22 @@ def main(argv=None) -> int:
                "sample": f"output rows [0,{half}) and [{w.M - half},{w.M}) of the same product "
                          f"({rows}x{w.N}x{w.K}), {cpu_s:.1f} s on {cpu_model()}"}
         Cg = outs[0].view(w.M, w.N).cpu()
-        if w.out == "f32":
+        if w.out_type == "f32":
             cg = Cg.double().numpy()
         else:
-            cg = oracle.decode(Cg.view(torch.int16).numpy().view(np.uint16), w.dtype)
+            cg = oracle.decode(Cg.view(torch.int16).numpy().view(np.uint16), w.out_type)
         bad = 0
         for (r0, r1), (cref, sabs) in zip(blocks, refs):
-            bad += int((~oracle.within_tolerance(cg[r0:r1], cref, sabs,
-                                                  out=w.dtype if w.out == "same" else "f32")).sum())
+            bad += int((~oracle.within_tolerance(cg[r0:r1], cref, sabs, out=w.out_type)).sum())
         check = {"rows": rows, "elements": rows * w.N, "outside_tolerance": bad, "pass": bad == 0}
 
     traffic = traffic_for(w.name, a.schedule)
+    peak = PEAK_TFLOPS[w.dtype]
+    metric = METRIC if w.name == si.HEADLINE else (
+        f"{ {'f16': 'FP16', 'bf16': 'BF16', 'fp8': 'FP8 E4M3'}[w.dtype]} GEMM TFLOP/s at "
+        f"M={w.M},N={w.N},K={w.K} and % of MI355X MFMA peak")
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -261,16 +270,16 @@ def main(argv=None) -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "operands": w.dtype,
-                   "accumulate": "f32", "out": w.dtype if w.out == "same" else "f32",
+                   "accumulate": "f32", "out": w.out_type,
                    "b_layout": "N x K row-major" if w.trans_b else "K x N row-major",
                    "values": w.dist, "seed": w.seed, "rotating_sets": nrot,
                    "schedule": a.schedule},
-        "pct_of_peak": round(100.0 * tflops / PEAK_TFLOPS, 2),
-        "pct_of_unit_peak": round(100.0 * tflops / PEAK_TFLOPS_UNITS, 2),
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "pct_of_unit_peak": round(100.0 * tflops / PEAK_TFLOPS_UNITS[w.dtype], 2),
         "batch_median_ms": round(batch_med, 6),
         "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": traffic},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
         "kernel": {"vgprs": info["num_regs"], "scratch_bytes_per_lane": info["local_bytes"],
                    "lds_bytes": info["shared_bytes"], "threads": info["block_threads"]},
         "cpu_baseline": cpu,

@@ -1,8 +1,9 @@
 /*
  * mcs_gemm.h -- C ABI of libmcs_gemm.so, a gfx950 (MI355X) dense GEMM
  *
- *     C = A . B        FP16 or BF16 operands, FP32 accumulation,
- *                      FP16/BF16 (same as the operands) or FP32 output.
+ *     C = A . B        FP16, BF16 or FP8 (E4M3) operands, FP32 accumulation,
+ *                      FP16/BF16 (same as the operands; BF16 for FP8
+ *                      operands) or FP32 output.
  *
  * The operation is the tiled dense product of "Two Waves, One Stage Apart:
  * Warp-Pipelining Triton GEMMs on AMD Instinct" (opening section: a tiled
@@ -12,7 +13,9 @@
  * "Creating and Closing the Offset", "MI350 Series (gfx950, CDNA 4): Three
  * Overlapping Flows"); its buffer-resource loads with out-of-range reads
  * returning zero follow "Porting High-Performance HIP Kernels to FlyDSL",
- * section "Buffer Resource Descriptors".
+ * section "Buffer Resource Descriptors".  The FP8 product is the second GEMM
+ * of that page (section "MFMA in FlyDSL": E4M3 operands through the scaled
+ * 16x16x128 MFMA with unit scales, B given transposed).
  *
  * Definition (every element, exactly up to FP32 rounding):
  *     C[i*ldc + j] = sum_{k<K} A[i*lda + k] * b(k, j)
@@ -56,13 +59,15 @@ enum gemm_status {
 };
 
 enum gemm_out_type {
-    GEMM_OUT_SAME = 0,   /* FP16 for gemm_f16, BF16 for gemm_bf16 */
-    GEMM_OUT_F32 = 1
+    GEMM_OUT_SAME = 0,   /* FP16 for gemm_f16, BF16 for gemm_bf16; not for FP8 */
+    GEMM_OUT_F32 = 1,
+    GEMM_OUT_BF16 = 2    /* BF16: FP8 and BF16 operands */
 };
 
 enum gemm_dtype {
     GEMM_DTYPE_F16 = 0,
-    GEMM_DTYPE_BF16 = 1
+    GEMM_DTYPE_BF16 = 1,
+    GEMM_DTYPE_FP8_E4M3 = 2   /* OCP FP8 E4M3 (no infinities), one byte */
 };
 
 /* Kernel schedule selector for gemm_ex. */
@@ -105,11 +110,26 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
               hipStream_t stream);
 
 /*
+ * gemm_fp8 -- C = A . B with FP8 E4M3 operands (one byte per element, leading
+ * dimensions in elements), FP32 accumulation; out_type GEMM_OUT_BF16 or
+ * GEMM_OUT_F32 (GEMM_OUT_SAME is GEMM_EINVAL).  Other arguments as gemm_f16.
+ * The fast kernels take B given N x K (trans_b = 1); B given K x N runs the
+ * generic kernel.  NaN operands (0x7F, 0xFF) propagate.
+ */
+int gemm_fp8(int64_t M, int64_t N, int64_t K,
+             const void *A, int64_t lda,
+             const void *B, int64_t ldb, int trans_b,
+             void *C, int64_t ldc, int out_type,
+             hipStream_t stream);
+
+/*
  * gemm_ex -- the same product with the operand type (gemm_dtype) and the
  * kernel schedule (gemm_schedule) chosen by the caller.  PIPELINED,
- * IN_PHASE and INTERLEAVED need 16-byte aligned A, B, C, lda/ldb/ldc and K
- * multiples of 8, and an even N when B is K x N; asking for them otherwise
- * returns GEMM_EINVAL (nothing is launched).
+ * IN_PHASE and INTERLEAVED need 16-byte aligned A, B, C, rows of A and B
+ * (lda, ldb times the element size) and of K elements that are whole 16-byte
+ * chunks, ldc a multiple of 8, and an even N when B is K x N (FP8: B given
+ * N x K); asking for them otherwise returns GEMM_EINVAL (nothing is
+ * launched).
  */
 int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K,
             const void *A, int64_t lda,
@@ -130,7 +150,8 @@ typedef struct gemm_kernel_attrs {
 /*
  * gemm_kernel_info -- attributes of the kernel gemm_ex would launch for
  * (dtype, trans_b, out_type, schedule).  Needs a HIP device.  Returns a
- * gemm_status; *out is filled on GEMM_OK.
+ * gemm_status (GEMM_EUNSUPPORTED for a combination no 256x256 kernel is
+ * compiled for: FP8 with B given K x N); *out is filled on GEMM_OK.
  */
 int gemm_kernel_info(int dtype, int trans_b, int out_type, int schedule,
                      gemm_kernel_attrs *out);

@@ -1,7 +1,8 @@
-"""Python binding of libmcs_gemm.so, the gfx950 warp-pipelined FP16/BF16 GEMM.
+"""Python binding of libmcs_gemm.so, the gfx950 warp-pipelined FP16/BF16/FP8 GEMM.
 
-The functions ``gemm_f16``, ``gemm_bf16``, ``gemm_ex``, ``gemm_kernel_info`` and
-``gemm_status_string`` mirror the C ABI in ``include/mcs_gemm.h`` one to one
+The functions ``gemm_f16``, ``gemm_bf16``, ``gemm_fp8``, ``gemm_ex``,
+``gemm_kernel_info`` and ``gemm_status_string`` mirror the C ABI in
+``include/mcs_gemm.h`` one to one
 (sizes, raw device pointers as integers, a raw ``hipStream_t``).  ``gemm``
 marshals torch tensors onto them: torch provides device memory and the
 current stream, every step of the product runs in the library's HIP kernels.
@@ -20,8 +21,8 @@ LIBRARY = os.path.join(_PKG, "libmcs_gemm.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "mcs_gemm.h")
 
 GEMM_OK, GEMM_EINVAL, GEMM_EUNSUPPORTED, GEMM_EHIP = 0, -1, -3, -4
-GEMM_OUT_SAME, GEMM_OUT_F32 = 0, 1
-GEMM_DTYPE_F16, GEMM_DTYPE_BF16 = 0, 1
+GEMM_OUT_SAME, GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1, 2
+GEMM_DTYPE_F16, GEMM_DTYPE_BF16, GEMM_DTYPE_FP8_E4M3 = 0, 1, 2
 GEMM_SCHED_AUTO, GEMM_SCHED_PIPELINED, GEMM_SCHED_IN_PHASE, GEMM_SCHED_GENERIC, GEMM_SCHED_INTERLEAVED = 0, 1, 2, 3, 4
 
 
@@ -51,7 +52,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     sig = [i64, i64, i64, vp, i64, vp, i64, ci, vp, i64, ci]
-    for name in ("gemm_f16", "gemm_bf16"):
+    for name in ("gemm_f16", "gemm_bf16", "gemm_fp8"):
         f = getattr(lib, name)
         f.argtypes = sig + [vp]
         f.restype = ci
@@ -79,6 +80,10 @@ def gemm_f16(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream) -> int:
 
 def gemm_bf16(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream) -> int:
     return load().gemm_bf16(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream)
+
+
+def gemm_fp8(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream) -> int:
+    return load().gemm_fp8(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream)
 
 
 def gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream) -> int:
@@ -109,16 +114,18 @@ def gemm(A, B, trans_b: bool = False, out=None, out_dtype=None,
          schedule: int = GEMM_SCHED_AUTO, stream=None):
     """C = A @ B (trans_b=False, B is K x N) or A @ B.T (trans_b=True, B is N x K).
 
-    A, B: 2-D float16/bfloat16 CUDA tensors with unit column stride (rows may
-    be padded: the row stride is passed as the leading dimension).  ``out``
-    (M x N, unit column stride) is written in place if given; otherwise a
-    tensor of ``out_dtype`` (default: the operand dtype; float32 allowed) is
-    allocated by torch.  Runs on the current stream (or ``stream``) and does
-    not synchronise."""
+    A, B: 2-D float16, bfloat16 or float8_e4m3fn CUDA tensors with unit
+    column stride (rows may be padded: the row stride is passed as the
+    leading dimension).  ``out`` (M x N, unit column stride) is written in
+    place if given; otherwise a tensor of ``out_dtype`` is allocated by torch
+    (default: the operand dtype, bfloat16 for FP8 operands; float32 allowed).
+    Runs on the current stream (or ``stream``) and does not synchronise."""
     import torch
 
-    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
-        raise TypeError("A and B must both be float16 or both bfloat16")
+    dtypes = {torch.float16: GEMM_DTYPE_F16, torch.bfloat16: GEMM_DTYPE_BF16,
+              torch.float8_e4m3fn: GEMM_DTYPE_FP8_E4M3}
+    if A.dtype != B.dtype or A.dtype not in dtypes:
+        raise TypeError("A and B must both be float16, bfloat16 or float8_e4m3fn")
     if A.dim() != 2 or B.dim() != 2:
         raise ValueError("A and B must be 2-D")
     if A.stride(1) != 1 or B.stride(1) != 1:
@@ -130,17 +137,20 @@ def gemm(A, B, trans_b: bool = False, out=None, out_dtype=None,
         Kb, N = B.shape
     if Kb != K:
         raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    fp8 = A.dtype == torch.float8_e4m3fn
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
+        out = torch.empty((M, N), dtype=out_dtype or (torch.bfloat16 if fp8 else A.dtype), device=A.device)
     if out.shape != (M, N) or (out.stride(1) != 1 and N > 1):
         raise ValueError("out must be M x N with unit column stride")
     if out.dtype == torch.float32:
         out_type = GEMM_OUT_F32
-    elif out.dtype == A.dtype:
+    elif out.dtype == torch.bfloat16 and A.dtype != torch.float16:
+        out_type = GEMM_OUT_BF16
+    elif out.dtype == A.dtype and not fp8:
         out_type = GEMM_OUT_SAME
     else:
-        raise TypeError("out must have the operand dtype or float32")
-    dtype = GEMM_DTYPE_F16 if A.dtype == torch.float16 else GEMM_DTYPE_BF16
+        raise TypeError("out must be float32, or the operand dtype (bfloat16 for FP8 operands)")
+    dtype = dtypes[A.dtype]
     lda = A.stride(0) if M > 1 else max(K, 1)
     ldb = B.stride(0) if B.shape[0] > 1 else max(B.shape[1], 1)
     ldc = out.stride(0) if M > 1 else max(N, 1)

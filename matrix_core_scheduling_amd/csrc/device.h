@@ -15,6 +15,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -27,9 +28,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // LDS: two buffers (one per K-step in flight), each [A0 | A1 | B0 | B1]
 // halves of 16 KiB.  An A half (and a B half when B is N x K) is 128 rows x
-// 64 k, 128-byte rows of eight 16-byte chunks stored at chunk ^ (row & 7).  A
-// B half when B is K x N is 64 k-rows x 128 n, 256-byte rows with chunk ^
-// 2*((k & 3) + 4*((k >> 3) & 1)), read with ds_read_b64_tr_b16.
+// 128 bytes of k (64 FP16/BF16 or 128 FP8 elements), eight 16-byte chunks per
+// row stored at chunk ^ (row & 7).  A B half when B is K x N (16-bit operands
+// only) is 64 k-rows x 128 n, 256-byte rows with chunk ^ 2*((k & 3) + 4*((k >>
+// 3) & 1)), read with ds_read_b64_tr_b16.
 constexpr uint32_t kHalf = 16384;          // bytes of one operand half in LDS
 constexpr uint32_t kBuf = 4 * kHalf;       // one K-step: A0 A1 B0 B1
 constexpr uint32_t kOffA = 0, kOffB = 2 * kHalf;
@@ -110,14 +112,29 @@ __device__ __forceinline__ i32x2 lds_read64_tr(uint32_t addr) {
     return __builtin_bit_cast(i32x2, v);
 }
 
-template <bool kBF16>
+// One 16x16x32 FP16/BF16 MFMA: x holds the 16-column operand (k-slice of
+// 8 elements per lane), y the 16-row operand.
+template <int kElem>
 __device__ __forceinline__ f32x4 mfma(i32x4 x, i32x4 y, f32x4 c) {
-    if constexpr (kBF16)
+    static_assert(kElem != kElemFP8, "FP8 takes mfma_fp8");
+    if constexpr (kElem == kElemBF16)
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
                                                        __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
     else
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x),
                                                       __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
+}
+
+// One 16x16x128 FP8 E4M3 MFMA (the scaled f8f6f4 form with the identity
+// scale 2^0 = E8M0 0x7F in every byte, operand formats 0 = E4M3, as in
+// "Porting High-Performance HIP Kernels to FlyDSL", section "MFMA in
+// FlyDSL").  A lane's 32 bytes of each operand are the same two 16-byte LDS
+// chunks a FP16 lane reads for its two k-slices; both operands use the same
+// lane -> k assignment, so the sum runs over the whole 128-deep K-step.
+__device__ __forceinline__ f32x4 mfma_fp8(i32x4 x0, i32x4 x1, i32x4 y0, i32x4 y1, f32x4 c) {
+    const i32x8 x = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const i32x8 y = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
 }
 
 // 32-bit LDS byte address of a __shared__ array.
@@ -137,27 +154,29 @@ __device__ __forceinline__ uint32_t lds_address(T *smem) {
 // the copy itself writes the XOR-swizzled layout.  A piece of a B half given
 // K x N is 4 k-rows x 256 bytes, swizzled the same way for the transposing
 // read.
-template <bool kTransB, int kWaves>
+template <int kElem, bool kTransB, int kWaves>
 struct Loader {
     static constexpr int P = 16 / kWaves;   // pieces per wave per half
+    static constexpr int kEB = elem_bytes(kElem), kStepK = step_k(kElem);
     static_assert(P * kWaves == 16, "waves must divide the 16 pieces of a half");
+    static_assert(kTransB || kElem != kElemFP8, "FP8 B is taken given N x K");
 
     uint32_t lds0;                   // LDS byte address of buffer 0
     uint32_t cpA[P], cpB[P];         // copy voffsets
-    int cpAchunk[P];                 // k-chunk (of 8) each A / N x K B copy lane moves
+    int cpAchunk[P];                 // 16-byte k-chunk (of 8) each A / N x K B copy lane moves
     int wave;
     const GemmParams &p;
     int m0, n0;
     // Per-half copy windows (uniform, computed once) of A and of B given N x
     // K: byte address of the half's first row at k = 0, the window's extent at
-    // k = 0 (start of the last valid row + 2K bytes), and 2K, or 0 when the
-    // half holds no valid row.  At K-step s the window starts 128*s bytes on
-    // and holds data while 128*s < 2K.
+    // k = 0 (start of the last valid row + the K elements' bytes KB), and KB,
+    // or 0 when the half holds no valid row.  At K-step s the window starts
+    // 128*s bytes on and holds data while 128*s < KB.
     uint64_t aAddr[2], bAddr[2];
-    uint32_t aEnd[2], bEnd[2], aK2[2], bK2[2];
+    uint32_t aEnd[2], bEnd[2], aKB[2], bKB[2];
     // B given K x N: first column of the half, bytes of one k-row's valid
     // columns, and whether the half holds any valid column
-    const uint16_t *bBase[2];
+    const char *bBase[2];
     uint32_t bSpan[2];
     bool bLive[2];
 
@@ -168,21 +187,22 @@ struct Loader {
         m0 = tm * kTileM;
         n0 = tn * kTileN;
         lds0 = 0;
-        const uint32_t k2 = 2u * static_cast<uint32_t>(p.K);
+        const uint32_t kb = static_cast<uint32_t>(kEB) * static_cast<uint32_t>(p.K);
+        const char *A = static_cast<const char *>(p.A), *B = static_cast<const char *>(p.B);
         for (int h = 0; h < 2; ++h) {
             const int rows = min(max(p.M - (m0 + 128 * h), 0), 128);
-            aAddr[h] = reinterpret_cast<uint64_t>(p.A + (int64_t)(m0 + 128 * h) * p.lda);
-            aEnd[h] = rows > 0 ? static_cast<uint32_t>((rows - 1) * p.lda * 2) + k2 : 0u;
-            aK2[h] = rows > 0 ? k2 : 0u;
+            aAddr[h] = reinterpret_cast<uint64_t>(A + (int64_t)(m0 + 128 * h) * p.lda * kEB);
+            aEnd[h] = rows > 0 ? static_cast<uint32_t>((rows - 1) * p.lda * kEB) + kb : 0u;
+            aKB[h] = rows > 0 ? kb : 0u;
             const int cols = min(max(p.N - (n0 + 128 * h), 0), 128);
             if constexpr (kTransB) {
-                bAddr[h] = reinterpret_cast<uint64_t>(p.B + (int64_t)(n0 + 128 * h) * p.ldb);
-                bEnd[h] = cols > 0 ? static_cast<uint32_t>((cols - 1) * p.ldb * 2) + k2 : 0u;
-                bK2[h] = cols > 0 ? k2 : 0u;
+                bAddr[h] = reinterpret_cast<uint64_t>(B + (int64_t)(n0 + 128 * h) * p.ldb * kEB);
+                bEnd[h] = cols > 0 ? static_cast<uint32_t>((cols - 1) * p.ldb * kEB) + kb : 0u;
+                bKB[h] = cols > 0 ? kb : 0u;
             } else {
                 bLive[h] = cols > 0;
-                bBase[h] = p.B + n0 + 128 * h;
-                bSpan[h] = static_cast<uint32_t>(cols * 2);
+                bBase[h] = B + (n0 + 128 * h) * kEB;
+                bSpan[h] = static_cast<uint32_t>(cols * kEB);
             }
         }
         const int x = lane >> 3, pch = lane & 7;
@@ -190,28 +210,28 @@ struct Loader {
             const int row = 8 * (P * wave + i) + x;           // row of the half
             const int c = pch ^ x;                             // logical 16-byte k-chunk (row & 7 = x)
             cpAchunk[i] = c;
-            cpA[i] = static_cast<uint32_t>(row * p.lda * 2 + c * 16);
+            cpA[i] = static_cast<uint32_t>(row * p.lda * kEB + c * 16);
             if constexpr (kTransB)
-                cpB[i] = static_cast<uint32_t>(row * p.ldb * 2 + c * 16);
+                cpB[i] = static_cast<uint32_t>(row * p.ldb * kEB + c * 16);
         }
         if constexpr (!kTransB) {
             const int y = lane >> 4, pc = lane & 15;
             for (int i = 0; i < P; ++i) {
                 const int krow = 4 * (P * wave + i) + y;
                 const int ch = pc ^ (2 * ((krow & 3) + 4 * ((krow >> 3) & 1)));   // logical n-chunk
-                cpB[i] = static_cast<uint32_t>(krow * p.ldb * 2 + ch * 16);
+                cpB[i] = static_cast<uint32_t>(krow * p.ldb * kEB + ch * 16);
             }
         }
     }
 
     // Buffer resource of a row-major (k contiguous) half at K-step s.
-    static __device__ __forceinline__ i32x4 step_rsrc(uint64_t addr, uint32_t end, uint32_t k2, int s) {
-        const uint32_t koff = static_cast<uint32_t>(s) * (2 * kTileK);
+    static __device__ __forceinline__ i32x4 step_rsrc(uint64_t addr, uint32_t end, uint32_t kb, int s) {
+        const uint32_t koff = static_cast<uint32_t>(s) * kStepBytes;
         const uint64_t a = addr + koff;
         i32x4 r;
         r.x = static_cast<int>(static_cast<uint32_t>(a));
         r.y = static_cast<int>(static_cast<uint32_t>(a >> 32));   // < 2^16: stride 0
-        r.z = static_cast<int>(koff < k2 ? end - koff : 0u);
+        r.z = static_cast<int>(koff < kb ? end - koff : 0u);
         r.w = 0x00020000;
         return r;
     }
@@ -224,11 +244,11 @@ struct Loader {
     // either whole (64 k left) or wholly past the end.
     template <bool kMask = true, int I0 = 0, int I1 = P>
     __device__ __forceinline__ void copy_a(int s, uint32_t buf, int h) const {
-        const int kv = p.K - s * kTileK;                      // k left (may be <= 0)
-        const i32x4 rs = step_rsrc(aAddr[h], aEnd[h], aK2[h], s);
+        const int kvb = (p.K - s * kStepK) * kEB;             // bytes of k left (may be <= 0)
+        const i32x4 rs = step_rsrc(aAddr[h], aEnd[h], aKB[h], s);
         const uint32_t dst = lds0 + buf + kOffA + h * kHalf + P * wave * 1024;
         static_for<I0, I1>([&](auto i) {
-            const uint32_t v = (!kMask || cpAchunk[i] * 8 < kv) ? cpA[i] : kOutOfWindow;
+            const uint32_t v = (!kMask || cpAchunk[i] * 16 < kvb) ? cpA[i] : kOutOfWindow;
             copy16<i * 1024>(rs, dst, v);
         });
     }
@@ -236,21 +256,21 @@ struct Loader {
     // Copy half h of operand B (columns n0+128h..) for K-step s into buffer `buf`.
     template <bool kMask = true, int I0 = 0, int I1 = P>
     __device__ __forceinline__ void copy_b(int s, uint32_t buf, int h) const {
-        const int kv = p.K - s * kTileK;
+        const int kv = p.K - s * kStepK;                      // k left (may be <= 0)
         const uint32_t dst = lds0 + buf + kOffB + h * kHalf + P * wave * 1024;
         if constexpr (kTransB) {
-            const i32x4 rs = step_rsrc(bAddr[h], bEnd[h], bK2[h], s);
+            const i32x4 rs = step_rsrc(bAddr[h], bEnd[h], bKB[h], s);
             static_for<I0, I1>([&](auto i) {
-                const uint32_t v = (!kMask || cpAchunk[i] * 8 < kv) ? cpB[i] : kOutOfWindow;
+                const uint32_t v = (!kMask || cpAchunk[i] * 16 < kv * kEB) ? cpB[i] : kOutOfWindow;
                 copy16<i * 1024>(rs, dst, v);
             });
         } else {
             // k-rows k0 .. k0+rows-1; the window ends at the last valid column
             // of the last valid k-row, so k-rows >= K read 0 without a mask
-            const int rows = min(kv, kTileK);
+            const int rows = min(kv, kStepK);
             const uint32_t nrec = (bLive[h] && kv > 0)
-                ? static_cast<uint32_t>(rows - 1) * static_cast<uint32_t>(p.ldb * 2) + bSpan[h] : 0u;
-            const i32x4 rs = make_rsrc(bBase[h] + (int64_t)s * kTileK * p.ldb, nrec);
+                ? static_cast<uint32_t>(rows - 1) * static_cast<uint32_t>(p.ldb * kEB) + bSpan[h] : 0u;
+            const i32x4 rs = make_rsrc(bBase[h] + (int64_t)s * kStepK * p.ldb * kEB, nrec);
             static_for<I0, I1>([&](auto i) { copy16<i * 1024>(rs, dst, cpB[i]); });
         }
     }
@@ -312,9 +332,9 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &t
 // col0 .. col0+63 of row `row`).  With the B fragment as the first MFMA
 // operand, lane l of tile nt holds columns 16nt + 4(l >> 4) .. +3 of row
 // l & 15.  FP32 output stores those four values (16 bytes).  For a 16-bit
-// output (round to nearest even), lanes l and l^16 trade halves of tiles nt
-// and nt+1 so every lane stores eight consecutive columns (16 bytes).
-// Columns at or past N are not written.
+// output (FP16, or BF16 with kBF16; round to nearest even), lanes l and l^16
+// trade halves of tiles nt and nt+1 so every lane stores eight consecutive
+// columns (16 bytes).  Columns at or past N are not written.
 template <bool kBF16, bool kOutF32>
 __device__ __forceinline__ void store_strip(const GemmParams &p, const f32x4 (&v4)[4], int row,
                                             int col0, int lane) {

@@ -1,25 +1,33 @@
-// Generic GEMM kernel for operands the pipelined kernel cannot take (pointers
-// or leading dimensions not 16-byte aligned, K not a multiple of 8, very wide
-// rows): C = A . B with FP32 fused multiply-adds in increasing k, 64-bit
-// indexing, element loads.  Same definition as the pipelined kernel, slower.
+// Generic GEMM kernel for operands the 256x256 kernels cannot take (pointers
+// or leading dimensions not 16-byte aligned, rows of K not a whole number of
+// 16-byte chunks, very wide rows, FP8 B given K x N): C = A . B with FP32
+// fused multiply-adds in increasing k, 64-bit indexing, element loads.  Same
+// definition as the 256x256 kernels, slower.
 #include "internal.h"
 
 namespace mcs {
 namespace {
 
-template <bool kBF16>
-__device__ __forceinline__ float widen(uint16_t bits) {
-    if constexpr (kBF16)
-        return __uint_as_float(static_cast<uint32_t>(bits) << 16);
-    else
-        return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+// Element idx of an operand, widened exactly to FP32 (FP8 E4M3 through the
+// hardware conversion).
+template <int kElem>
+__device__ __forceinline__ float widen(const void *base, int64_t idx) {
+    if constexpr (kElem == kElemFP8) {
+        return __builtin_amdgcn_cvt_f32_fp8(static_cast<const uint8_t *>(base)[idx], 0);
+    } else {
+        const uint16_t bits = static_cast<const uint16_t *>(base)[idx];
+        if constexpr (kElem == kElemBF16)
+            return __uint_as_float(static_cast<uint32_t>(bits) << 16);
+        else
+            return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+    }
 }
 
 constexpr int kGenK = 16;
 
 // 64x64 output tile per 256-thread workgroup; thread (ty, tx) owns rows
 // ty + 16*i and columns tx + 16*j, i, j < 4.
-template <bool kBF16, bool kTransB, bool kOutF32>
+template <int kElem, bool kTransB, bool kOutF32>
 __global__ void __launch_bounds__(kGenThreads) gemm_generic_kernel(GemmParams p) {
     __shared__ float As[kGenK][kGenTile + 1];
     __shared__ float Bs[kGenK][kGenTile + 1];
@@ -34,7 +42,7 @@ __global__ void __launch_bounds__(kGenThreads) gemm_generic_kernel(GemmParams p)
         for (int e = threadIdx.x; e < kGenK * kGenTile; e += kGenThreads) {
             const int kk = e % kGenK, mm = e / kGenK;
             const int64_t gm = m0 + mm, gk = k0 + kk;
-            As[kk][mm] = (gm < p.M && gk < p.K) ? widen<kBF16>(p.A[gm * p.lda + gk]) : 0.f;
+            As[kk][mm] = (gm < p.M && gk < p.K) ? widen<kElem>(p.A, gm * p.lda + gk) : 0.f;
         }
         for (int e = threadIdx.x; e < kGenK * kGenTile; e += kGenThreads) {
             int kk, nn;
@@ -43,7 +51,7 @@ __global__ void __launch_bounds__(kGenThreads) gemm_generic_kernel(GemmParams p)
             const int64_t gn = n0 + nn, gk = k0 + kk;
             float v = 0.f;
             if (gn < p.N && gk < p.K)
-                v = widen<kBF16>(kTransB ? p.B[gn * p.ldb + gk] : p.B[gk * p.ldb + gn]);
+                v = widen<kElem>(p.B, kTransB ? gn * p.ldb + gk : gk * p.ldb + gn);
             Bs[kk][nn] = v;
         }
         __syncthreads();
@@ -61,7 +69,7 @@ __global__ void __launch_bounds__(kGenThreads) gemm_generic_kernel(GemmParams p)
             if (gn >= p.N) continue;
             if constexpr (kOutF32) {
                 reinterpret_cast<float *>(p.C)[gm * p.ldc + gn] = acc[i][j];
-            } else if constexpr (kBF16) {
+            } else if constexpr (kElem != kElemF16) {
                 reinterpret_cast<__bf16 *>(p.C)[gm * p.ldc + gn] = static_cast<__bf16>(acc[i][j]);
             } else {
                 reinterpret_cast<_Float16 *>(p.C)[gm * p.ldc + gn] = static_cast<_Float16>(acc[i][j]);
@@ -86,14 +94,16 @@ __global__ void __launch_bounds__(256) zero_fill(GemmParams p) {
 
 }  // namespace
 
-const void *generic_kernel(bool bf16, bool trans_b, bool out_f32) {
-#define MCS_PICK(B, T, O)                                 \
-    if (bf16 == B && trans_b == T && out_f32 == O)        \
-        return reinterpret_cast<const void *>(&gemm_generic_kernel<B, T, O>);
-    MCS_PICK(false, false, false) MCS_PICK(false, false, true)
-    MCS_PICK(false, true, false) MCS_PICK(false, true, true)
-    MCS_PICK(true, false, false) MCS_PICK(true, false, true)
-    MCS_PICK(true, true, false) MCS_PICK(true, true, true)
+const void *generic_kernel(int elem, bool trans_b, bool out_f32) {
+#define MCS_PICK(E, T, O)                                 \
+    if (elem == E && trans_b == T && out_f32 == O)        \
+        return reinterpret_cast<const void *>(&gemm_generic_kernel<E, T, O>);
+#define MCS_PICK_E(E) MCS_PICK(E, false, false) MCS_PICK(E, false, true) \
+                      MCS_PICK(E, true, false) MCS_PICK(E, true, true)
+    MCS_PICK_E(kElemF16)
+    MCS_PICK_E(kElemBF16)
+    MCS_PICK_E(kElemFP8)
+#undef MCS_PICK_E
 #undef MCS_PICK
     return nullptr;
 }

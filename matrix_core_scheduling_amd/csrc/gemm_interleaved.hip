@@ -65,13 +65,13 @@ namespace {
 constexpr int kWaves = kInterThreads / 64;
 constexpr int kCopyWait = 16;              // vmcnt before each barrier
 
-template <bool kTransB>
-struct Interleave : Loader<kTransB, kWaves> {
-    using Loader<kTransB, kWaves>::lds0;
+template <int kElem, bool kTransB>
+struct Interleave : Loader<kElem, kTransB, kWaves> {
+    using Loader<kElem, kTransB, kWaves>::lds0;
     FragOffsets fa, fb;
 
     __device__ __forceinline__ Interleave(const GemmParams &prm, int tm, int tn)
-        : Loader<kTransB, kWaves>(prm, tm, tn) {
+        : Loader<kElem, kTransB, kWaves>(prm, tm, tn) {
         const int lane = threadIdx.x & 63;
         const int wm = this->wave & 1, wn = this->wave >> 1;
         fa.rows(64 * wm, lane);
@@ -128,23 +128,38 @@ struct Interleave : Loader<kTransB, kWaves> {
     // One cluster: acc += a . b over the K-step while fragment `nf` (operand
     // kind kReadB ? B : A, half rh, buffer u of bs) is read and half ch of
     // operand kCopyB ? B : A is copied for K-step cs into buffer cbuf.  Group
-    // g issues fragment piece g and, for odd g, one copy.
-    template <bool kBF16, bool kReadB, bool kCopyB, bool kMask>
+    // g issues one fragment piece and, for odd g, one copy.  For 16-bit
+    // operands a group is one k-slice of one A tile against four B tiles and
+    // the pieces go k-slice-major (the next cluster's first groups use k-slice
+    // 0 of every tile).  For FP8 a group is two 16x16x128 MFMAs, each taking
+    // both 16-byte chunks of its tiles, so the pieces go tile-major; with
+    // kNtMajor the groups walk B tiles (the cluster whose B fragment was read
+    // by the previous cluster), otherwise A tiles.
+    template <bool kReadB, bool kCopyB, bool kMask, bool kNtMajor>
     __device__ __forceinline__ void cluster(f32x4 (&acc)[4][4], const i32x4 (&a)[4][2],
                                             const i32x4 (&b)[4][2], i32x4 (&nf)[4][2],
                                             const Bases &bs, int u, int rh, int cs, uint32_t cbuf,
                                             int ch) const {
         static_for<0, 8>([&](auto g) {
-            nf[g & 3][g >> 2] = kReadB ? read_b(bs, u, rh, g) : read_a(bs, u, rh, g);
+            constexpr int j = kElem == kElemFP8 ? (g & 1) * 4 + (g >> 1) : int(g);
+            nf[j & 3][j >> 2] = kReadB ? read_b(bs, u, rh, j) : read_a(bs, u, rh, j);
             if constexpr (g & 1) {
                 if constexpr (kCopyB)
                     this->template copy_b<kMask, g / 2, g / 2 + 1>(cs, cbuf, ch);
                 else
                     this->template copy_a<kMask, g / 2, g / 2 + 1>(cs, cbuf, ch);
             }
-            constexpr int ks = g >> 2, mt = g & 3;
-            for (int nt = 0; nt < 4; ++nt)
-                acc[mt][nt] = mfma<kBF16>(b[nt][ks], a[mt][ks], acc[mt][nt]);
+            if constexpr (kElem == kElemFP8) {
+                constexpr int t = g >> 1, o0 = 2 * (g & 1);
+                for (int o = o0; o < o0 + 2; ++o) {
+                    const int mt = kNtMajor ? o : t, nt = kNtMajor ? t : o;
+                    acc[mt][nt] = mfma_fp8(b[nt][0], b[nt][1], a[mt][0], a[mt][1], acc[mt][nt]);
+                }
+            } else {
+                constexpr int ks = g >> 2, mt = g & 3;
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = mfma<kElem>(b[nt][ks], a[mt][ks], acc[mt][nt]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         });
     }
@@ -159,7 +174,7 @@ __device__ __forceinline__ void wait_and_rendezvous() {
     rendezvous();
 }
 
-template <bool kBF16, bool kTransB, bool kOutF32>
+template <int kElem, bool kTransB, bool kOutF32>
 __global__ void __launch_bounds__(kInterThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_interleaved_kernel(GemmParams p) {
@@ -167,7 +182,7 @@ gemm_interleaved_kernel(GemmParams p) {
 
     int tm, tn;
     tile_coords(p, tm, tn);
-    Interleave<kTransB> il(p, tm, tn);
+    Interleave<kElem, kTransB> il(p, tm, tn);
     il.lds0 = lds_address(smem);
     const int wave = il.wave;
 
@@ -204,17 +219,17 @@ gemm_interleaved_kernel(GemmParams p) {
     // the register allocator rotate the 256 accumulators through copies.)
     // The copies of K-step s+2 need the per-lane k mask only when that step
     // is the partial last one.
-    const int tail = (p.K % kTileK) ? p.steps - 1 : -1;
+    const int tail = (p.K % step_k(kElem)) ? p.steps - 1 : -1;
     auto kstep = [&](int s, auto mask) {
         constexpr bool kMask = decltype(mask)::value;
         const uint32_t cur = (s & 1) ? kBuf : 0u, nxt = kBuf - cur;
         const auto bs = il.bases(cur, nxt);
         wait_and_rendezvous();
-        il.template cluster<kBF16, true, false, kMask>(acc[0][0], a0, b0, b1, bs, 0, 1, s + 2, cur, 0);
-        il.template cluster<kBF16, false, true, kMask>(acc[0][1], a0, b1, a1, bs, 0, 1, s + 2, cur, 0);
+        il.template cluster<true, false, kMask, true>(acc[0][0], a0, b0, b1, bs, 0, 1, s + 2, cur, 0);
+        il.template cluster<false, true, kMask, true>(acc[0][1], a0, b1, a1, bs, 0, 1, s + 2, cur, 0);
         wait_and_rendezvous();
-        il.template cluster<kBF16, false, true, kMask>(acc[1][0], a1, b0, a0, bs, 1, 0, s + 2, cur, 1);
-        il.template cluster<kBF16, true, false, kMask>(acc[1][1], a1, b1, b0, bs, 1, 0, s + 2, cur, 1);
+        il.template cluster<false, true, kMask, false>(acc[1][0], a1, b0, a0, bs, 1, 0, s + 2, cur, 1);
+        il.template cluster<true, false, kMask, false>(acc[1][1], a1, b1, b0, bs, 1, 0, s + 2, cur, 1);
     };
     int s = 0;
     if constexpr (kTransB) {
@@ -239,21 +254,22 @@ gemm_interleaved_kernel(GemmParams p) {
             if (row >= p.M) continue;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
-                store_strip<kBF16, kOutF32>(p, acc[qa][qb][mt], row, il.n0 + 128 * qb + 64 * wn, lane);
+                store_strip<kElem != kElemF16, kOutF32>(p, acc[qa][qb][mt], row, il.n0 + 128 * qb + 64 * wn, lane);
         }
 }
 
 }  // namespace
 
-const void *interleaved_kernel(bool bf16, bool trans_b, bool out_f32) {
-#define MCS_PICK(B, T, O)                                                            \
-    if (bf16 == B && trans_b == T && out_f32 == O)                                  \
-        return reinterpret_cast<const void *>(&gemm_interleaved_kernel<B, T, O>);
-#define MCS_PICK_O(B, T) MCS_PICK(B, T, false) MCS_PICK(B, T, true)
-    MCS_PICK_O(false, false)
-    MCS_PICK_O(false, true)
-    MCS_PICK_O(true, false)
-    MCS_PICK_O(true, true)
+const void *interleaved_kernel(int elem, bool trans_b, bool out_f32) {
+#define MCS_PICK(E, T, O)                                                            \
+    if (elem == E && trans_b == T && out_f32 == O)                                  \
+        return reinterpret_cast<const void *>(&gemm_interleaved_kernel<E, T, O>);
+#define MCS_PICK_O(E, T) MCS_PICK(E, T, false) MCS_PICK(E, T, true)
+    MCS_PICK_O(kElemF16, false)
+    MCS_PICK_O(kElemF16, true)
+    MCS_PICK_O(kElemBF16, false)
+    MCS_PICK_O(kElemBF16, true)
+    MCS_PICK_O(kElemFP8, true)
 #undef MCS_PICK_O
 #undef MCS_PICK
     return nullptr;

@@ -78,13 +78,13 @@ constexpr int kCopyWait = 8;               // vmcnt at the end of each memory st
 
 // Per-wave state of the 8-wave kernel: the shared copy loader plus this
 // wave's fragment read offsets.
-template <bool kBF16, bool kTransB, bool kOutF32, bool kOffset>
-struct Pipeline : Loader<kTransB, 8> {
-    using Loader<kTransB, 8>::lds0;
+template <int kElem, bool kTransB, bool kOutF32, bool kOffset>
+struct Pipeline : Loader<kElem, kTransB, 8> {
+    using Loader<kElem, kTransB, 8>::lds0;
     FragOffsets fa, fb;
 
     __device__ __forceinline__ Pipeline(const GemmParams &prm, int tm, int tn)
-        : Loader<kTransB, 8>(prm, tm, tn) {
+        : Loader<kElem, kTransB, 8>(prm, tm, tn) {
         const int lane = threadIdx.x & 63;
         const int wm = this->wave & 3, wn = this->wave >> 2;
         fa.rows(32 * wm, lane);
@@ -118,13 +118,21 @@ struct Pipeline : Loader<kTransB, 8> {
     }
 };
 
-template <bool kBF16>
+// One quadrant's MFMAs over the K-step: two 16x16x32 k-slices for 16-bit
+// operands, or one 16x16x128 FP8 MFMA over both chunks.
+template <int kElem>
 __device__ __forceinline__ void quadrant(f32x4 (&acc)[2][4], const i32x4 (&a)[2][2],
                                          const i32x4 (&b)[4][2]) {
-    for (int ks = 0; ks < 2; ++ks)
+    if constexpr (kElem == kElemFP8) {
         for (int mt = 0; mt < 2; ++mt)
             for (int nt = 0; nt < 4; ++nt)
-                acc[mt][nt] = mfma<kBF16>(b[nt][ks], a[mt][ks], acc[mt][nt]);
+                acc[mt][nt] = mfma_fp8(b[nt][0], b[nt][1], a[mt][0], a[mt][1], acc[mt][nt]);
+    } else {
+        for (int ks = 0; ks < 2; ++ks)
+            for (int mt = 0; mt < 2; ++mt)
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[mt][nt] = mfma<kElem>(b[nt][ks], a[mt][ks], acc[mt][nt]);
+    }
 }
 
 __device__ __forceinline__ void mem_stage_begin() { __builtin_amdgcn_s_setprio(1); }
@@ -140,7 +148,7 @@ __device__ __forceinline__ void mem_stage_end() {
     rendezvous();
 }
 
-template <bool kBF16, bool kTransB, bool kOutF32, bool kOffset>
+template <int kElem, bool kTransB, bool kOutF32, bool kOffset>
 __global__ void __launch_bounds__(kPipeThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_pipelined_kernel(GemmParams p) {
@@ -148,7 +156,7 @@ gemm_pipelined_kernel(GemmParams p) {
 
     int tm, tn;
     tile_coords(p, tm, tn);
-    Pipeline<kBF16, kTransB, kOutF32, kOffset> pl(p, tm, tn);
+    Pipeline<kElem, kTransB, kOutF32, kOffset> pl(p, tm, tn);
     pl.lds0 = lds_address(smem);
     const int wave = pl.wave;
 
@@ -193,8 +201,8 @@ gemm_pipelined_kernel(GemmParams p) {
             const uint32_t cur = u ? kBuf : 0u, nxt = u ? 0u : kBuf;
             const int s = t + u;
             // S0: quadrants Q00 and Q10
-            quadrant<kBF16>(acc[0][0], a0, b0);
-            quadrant<kBF16>(acc[1][0], a1, b0);
+            quadrant<kElem>(acc[0][0], a0, b0);
+            quadrant<kElem>(acc[1][0], a1, b0);
             rendezvous();
             // S1
             mem_stage_begin();
@@ -204,8 +212,8 @@ gemm_pipelined_kernel(GemmParams p) {
             pl.copy_b(s + 2, cur, 0);
             mem_stage_end();
             // S2: quadrants Q01 and Q11
-            quadrant<kBF16>(acc[0][1], a0, b1);
-            quadrant<kBF16>(acc[1][1], a1, b1);
+            quadrant<kElem>(acc[0][1], a0, b1);
+            quadrant<kElem>(acc[1][1], a1, b1);
             rendezvous();
             // S3
             mem_stage_begin();
@@ -233,22 +241,23 @@ gemm_pipelined_kernel(GemmParams p) {
             const int row = pl.m0 + 128 * qa + 32 * wm + 16 * mt + (lane & 15);
             if (row >= p.M) continue;
             for (int qb = 0; qb < 2; ++qb)
-                store_strip<kBF16, kOutF32>(p, acc[qa][qb][mt], row, pl.n0 + 128 * qb + 64 * wn, lane);
+                store_strip<kElem != kElemF16, kOutF32>(p, acc[qa][qb][mt], row, pl.n0 + 128 * qb + 64 * wn, lane);
         }
 }
 
 }  // namespace
 
-const void *pipelined_kernel(bool bf16, bool trans_b, bool out_f32, bool offset) {
-#define MCS_PICK(B, T, O, S)                                                         \
-    if (bf16 == B && trans_b == T && out_f32 == O && offset == S)                   \
-        return reinterpret_cast<const void *>(&gemm_pipelined_kernel<B, T, O, S>);
-#define MCS_PICK_S(B, T, O) MCS_PICK(B, T, O, true) MCS_PICK(B, T, O, false)
-#define MCS_PICK_O(B, T) MCS_PICK_S(B, T, false) MCS_PICK_S(B, T, true)
-    MCS_PICK_O(false, false)
-    MCS_PICK_O(false, true)
-    MCS_PICK_O(true, false)
-    MCS_PICK_O(true, true)
+const void *pipelined_kernel(int elem, bool trans_b, bool out_f32, bool offset) {
+#define MCS_PICK(E, T, O, S)                                                         \
+    if (elem == E && trans_b == T && out_f32 == O && offset == S)                   \
+        return reinterpret_cast<const void *>(&gemm_pipelined_kernel<E, T, O, S>);
+#define MCS_PICK_S(E, T, O) MCS_PICK(E, T, O, true) MCS_PICK(E, T, O, false)
+#define MCS_PICK_O(E, T) MCS_PICK_S(E, T, false) MCS_PICK_S(E, T, true)
+    MCS_PICK_O(kElemF16, false)
+    MCS_PICK_O(kElemF16, true)
+    MCS_PICK_O(kElemBF16, false)
+    MCS_PICK_O(kElemBF16, true)
+    MCS_PICK_O(kElemFP8, true)
 #undef MCS_PICK_O
 #undef MCS_PICK_S
 #undef MCS_PICK

@@ -6,10 +6,13 @@
 
 namespace mcs {
 
+// Operand element kinds (a template parameter of every kernel).
+enum Elem : int { kElemF16 = 0, kElemBF16 = 1, kElemFP8 = 2 };
+
 // Everything a kernel needs, passed by value as the single kernel argument.
 struct GemmParams {
-    const uint16_t *A;  // M x K operand bits, row stride lda (elements)
-    const uint16_t *B;  // K x N (trans_b = 0) or N x K (trans_b = 1), row stride ldb
+    const void *A;      // M x K operand bits, row stride lda (elements)
+    const void *B;      // K x N (trans_b = 0) or N x K (trans_b = 1), row stride ldb
     void *C;            // M x N result, row stride ldc
     int64_t lda, ldb, ldc;
     int M, N, K;
@@ -18,18 +21,23 @@ struct GemmParams {
     int group_m;           // tile rows per group in the L2-friendly tile order
 };
 
-// Pipelined 256x256x64 kernel: 8 waves, two wave groups.
-constexpr int kTileM = 256, kTileN = 256, kTileK = 64, kPipeThreads = 512;
+// Pipelined 256x256 kernel: 8 waves, two wave groups.  A K-step moves 128
+// bytes of every operand row: 64 FP16/BF16 or 128 FP8 elements.
+constexpr int kTileM = 256, kTileN = 256, kStepBytes = 128, kPipeThreads = 512;
+constexpr int elem_bytes(int elem) { return elem == kElemFP8 ? 1 : 2; }
+constexpr int step_k(int elem) { return kStepBytes / elem_bytes(elem); }
 // Within-wave interleaved kernel: the same 256x256x64 tile with 4 waves.
 constexpr int kInterThreads = 256;
 // Generic kernel: 64x64 tiles of 256 threads.
 constexpr int kGenTile = 64, kGenThreads = 256;
 
-// Return the device function for (bf16, trans_b, out_f32[, offset]) so the host
-// can launch it or query its attributes; nullptr for an unknown combination.
-const void *pipelined_kernel(bool bf16, bool trans_b, bool out_f32, bool offset);
-const void *interleaved_kernel(bool bf16, bool trans_b, bool out_f32);
-const void *generic_kernel(bool bf16, bool trans_b, bool out_f32);
+// Return the device function for (elem, trans_b, out_f32[, offset]) so the host
+// can launch it or query its attributes; nullptr for a combination that is not
+// compiled (the 256x256 kernels take FP8 operands only with B given N x K).
+// A 16-bit output is FP16 for FP16 operands and BF16 otherwise.
+const void *pipelined_kernel(int elem, bool trans_b, bool out_f32, bool offset);
+const void *interleaved_kernel(int elem, bool trans_b, bool out_f32);
+const void *generic_kernel(int elem, bool trans_b, bool out_f32);
 const void *zero_fill_kernel(bool out_f32);
 
 }  // namespace mcs

@@ -13,17 +13,26 @@ TORCH_DT = {}
 def _torch():
     import torch
     if not TORCH_DT:
-        TORCH_DT.update({"f16": torch.float16, "bf16": torch.bfloat16})
+        TORCH_DT.update({"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn,
+                         "f32": torch.float32})
     return torch
 
 
+def out_elem(elem: str, out: str) -> str:
+    """Element type of C for operand type elem and output choice out ("same", "f32", "bf16")."""
+    return elem if out == "same" else out
+
+
 def upload(bits: np.ndarray, elem: str, pad_front: int = 0):
-    """uint16 bits (rows x ld) -> device tensor of the operand dtype.  With
-    pad_front > 0 the data starts pad_front elements into the allocation
-    (to build misaligned operands)."""
+    """Bit patterns (rows x ld; uint16, or uint8 for fp8) -> device tensor of the
+    operand dtype.  With pad_front > 0 the data starts pad_front elements into
+    the allocation (to build misaligned operands)."""
     torch = _torch()
-    flat = np.ascontiguousarray(bits).reshape(-1).view(np.int16)
-    t = torch.empty(flat.size + pad_front, dtype=torch.int16, device="cuda")
+    if elem == "fp8":
+        flat, tdt = np.ascontiguousarray(bits).reshape(-1), torch.uint8
+    else:
+        flat, tdt = np.ascontiguousarray(bits).reshape(-1).view(np.int16), torch.int16
+    t = torch.empty(flat.size + pad_front, dtype=tdt, device="cuda")
     t[pad_front:].copy_(torch.from_numpy(flat.copy()))
     return t.view(TORCH_DT[elem]), pad_front
 
@@ -32,6 +41,7 @@ def run(elem: str, M: int, N: int, K: int, a_bits, b_bits, trans_b: int, out: st
         schedule: int = mcs.GEMM_SCHED_AUTO, ldc: int | None = None, c_fill: float | None = None,
         a_offset: int = 0, entry: str = "ex", return_raw: bool = False, allow_refusal: bool = False):
     """C = A.B on the GPU through the C ABI; returns (C float64 M x N, raw C bits).
+    out: "same" (the operand type; not for fp8), "f32" or "bf16".
 
     With allow_refusal, a GEMM_EINVAL answer (the requested schedule cannot
     take these operands; nothing was launched) returns None instead."""
@@ -43,19 +53,19 @@ def run(elem: str, M: int, N: int, K: int, a_bits, b_bits, trans_b: int, out: st
     A, off = upload(a_bits, elem, a_offset)
     B, _ = upload(b_bits, elem)
     ldc = N if ldc is None else ldc
-    cdt = torch.float32 if out == "f32" else TORCH_DT[elem]
-    C = torch.empty(max(M, 1) * ldc, dtype=cdt, device="cuda")
+    oe = out_elem(elem, out)
+    C = torch.empty(max(M, 1) * ldc, dtype=TORCH_DT[oe], device="cuda")
     if c_fill is not None:
         C.fill_(c_fill)
-    out_type = mcs.GEMM_OUT_F32 if out == "f32" else mcs.GEMM_OUT_SAME
+    out_type = {"same": mcs.GEMM_OUT_SAME, "f32": mcs.GEMM_OUT_F32, "bf16": mcs.GEMM_OUT_BF16}[out]
     stream = torch.cuda.current_stream().cuda_stream
-    a_ptr = A.data_ptr() + 2 * off
+    a_ptr = A.data_ptr() + (1 if elem == "fp8" else 2) * off
     if entry == "ex":
-        dt = mcs.GEMM_DTYPE_F16 if elem == "f16" else mcs.GEMM_DTYPE_BF16
+        dt = {"f16": mcs.GEMM_DTYPE_F16, "bf16": mcs.GEMM_DTYPE_BF16, "fp8": mcs.GEMM_DTYPE_FP8_E4M3}[elem]
         st = mcs.gemm_ex(dt, M, N, K, a_ptr, lda, B.data_ptr(), ldb, trans_b, C.data_ptr(), ldc,
                          out_type, schedule, stream)
     else:
-        fn = mcs.gemm_f16 if elem == "f16" else mcs.gemm_bf16
+        fn = {"f16": mcs.gemm_f16, "bf16": mcs.gemm_bf16, "fp8": mcs.gemm_fp8}[elem]
         st = fn(M, N, K, a_ptr, lda, B.data_ptr(), ldb, trans_b, C.data_ptr(), ldc, out_type, stream)
     if allow_refusal and st == mcs.GEMM_EINVAL:
         return None
@@ -63,12 +73,12 @@ def run(elem: str, M: int, N: int, K: int, a_bits, b_bits, trans_b: int, out: st
     torch.cuda.synchronize()
     full = C.view(max(M, 1), ldc)
     raw = full.cpu()
-    if out == "f32":
+    if oe == "f32":
         vals = raw.double().numpy()
         bits = raw.numpy().view(np.uint32)
     else:
         bits = raw.view(torch.int16).numpy().view(np.uint16)
-        vals = oracle.decode(bits, elem)
+        vals = oracle.decode(bits, oe)
     if return_raw:
         return vals[:M, :N], bits, vals
     return vals[:M, :N], bits[:M, :N]
@@ -86,13 +96,14 @@ def assert_within_tolerance(c, cref, sabs, what="", out="f16"):
 
 def assert_bit_exact(c_bits, cref, elem, out, what=""):
     """Integer regime: C must be the round-to-nearest-even of the exact value."""
-    if out == "f32":
+    oe = out_elem(elem, out)
+    if oe == "f32":
         want = cref.astype(np.float32)
         got = c_bits.view(np.float32)
         eq = got.astype(np.float64) == want.astype(np.float64)
     else:
-        want = oracle.round_to(cref, elem)
-        eq = oracle.decode(c_bits, elem) == oracle.decode(want, elem)     # +0 == -0
+        want = oracle.round_to(cref, oe)
+        eq = oracle.decode(c_bits, oe) == oracle.decode(want, oe)         # +0 == -0
     if not eq.all():
         bad = np.argwhere(~eq)
         i, j = bad[0]

@@ -18,7 +18,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = mcs.header_functions()
-    assert set(names) == {"gemm_f16", "gemm_bf16", "gemm_ex", "gemm_kernel_info", "gemm_status_string"}
+    assert set(names) == {"gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_ex", "gemm_kernel_info",
+                          "gemm_status_string"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -37,32 +38,46 @@ def test_status_strings(lib):
 
 
 # (M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type) -> expected status; pointers are
-# fake non-null integers: validation must reject before any launch.
+# fake non-null integers: validation must reject before any launch.  O stands for
+# a valid output type of the entry point (GEMM_OUT_SAME, or GEMM_OUT_BF16 for FP8).
 P = 0x1000
+O = "valid-out"
 BAD = [
-    ((-1, 4, 4, P, 4, P, 4, 0, P, 4, 0), mcs.GEMM_EINVAL),        # negative M
-    ((4, -1, 4, P, 4, P, 4, 0, P, 4, 0), mcs.GEMM_EINVAL),        # negative N
-    ((4, 4, -3, P, 4, P, 4, 0, P, 4, 0), mcs.GEMM_EINVAL),        # negative K
-    ((4, 4, 8, P, 7, P, 4, 0, P, 4, 0), mcs.GEMM_EINVAL),         # lda < K
-    ((4, 4, 8, P, 8, P, 3, 0, P, 4, 0), mcs.GEMM_EINVAL),         # ldb < N (B is K x N)
-    ((4, 4, 8, P, 8, P, 7, 1, P, 4, 0), mcs.GEMM_EINVAL),         # ldb < K (B is N x K)
-    ((4, 4, 8, P, 8, P, 8, 0, P, 3, 0), mcs.GEMM_EINVAL),         # ldc < N
-    ((4, 4, 8, P, 8, P, 8, 2, P, 8, 0), mcs.GEMM_EINVAL),         # trans_b not 0/1
-    ((4, 4, 8, P, 8, P, 8, 0, P, 8, 2), mcs.GEMM_EINVAL),         # out_type not 0/1
-    ((4, 4, 8, 0, 8, P, 8, 0, P, 8, 0), mcs.GEMM_EINVAL),         # null A
-    ((4, 4, 8, P, 8, 0, 8, 0, P, 8, 0), mcs.GEMM_EINVAL),         # null B
-    ((4, 4, 8, P, 8, P, 8, 0, 0, 8, 0), mcs.GEMM_EINVAL),         # null C
-    ((1 << 31, 4, 8, P, 8, P, 8, 0, P, 8, 0), mcs.GEMM_EUNSUPPORTED),
-    ((4, 4, 8, P, 1 << 31, P, 8, 0, P, 8, 0), mcs.GEMM_EUNSUPPORTED),
-    ((0, 4, 8, 0, 8, 0, 8, 0, 0, 8, 0), mcs.GEMM_OK),             # empty: no-op, no launch
-    ((4, 0, 8, 0, 8, 0, 8, 0, 0, 8, 0), mcs.GEMM_OK),
+    ((-1, 4, 4, P, 4, P, 4, 0, P, 4, O), mcs.GEMM_EINVAL),        # negative M
+    ((4, -1, 4, P, 4, P, 4, 0, P, 4, O), mcs.GEMM_EINVAL),        # negative N
+    ((4, 4, -3, P, 4, P, 4, 0, P, 4, O), mcs.GEMM_EINVAL),        # negative K
+    ((4, 4, 8, P, 7, P, 4, 0, P, 4, O), mcs.GEMM_EINVAL),         # lda < K
+    ((4, 4, 8, P, 8, P, 3, 0, P, 4, O), mcs.GEMM_EINVAL),         # ldb < N (B is K x N)
+    ((4, 4, 8, P, 8, P, 7, 1, P, 4, O), mcs.GEMM_EINVAL),         # ldb < K (B is N x K)
+    ((4, 4, 8, P, 8, P, 8, 0, P, 3, O), mcs.GEMM_EINVAL),         # ldc < N
+    ((4, 4, 8, P, 8, P, 8, 2, P, 8, O), mcs.GEMM_EINVAL),         # trans_b not 0/1
+    ((4, 4, 8, P, 8, P, 8, 0, P, 8, 7), mcs.GEMM_EINVAL),         # out_type unknown
+    ((4, 4, 8, 0, 8, P, 8, 0, P, 8, O), mcs.GEMM_EINVAL),         # null A
+    ((4, 4, 8, P, 8, 0, 8, 0, P, 8, O), mcs.GEMM_EINVAL),         # null B
+    ((4, 4, 8, P, 8, P, 8, 0, 0, 8, O), mcs.GEMM_EINVAL),         # null C
+    ((1 << 31, 4, 8, P, 8, P, 8, 0, P, 8, O), mcs.GEMM_EUNSUPPORTED),
+    ((4, 4, 8, P, 1 << 31, P, 8, 0, P, 8, O), mcs.GEMM_EUNSUPPORTED),
+    ((0, 4, 8, 0, 8, 0, 8, 0, 0, 8, O), mcs.GEMM_OK),             # empty: no-op, no launch
+    ((4, 0, 8, 0, 8, 0, 8, 0, 0, 8, O), mcs.GEMM_OK),
 ]
+VALID_OUT = {"gemm_f16": mcs.GEMM_OUT_SAME, "gemm_bf16": mcs.GEMM_OUT_SAME, "gemm_fp8": mcs.GEMM_OUT_BF16}
 
 
 @pytest.mark.parametrize("args,want", BAD)
-@pytest.mark.parametrize("fn", ["gemm_f16", "gemm_bf16"])
+@pytest.mark.parametrize("fn", ["gemm_f16", "gemm_bf16", "gemm_fp8"])
 def test_validation_before_launch(lib, fn, args, want):
+    args = tuple(VALID_OUT[fn] if a == O else a for a in args)
     assert getattr(mcs, fn)(*args, 0) == want
+
+
+def test_output_types_per_operand_type(lib):
+    """FP16 operands: FP16 or FP32 out; BF16: BF16 (SAME or BF16) or FP32; FP8:
+    BF16 or FP32 (no FP8 output).  Checked on an empty product (no launch)."""
+    empty = (0, 4, 8, 0, 8, 0, 8, 0, 0, 8)
+    assert mcs.gemm_f16(*empty, mcs.GEMM_OUT_BF16, 0) == mcs.GEMM_EINVAL
+    assert mcs.gemm_bf16(*empty, mcs.GEMM_OUT_BF16, 0) == mcs.GEMM_OK
+    assert mcs.gemm_fp8(*empty, mcs.GEMM_OUT_SAME, 0) == mcs.GEMM_EINVAL
+    assert mcs.gemm_fp8(*empty, mcs.GEMM_OUT_F32, 0) == mcs.GEMM_OK
 
 
 def test_ex_rejects_bad_dtype_and_schedule(lib):
@@ -82,6 +97,13 @@ def test_pipelined_schedule_refuses_unaligned_operands(lib):
     args = (256, 256, 60, P, 64, P, 64, 1, P, 256, 0)             # K % 8 != 0
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
+    fp8 = mcs.GEMM_DTYPE_FP8_E4M3
+    args = (256, 256, 136, P, 256, P, 256, 1, P, 256, mcs.GEMM_OUT_BF16)  # FP8: K % 16 != 0
+    assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
+    args = (256, 256, 128, P, 136, P, 256, 1, P, 256, mcs.GEMM_OUT_BF16)  # FP8: lda % 16 != 0
+    assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
+    args = (256, 256, 128, P, 128, P, 256, 0, P, 256, mcs.GEMM_OUT_BF16)  # FP8, B given K x N
+    assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

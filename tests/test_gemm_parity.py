@@ -181,12 +181,12 @@ def test_workload(name):
     c, _ = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, entry="abi")
     if w.M * w.N * w.K <= 2 ** 31:
         cref, sabs = oracle.gemm(a, b, w.dtype, w.trans_b)
-        assert_within_tolerance(c, cref, sabs, name, out=w.dtype if w.out == "same" else "f32")
+        assert_within_tolerance(c, cref, sabs, name, out=w.out_type)
     else:
         ii, jj = sample_points(w.M, w.N, 3000, seed=w.seed)
         cref, sabs = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
         assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name,
-                                out=w.dtype if w.out == "same" else "f32")
+                                out=w.out_type)
         # properties at every element: finite, and bounded by the operands
         assert np.isfinite(c).all()
 
@@ -226,7 +226,7 @@ def test_workload_interleaved(name):
     ii, jj = sample_points(w.M, w.N, 3000, seed=w.seed + 1)
     cref, sabs = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
     assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name,
-                            out=w.dtype if w.out == "same" else "f32")
+                            out=w.out_type)
     _, bits_p = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, schedule=mcs.GEMM_SCHED_PIPELINED)
     assert np.array_equal(bits, bits_p)
 
