@@ -1,12 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the gfx950 warp-pipelined GEMM; prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--schedule S] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--schedule S] [--splits N|auto] [--gpus 1]
 
-A step is one C = A.B launch of the whole product (by default FP16 operands,
-FP32 accumulation, FP16 output on the compute-bound 4096x4096x8192 shape; the
-other workloads include 8192^3 BF16 and 8192^3 FP8 E4M3), on inputs already
-resident in HBM.  Inputs are seeded synthetic matrices (A and
+A step is one C = A.B of the whole product (by default FP16 operands, FP32
+accumulation, FP16 output on the compute-bound 4096x4096x8192 shape, one
+launch; the other workloads include 8192^3 BF16, 8192^3 FP8 E4M3 and the
+512x4096x8192 row block one GPU of eight would hold, which runs split K: two
+launches per step), on inputs already resident in HBM.  Inputs are seeded synthetic matrices (A and
 B uniform in [-1, 1), B given N x K); enough rotating input sets are kept on
 the device that one pass over them exceeds the 256 MB last-level cache, and
 consecutive steps use consecutive sets.  Warm-up launches are untimed; the K
@@ -103,6 +104,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS))
     ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "interleaved", "generic"])
+    ap.add_argument("--splits", default="auto",
+                    help="K-slices (gemm_ex_splitk) or 'auto' (gemm_splitk_suggest; 1 for the default shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -161,11 +164,17 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     fn = {"f16": mcs.load().gemm_f16, "bf16": mcs.load().gemm_bf16, "fp8": mcs.load().gemm_fp8}[w.dtype]
+    splits = (mcs.gemm_splitk_suggest(dtype, w.M, w.N, w.K, 0) if a.splits == "auto" else int(a.splits))
+    ws_bytes = mcs.gemm_splitk_workspace_bytes(dtype, w.M, w.N, w.K, splits) if splits > 1 else 0
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     def launch(i):
         A, B = sets[i % nrot]
         C = outs[i % nrot]
-        if sched == mcs.GEMM_SCHED_AUTO:
+        if splits > 1:
+            st = mcs.gemm_ex_splitk(dtype, w.M, w.N, w.K, A.data_ptr(), lda, B.data_ptr(), ldb, w.trans_b,
+                                    C.data_ptr(), ldc, out_type, sched, splits, ws.data_ptr(), ws_bytes, sh)
+        elif sched == mcs.GEMM_SCHED_AUTO:
             st = fn(w.M, w.N, w.K, A.data_ptr(), lda, B.data_ptr(), ldb, w.trans_b, C.data_ptr(), ldc,
                     out_type, sh)
         else:
@@ -273,7 +282,7 @@ def main(argv=None) -> int:
                    "accumulate": "f32", "out": w.out_type,
                    "b_layout": "N x K row-major" if w.trans_b else "K x N row-major",
                    "values": w.dist, "seed": w.seed, "rotating_sets": nrot,
-                   "schedule": a.schedule},
+                   "schedule": a.schedule, "splits": splits},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "pct_of_unit_peak": round(100.0 * tflops / PEAK_TFLOPS_UNITS[w.dtype], 2),
         "batch_median_ms": round(batch_med, 6),

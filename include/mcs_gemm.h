@@ -137,6 +137,43 @@ int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K,
             void *C, int64_t ldc, int out_type, int schedule,
             hipStream_t stream);
 
+/*
+ * Split K for products with few output tiles (shapes whose 256x256 tiles
+ * cannot fill the GPU; the pages' kernels take one workgroup per output tile,
+ * this entry point is not from them).  gemm_ex_splitk computes the same C as
+ * gemm_ex in two kernels on `stream`: the K range is cut into at most
+ * `splits` slices of whole K-steps, each slice's FP32 partial product is
+ * written to `workspace` by the 256x256 kernel of `schedule` (AUTO means
+ * PIPELINED), and a second kernel sums the slices in order and writes C
+ * rounded to out_type.  The caller owns the workspace (device memory, 16-byte
+ * aligned, at least the size gemm_splitk_workspace_bytes reports); the
+ * library allocates nothing.  Calls that share a workspace must not overlap.
+ *   splits     1 .. 256; 1, or a K too short for two slices, runs gemm_ex
+ *              (no workspace needed)
+ * Returns GEMM_EINVAL for a missing, misaligned or too small workspace, for
+ * schedule GENERIC, or for an explicit schedule the operands do not allow
+ * (with AUTO, such operands run gemm_ex's generic kernel unsplit).
+ */
+int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K,
+                   const void *A, int64_t lda,
+                   const void *B, int64_t ldb, int trans_b,
+                   void *C, int64_t ldc, int out_type, int schedule,
+                   int splits, void *workspace, int64_t workspace_bytes,
+                   hipStream_t stream);
+
+/* Workspace bytes gemm_ex_splitk needs for these sizes and splits (0 when it
+ * would not split).  Returns a gemm_status. */
+int gemm_splitk_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int splits,
+                                int64_t *bytes);
+
+/* A split count for gemm_ex_splitk: 1 unless the 256x256 tiles fill fewer
+ * than `cus` compute units (0 = 256, MI355X) and every slice keeps at least
+ * 32 K-steps; then as many slices as the idle CUs allow.  (Each slice pays
+ * the pipeline's fill and drain and the workspace traffic: on MI355X the
+ * 512x4096x8192 FP16 product runs 123.7 us unsplit and 53.0 us with 4
+ * slices, while 1024^3, with 16 K-steps, gains nothing.) */
+int gemm_splitk_suggest(int dtype, int64_t M, int64_t N, int64_t K, int cus);
+
 /* Static description of one compiled kernel variant (from the code object). */
 typedef struct gemm_kernel_attrs {
     int num_regs;          /* VGPRs per lane as reported by the runtime */

@@ -1,6 +1,7 @@
 """Python binding of libmcs_gemm.so, the gfx950 warp-pipelined FP16/BF16/FP8 GEMM.
 
 The functions ``gemm_f16``, ``gemm_bf16``, ``gemm_fp8``, ``gemm_ex``,
+``gemm_ex_splitk``, ``gemm_splitk_workspace_bytes``, ``gemm_splitk_suggest``,
 ``gemm_kernel_info`` and ``gemm_status_string`` mirror the C ABI in
 ``include/mcs_gemm.h`` one to one
 (sizes, raw device pointers as integers, a raw ``hipStream_t``).  ``gemm``
@@ -58,6 +59,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         f.restype = ci
     lib.gemm_ex.argtypes = [ci] + sig + [ci, vp]
     lib.gemm_ex.restype = ci
+    lib.gemm_ex_splitk.argtypes = [ci] + sig + [ci, ci, vp, i64, vp]
+    lib.gemm_ex_splitk.restype = ci
+    lib.gemm_splitk_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(i64)]
+    lib.gemm_splitk_workspace_bytes.restype = ci
+    lib.gemm_splitk_suggest.argtypes = [ci, i64, i64, i64, ci]
+    lib.gemm_splitk_suggest.restype = ci
     lib.gemm_kernel_info.argtypes = [ci, ci, ci, ci, ctypes.POINTER(GemmKernelAttrs)]
     lib.gemm_kernel_info.restype = ci
     lib.gemm_status_string.argtypes = [ci]
@@ -88,6 +95,25 @@ def gemm_fp8(M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, stream) -> int:
 
 def gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream) -> int:
     return load().gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream)
+
+
+def gemm_ex_splitk(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, splits,
+                   workspace, workspace_bytes, stream) -> int:
+    return load().gemm_ex_splitk(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule,
+                                 splits, workspace, workspace_bytes, stream)
+
+
+def gemm_splitk_workspace_bytes(dtype: int, M: int, N: int, K: int, splits: int) -> int:
+    """Bytes of workspace gemm_ex_splitk needs (0 when it would not split)."""
+    n = ctypes.c_int64(0)
+    st = load().gemm_splitk_workspace_bytes(dtype, M, N, K, splits, ctypes.byref(n))
+    if st != GEMM_OK:
+        raise GemmError(st, "gemm_splitk_workspace_bytes")
+    return n.value
+
+
+def gemm_splitk_suggest(dtype: int, M: int, N: int, K: int, cus: int = 0) -> int:
+    return load().gemm_splitk_suggest(dtype, M, N, K, cus)
 
 
 def gemm_kernel_info(dtype: int, trans_b: int, out_type: int, schedule: int) -> dict:

@@ -154,6 +154,23 @@ __device__ __forceinline__ uint32_t lds_address(T *smem) {
 // the copy itself writes the XOR-swizzled layout.  A piece of a B half given
 // K x N is 4 k-rows x 256 bytes, swizzled the same way for the transposing
 // read.
+// Copy windows of one 256x256 output tile (uniform values).  For A and for B
+// given N x K, per half: byte address of the half's first row at k = 0, the
+// window's extent at k = 0 (start of the last valid row + the K elements'
+// bytes KB), and KB, or 0 when the half holds no valid row; at K-step s the
+// window starts 128*s bytes on and holds data while 128*s < KB.  For B given
+// K x N, per half: first column, bytes of one k-row's valid columns, and
+// whether the half holds any valid column.  A tile with no valid row or
+// column (the "no tile" value) copies zeros.
+struct TileWindows {
+    int m0, n0;
+    uint64_t aAddr[2], bAddr[2];
+    uint32_t aEnd[2], bEnd[2], aKB[2], bKB[2];
+    const char *bBase[2];
+    uint32_t bSpan[2];
+    bool bLive[2];
+};
+
 template <int kElem, bool kTransB, int kWaves>
 struct Loader {
     static constexpr int P = 16 / kWaves;   // pieces per wave per half
@@ -166,45 +183,14 @@ struct Loader {
     int cpAchunk[P];                 // 16-byte k-chunk (of 8) each A / N x K B copy lane moves
     int wave;
     const GemmParams &p;
-    int m0, n0;
-    // Per-half copy windows (uniform, computed once) of A and of B given N x
-    // K: byte address of the half's first row at k = 0, the window's extent at
-    // k = 0 (start of the last valid row + the K elements' bytes KB), and KB,
-    // or 0 when the half holds no valid row.  At K-step s the window starts
-    // 128*s bytes on and holds data while 128*s < KB.
-    uint64_t aAddr[2], bAddr[2];
-    uint32_t aEnd[2], bEnd[2], aKB[2], bKB[2];
-    // B given K x N: first column of the half, bytes of one k-row's valid
-    // columns, and whether the half holds any valid column
-    const char *bBase[2];
-    uint32_t bSpan[2];
-    bool bLive[2];
+    TileWindows win;                 // the tile being computed
 
     __device__ __forceinline__ Loader(const GemmParams &prm, int tm, int tn) : p(prm) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        m0 = tm * kTileM;
-        n0 = tn * kTileN;
         lds0 = 0;
-        const uint32_t kb = static_cast<uint32_t>(kEB) * static_cast<uint32_t>(p.K);
-        const char *A = static_cast<const char *>(p.A), *B = static_cast<const char *>(p.B);
-        for (int h = 0; h < 2; ++h) {
-            const int rows = min(max(p.M - (m0 + 128 * h), 0), 128);
-            aAddr[h] = reinterpret_cast<uint64_t>(A + (int64_t)(m0 + 128 * h) * p.lda * kEB);
-            aEnd[h] = rows > 0 ? static_cast<uint32_t>((rows - 1) * p.lda * kEB) + kb : 0u;
-            aKB[h] = rows > 0 ? kb : 0u;
-            const int cols = min(max(p.N - (n0 + 128 * h), 0), 128);
-            if constexpr (kTransB) {
-                bAddr[h] = reinterpret_cast<uint64_t>(B + (int64_t)(n0 + 128 * h) * p.ldb * kEB);
-                bEnd[h] = cols > 0 ? static_cast<uint32_t>((cols - 1) * p.ldb * kEB) + kb : 0u;
-                bKB[h] = cols > 0 ? kb : 0u;
-            } else {
-                bLive[h] = cols > 0;
-                bBase[h] = B + (n0 + 128 * h) * kEB;
-                bSpan[h] = static_cast<uint32_t>(cols * kEB);
-            }
-        }
+        win = windows(tm, tn);
         const int x = lane >> 3, pch = lane & 7;
         for (int i = 0; i < P; ++i) {
             const int row = 8 * (P * wave + i) + x;           // row of the half
@@ -224,6 +210,33 @@ struct Loader {
         }
     }
 
+    // Windows of output tile (tm, tn); tm >= tiles_m gives the no-tile value.
+    __device__ __forceinline__ TileWindows windows(int tm, int tn) const {
+        TileWindows w;
+        w.m0 = tm * kTileM;
+        w.n0 = tn * kTileN;
+        const bool live = w.m0 < p.M;
+        const uint32_t kb = static_cast<uint32_t>(kEB) * static_cast<uint32_t>(p.K);
+        const char *A = static_cast<const char *>(p.A), *B = static_cast<const char *>(p.B);
+        for (int h = 0; h < 2; ++h) {
+            const int rows = min(max(p.M - (w.m0 + 128 * h), 0), 128);
+            w.aAddr[h] = reinterpret_cast<uint64_t>(A + (int64_t)(w.m0 + 128 * h) * p.lda * kEB);
+            w.aEnd[h] = rows > 0 ? static_cast<uint32_t>((rows - 1) * p.lda * kEB) + kb : 0u;
+            w.aKB[h] = rows > 0 ? kb : 0u;
+            const int cols = live ? min(max(p.N - (w.n0 + 128 * h), 0), 128) : 0;
+            if constexpr (kTransB) {
+                w.bAddr[h] = reinterpret_cast<uint64_t>(B + (int64_t)(w.n0 + 128 * h) * p.ldb * kEB);
+                w.bEnd[h] = cols > 0 ? static_cast<uint32_t>((cols - 1) * p.ldb * kEB) + kb : 0u;
+                w.bKB[h] = cols > 0 ? kb : 0u;
+            } else {
+                w.bLive[h] = cols > 0;
+                w.bBase[h] = B + (w.n0 + 128 * h) * kEB;
+                w.bSpan[h] = static_cast<uint32_t>(cols * kEB);
+            }
+        }
+        return w;
+    }
+
     // Buffer resource of a row-major (k contiguous) half at K-step s.
     static __device__ __forceinline__ i32x4 step_rsrc(uint64_t addr, uint32_t end, uint32_t kb, int s) {
         const uint32_t koff = static_cast<uint32_t>(s) * kStepBytes;
@@ -236,16 +249,16 @@ struct Loader {
         return r;
     }
 
-    // Copy half h of operand A (rows m0+128h..) for K-step s into buffer `buf`.
-    // The window ends at the last valid byte of the half's last valid row, so
-    // rows >= M and every k >= K (steps past the end: an empty window) read 0.
-    // Pieces I0 .. I1-1 of this wave's share (all of them by default).  kMask
-    // = false skips the per-lane k-chunk mask: allowed when the step is
-    // either whole (64 k left) or wholly past the end.
+    // Copy half h of operand A (rows m0+128h.. of tile w) for K-step s into
+    // buffer `buf`.  The window ends at the last valid byte of the half's last
+    // valid row, so rows >= M and every k >= K (steps past the end: an empty
+    // window) read 0.  Pieces I0 .. I1-1 of this wave's share (all of them by
+    // default).  kMask = false skips the per-lane k-chunk mask: allowed when
+    // the step is either whole (all its k valid) or wholly past the end.
     template <bool kMask = true, int I0 = 0, int I1 = P>
-    __device__ __forceinline__ void copy_a(int s, uint32_t buf, int h) const {
+    __device__ __forceinline__ void copy_a(const TileWindows &w, int s, uint32_t buf, int h) const {
         const int kvb = (p.K - s * kStepK) * kEB;             // bytes of k left (may be <= 0)
-        const i32x4 rs = step_rsrc(aAddr[h], aEnd[h], aKB[h], s);
+        const i32x4 rs = step_rsrc(w.aAddr[h], w.aEnd[h], w.aKB[h], s);
         const uint32_t dst = lds0 + buf + kOffA + h * kHalf + P * wave * 1024;
         static_for<I0, I1>([&](auto i) {
             const uint32_t v = (!kMask || cpAchunk[i] * 16 < kvb) ? cpA[i] : kOutOfWindow;
@@ -253,13 +266,13 @@ struct Loader {
         });
     }
 
-    // Copy half h of operand B (columns n0+128h..) for K-step s into buffer `buf`.
+    // Copy half h of operand B (columns n0+128h.. of tile w) for K-step s into buffer `buf`.
     template <bool kMask = true, int I0 = 0, int I1 = P>
-    __device__ __forceinline__ void copy_b(int s, uint32_t buf, int h) const {
+    __device__ __forceinline__ void copy_b(const TileWindows &w, int s, uint32_t buf, int h) const {
         const int kv = p.K - s * kStepK;                      // k left (may be <= 0)
         const uint32_t dst = lds0 + buf + kOffB + h * kHalf + P * wave * 1024;
         if constexpr (kTransB) {
-            const i32x4 rs = step_rsrc(bAddr[h], bEnd[h], bKB[h], s);
+            const i32x4 rs = step_rsrc(w.bAddr[h], w.bEnd[h], w.bKB[h], s);
             static_for<I0, I1>([&](auto i) {
                 const uint32_t v = (!kMask || cpAchunk[i] * 16 < kv * kEB) ? cpB[i] : kOutOfWindow;
                 copy16<i * 1024>(rs, dst, v);
@@ -268,11 +281,21 @@ struct Loader {
             // k-rows k0 .. k0+rows-1; the window ends at the last valid column
             // of the last valid k-row, so k-rows >= K read 0 without a mask
             const int rows = min(kv, kStepK);
-            const uint32_t nrec = (bLive[h] && kv > 0)
-                ? static_cast<uint32_t>(rows - 1) * static_cast<uint32_t>(p.ldb * kEB) + bSpan[h] : 0u;
-            const i32x4 rs = make_rsrc(bBase[h] + (int64_t)s * kStepK * p.ldb * kEB, nrec);
+            const uint32_t nrec = (w.bLive[h] && kv > 0)
+                ? static_cast<uint32_t>(rows - 1) * static_cast<uint32_t>(p.ldb * kEB) + w.bSpan[h] : 0u;
+            const i32x4 rs = make_rsrc(w.bBase[h] + (int64_t)s * kStepK * p.ldb * kEB, nrec);
             static_for<I0, I1>([&](auto i) { copy16<i * 1024>(rs, dst, cpB[i]); });
         }
+    }
+
+    // The same for the tile being computed.
+    template <bool kMask = true, int I0 = 0, int I1 = P>
+    __device__ __forceinline__ void copy_a(int s, uint32_t buf, int h) const {
+        copy_a<kMask, I0, I1>(win, s, buf, h);
+    }
+    template <bool kMask = true, int I0 = 0, int I1 = P>
+    __device__ __forceinline__ void copy_b(int s, uint32_t buf, int h) const {
+        copy_b<kMask, I0, I1>(win, s, buf, h);
     }
 };
 
@@ -308,11 +331,13 @@ struct FragOffsets {
     }
 };
 
-__device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &tn) {
+// Output tile of virtual workgroup wg (the workgroup id, or for a workgroup
+// that computes several tiles wg = id + r * grid for its r-th tile, the grid
+// a multiple of 8 so every tile stays on its workgroup's XCD).
+__device__ __forceinline__ void tile_coords(const GemmParams &p, int wg, int &tm, int &tn) {
     // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2);
     // renumber so each XCD gets a contiguous range of tiles, then walk that
     // range in groups of group_m tile rows so neighbours share A and B tiles.
-    const int wg = blockIdx.x;
     const int total = p.tiles_m * p.tiles_n;
     const int xcd = wg & 7, j = wg >> 3;
     const int q = total >> 3, r = total & 7;

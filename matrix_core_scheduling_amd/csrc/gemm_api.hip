@@ -72,6 +72,44 @@ int launch(const void *fn, dim3 grid, dim3 block, GemmParams &prm, hipStream_t s
     return to_status(hipLaunchKernel(fn, grid, block, args, 0, stream));
 }
 
+// One of the 256x256 kernels over `slices` K-slices of kslice elements each
+// (slices == 1: the whole product into C).  prm holds A, B, C, sizes and
+// leading dimensions; tiles, steps and the slice fields are filled here.
+int launch_tiles(int elem, int trans_b, bool out_f32, int schedule, GemmParams &prm, int64_t kslice,
+                 int slices, hipStream_t stream) {
+    const int64_t tm = (prm.M + mcs::kTileM - 1) / mcs::kTileM;
+    const int64_t tn = (prm.N + mcs::kTileN - 1) / mcs::kTileN;
+    if (tm * tn > kIntMax) return GEMM_EUNSUPPORTED;
+    const int64_t nk = (kslice + mcs::step_k(elem) - 1) / mcs::step_k(elem);
+    prm.tiles_m = static_cast<int>(tm);
+    prm.tiles_n = static_cast<int>(tn);
+    prm.group_m = 4;
+    prm.kslice = static_cast<int>(kslice);
+    const dim3 grid(static_cast<unsigned>(tm * tn), static_cast<unsigned>(slices));
+    if (schedule == GEMM_SCHED_INTERLEAVED) {
+        prm.steps = static_cast<int>(nk);   // one K-step per loop iteration
+        return launch(mcs::interleaved_kernel(elem, trans_b != 0, out_f32), grid,
+                      dim3(mcs::kInterThreads), prm, stream);
+    }
+    prm.steps = static_cast<int>(nk < 2 ? 2 : (nk + 1) / 2 * 2);
+    return launch(mcs::pipelined_kernel(elem, trans_b != 0, out_f32, schedule == GEMM_SCHED_PIPELINED),
+                  grid, dim3(mcs::kPipeThreads), prm, stream);
+}
+
+constexpr int kMaxSplits = 256;
+
+// K-slice length (a whole number of K-steps) and slice count for a request
+// of `splits` slices.
+void split_plan(int elem, int64_t K, int splits, int64_t &kslice, int &slices) {
+    const int64_t sk = mcs::step_k(elem);
+    const int64_t steps = (K + sk - 1) / sk;
+    const int64_t per = (steps + splits - 1) / splits;
+    kslice = per * sk;
+    slices = static_cast<int>((K + kslice - 1) / kslice);
+}
+
+int64_t ws_row(int64_t N) { return (N + 3) / 4 * 4; }
+
 }  // namespace
 
 extern "C" int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
@@ -114,21 +152,76 @@ extern "C" int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A
                       dim3(mcs::kGenThreads), prm, stream);
     }
 
-    const int64_t tm = (M + mcs::kTileM - 1) / mcs::kTileM;
-    const int64_t tn = (N + mcs::kTileN - 1) / mcs::kTileN;
-    if (tm * tn > kIntMax) return GEMM_EUNSUPPORTED;
-    const int64_t nk = (K + mcs::step_k(elem) - 1) / mcs::step_k(elem);
-    prm.tiles_m = static_cast<int>(tm);
-    prm.tiles_n = static_cast<int>(tn);
-    prm.steps = static_cast<int>(nk < 2 ? 2 : (nk + 1) / 2 * 2);
-    prm.group_m = 4;
-    if (schedule == GEMM_SCHED_INTERLEAVED) {
-        prm.steps = static_cast<int>(nk);   // one K-step per loop iteration
-        return launch(mcs::interleaved_kernel(elem, trans_b != 0, out_f32),
-                      dim3(static_cast<unsigned>(tm * tn)), dim3(mcs::kInterThreads), prm, stream);
-    }
-    return launch(mcs::pipelined_kernel(elem, trans_b != 0, out_f32, schedule == GEMM_SCHED_PIPELINED),
-                  dim3(static_cast<unsigned>(tm * tn)), dim3(mcs::kPipeThreads), prm, stream);
+    return launch_tiles(elem, trans_b, out_f32, schedule, prm, K, 1, stream);
+}
+
+extern "C" int gemm_splitk_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int splits,
+                                           int64_t *bytes) {
+    if (!bytes || splits < 1 || splits > kMaxSplits || M < 0 || N < 0 || K < 0) return GEMM_EINVAL;
+    if (dtype < GEMM_DTYPE_F16 || dtype > GEMM_DTYPE_FP8_E4M3) return GEMM_EINVAL;
+    if (M > kIntMax || N > kIntMax || K > kIntMax) return GEMM_EUNSUPPORTED;
+    int64_t kslice = 0;
+    int slices = 1;
+    if (K > 0) split_plan(elem_of(dtype), K, splits, kslice, slices);
+    *bytes = slices > 1 ? static_cast<int64_t>(slices) * M * ws_row(N) * 4 : 0;
+    return GEMM_OK;
+}
+
+extern "C" int gemm_splitk_suggest(int dtype, int64_t M, int64_t N, int64_t K, int cus) {
+    if (dtype < GEMM_DTYPE_F16 || dtype > GEMM_DTYPE_FP8_E4M3 || M <= 0 || N <= 0 || K <= 0) return 1;
+    if (cus <= 0) cus = 256;
+    const int64_t tiles = ((M + mcs::kTileM - 1) / mcs::kTileM) * ((N + mcs::kTileN - 1) / mcs::kTileN);
+    const int64_t steps = (K + mcs::step_k(elem_of(dtype)) - 1) / mcs::step_k(elem_of(dtype));
+    int64_t s = steps / 32;                          // at least 32 K-steps per slice
+    if (cus / tiles < s) s = cus / tiles;            // no more workgroups than CUs
+    return static_cast<int>(s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s));
+}
+
+extern "C" int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                              const void *B, int64_t ldb, int trans_b, void *C, int64_t ldc,
+                              int out_type, int schedule, int splits, void *workspace,
+                              int64_t workspace_bytes, hipStream_t stream) {
+    const int v = validate(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule);
+    if (v != GEMM_OK) return v;
+    if (splits < 1 || splits > kMaxSplits || schedule == GEMM_SCHED_GENERIC) return GEMM_EINVAL;
+    if (M == 0 || N == 0) return GEMM_OK;
+    const int elem = elem_of(dtype);
+    int64_t kslice = 0;
+    int slices = 1;
+    if (K > 0) split_plan(elem, K, splits, kslice, slices);
+    if (slices == 1)
+        return gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream);
+    const bool fast = pipelined_ok(elem, N, K, A, lda, B, ldb, trans_b, C, ldc);
+    if (!fast) return schedule == GEMM_SCHED_AUTO
+        ? gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream)
+        : GEMM_EINVAL;
+    const int64_t need = static_cast<int64_t>(slices) * M * ws_row(N) * 4;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return GEMM_EINVAL;
+    if (schedule == GEMM_SCHED_AUTO) schedule = GEMM_SCHED_PIPELINED;
+
+    GemmParams prm{};
+    prm.A = A;
+    prm.B = B;
+    prm.C = C;
+    prm.lda = lda;
+    prm.ldb = ldb;
+    prm.ldc = ldc;
+    prm.M = static_cast<int>(M);
+    prm.N = static_cast<int>(N);
+    prm.K = static_cast<int>(K);
+    prm.ws = static_cast<float *>(workspace);
+    prm.ldws = ws_row(N);
+    // pass 1: the FP32 partial product of every K-slice
+    int st = launch_tiles(elem, trans_b, true, schedule, prm, kslice, slices, stream);
+    if (st != GEMM_OK) return st;
+    // pass 2: sum the slices in order, round to the output type, write C
+    const int out_kind = out_type == GEMM_OUT_F32 ? 2 : (elem == mcs::kElemF16 ? 0 : 1);
+    const int64_t items = M * ((N + 3) / 4);
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    void *args[] = {&prm, &slices};
+    return to_status(hipLaunchKernel(mcs::splitk_reduce_kernel(out_kind),
+                                     dim3(static_cast<unsigned>(blocks)), dim3(256), args, 0, stream));
 }
 
 extern "C" int gemm_f16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,

@@ -92,7 +92,47 @@ __global__ void __launch_bounds__(256) zero_fill(GemmParams p) {
     }
 }
 
+// Split-K reduction: C = round(sum over the S slices of the FP32 partials),
+// summed in slice order.  One thread per 4 consecutive columns of a row
+// (rows of the workspace start 16-byte aligned); columns at or past N are not
+// written.  kOut: 0 FP16, 1 BF16, 2 FP32.
+template <int kOut>
+__global__ void __launch_bounds__(256) splitk_reduce(GemmParams p, int slices) {
+    const int64_t per_row = (p.N + 3) / 4;
+    const int64_t total = static_cast<int64_t>(p.M) * per_row;
+    const int64_t slice_stride = static_cast<int64_t>(p.M) * p.ldws;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < total;
+         e += static_cast<int64_t>(gridDim.x) * 256) {
+        const int64_t i = e / per_row, j = (e % per_row) * 4;
+        const float *src = p.ws + i * p.ldws + j;
+        float4 acc = *reinterpret_cast<const float4 *>(src);
+        for (int y = 1; y < slices; ++y) {
+            const float4 v = *reinterpret_cast<const float4 *>(src + y * slice_stride);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        const float r[4] = {acc.x, acc.y, acc.z, acc.w};
+        for (int c = 0; c < 4 && j + c < p.N; ++c) {
+            const int64_t o = i * p.ldc + j + c;
+            if constexpr (kOut == 2)
+                reinterpret_cast<float *>(p.C)[o] = r[c];
+            else if constexpr (kOut == 1)
+                reinterpret_cast<__bf16 *>(p.C)[o] = static_cast<__bf16>(r[c]);
+            else
+                reinterpret_cast<_Float16 *>(p.C)[o] = static_cast<_Float16>(r[c]);
+        }
+    }
+}
+
 }  // namespace
+
+const void *splitk_reduce_kernel(int out_kind) {
+    switch (out_kind) {
+        case 0: return reinterpret_cast<const void *>(&splitk_reduce<0>);
+        case 1: return reinterpret_cast<const void *>(&splitk_reduce<1>);
+        case 2: return reinterpret_cast<const void *>(&splitk_reduce<2>);
+        default: return nullptr;
+    }
+}
 
 const void *generic_kernel(int elem, bool trans_b, bool out_f32) {
 #define MCS_PICK(E, T, O)                                 \

@@ -177,11 +177,12 @@ __device__ __forceinline__ void wait_and_rendezvous() {
 template <int kElem, bool kTransB, bool kOutF32>
 __global__ void __launch_bounds__(kInterThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_interleaved_kernel(GemmParams p) {
+gemm_interleaved_kernel(GemmParams pin) {
+    const GemmParams p = slice_view<elem_bytes(kElem), kTransB>(pin);
     __shared__ __attribute__((aligned(1024))) char smem[2 * kBuf];
 
     int tm, tn;
-    tile_coords(p, tm, tn);
+    tile_coords(p, blockIdx.x, tm, tn);
     Interleave<kElem, kTransB> il(p, tm, tn);
     il.lds0 = lds_address(smem);
     const int wave = il.wave;
@@ -219,7 +220,8 @@ gemm_interleaved_kernel(GemmParams p) {
     // the register allocator rotate the 256 accumulators through copies.)
     // The copies of K-step s+2 need the per-lane k mask only when that step
     // is the partial last one.
-    const int tail = (p.K % step_k(kElem)) ? p.steps - 1 : -1;
+    constexpr int kSK = step_k(kElem);
+    const int tail = (p.K % kSK) ? (p.K + kSK - 1) / kSK - 1 : -1;   // the partial K-step, if any
     auto kstep = [&](int s, auto mask) {
         constexpr bool kMask = decltype(mask)::value;
         const uint32_t cur = (s & 1) ? kBuf : 0u, nxt = kBuf - cur;
@@ -250,11 +252,11 @@ gemm_interleaved_kernel(GemmParams p) {
     for (int qa = 0; qa < 2; ++qa)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const int row = il.m0 + 128 * qa + 64 * wm + 16 * mt + (lane & 15);
+            const int row = il.win.m0 + 128 * qa + 64 * wm + 16 * mt + (lane & 15);
             if (row >= p.M) continue;
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
-                store_strip<kElem != kElemF16, kOutF32>(p, acc[qa][qb][mt], row, il.n0 + 128 * qb + 64 * wn, lane);
+                store_strip<kElem != kElemF16, kOutF32>(p, acc[qa][qb][mt], row, il.win.n0 + 128 * qb + 64 * wn, lane);
         }
 }
 

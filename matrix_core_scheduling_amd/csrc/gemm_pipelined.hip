@@ -151,11 +151,12 @@ __device__ __forceinline__ void mem_stage_end() {
 template <int kElem, bool kTransB, bool kOutF32, bool kOffset>
 __global__ void __launch_bounds__(kPipeThreads)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-gemm_pipelined_kernel(GemmParams p) {
+gemm_pipelined_kernel(GemmParams pin) {
+    const GemmParams p = slice_view<elem_bytes(kElem), kTransB>(pin);
     __shared__ __attribute__((aligned(1024))) char smem[2 * kBuf];
 
     int tm, tn;
-    tile_coords(p, tm, tn);
+    tile_coords(p, blockIdx.x, tm, tn);
     Pipeline<kElem, kTransB, kOutF32, kOffset> pl(p, tm, tn);
     pl.lds0 = lds_address(smem);
     const int wave = pl.wave;
@@ -238,10 +239,10 @@ gemm_pipelined_kernel(GemmParams p) {
     const int wm = wave & 3, wn = wave >> 2;
     for (int qa = 0; qa < 2; ++qa)
         for (int mt = 0; mt < 2; ++mt) {
-            const int row = pl.m0 + 128 * qa + 32 * wm + 16 * mt + (lane & 15);
+            const int row = pl.win.m0 + 128 * qa + 32 * wm + 16 * mt + (lane & 15);
             if (row >= p.M) continue;
             for (int qb = 0; qb < 2; ++qb)
-                store_strip<kElem != kElemF16, kOutF32>(p, acc[qa][qb][mt], row, pl.n0 + 128 * qb + 64 * wn, lane);
+                store_strip<kElem != kElemF16, kOutF32>(p, acc[qa][qb][mt], row, pl.win.n0 + 128 * qb + 64 * wn, lane);
         }
 }
 

@@ -19,7 +19,30 @@ struct GemmParams {
     int tiles_m, tiles_n;  // output tiles of the launched kernel
     int steps;             // K-steps the main loop runs (the pipelined kernel: even, >= 2)
     int group_m;           // tile rows per group in the L2-friendly tile order
+    // Split K (launched with gridDim.y = number of slices > 1): slice y covers
+    // k in [y * kslice, min(K, (y + 1) * kslice)) and writes its FP32 partial
+    // product to ws + y * M * ldws (row stride ldws floats) instead of C.
+    int kslice;
+    float *ws;
+    int64_t ldws;
 };
+
+// The view of the product one workgroup computes: the whole of it, or with
+// several K-slices (gridDim.y > 1) slice blockIdx.y of it, whose FP32 result
+// goes to the workspace.  `steps` is already the slice's step count.
+template <int kElemBytes, bool kTransB>
+__device__ __forceinline__ GemmParams slice_view(const GemmParams &p) {
+    if (gridDim.y == 1) return p;
+    GemmParams q = p;
+    const int y = blockIdx.y;
+    const int64_t k0 = static_cast<int64_t>(y) * p.kslice;
+    q.K = static_cast<int>(min(static_cast<int64_t>(p.K) - k0, static_cast<int64_t>(p.kslice)));
+    q.A = static_cast<const char *>(p.A) + k0 * kElemBytes;
+    q.B = static_cast<const char *>(p.B) + k0 * kElemBytes * (kTransB ? 1 : p.ldb);
+    q.C = p.ws + static_cast<int64_t>(y) * p.M * p.ldws;
+    q.ldc = p.ldws;
+    return q;
+}
 
 // Pipelined 256x256 kernel: 8 waves, two wave groups.  A K-step moves 128
 // bytes of every operand row: 64 FP16/BF16 or 128 FP8 elements.
@@ -39,5 +62,7 @@ const void *pipelined_kernel(int elem, bool trans_b, bool out_f32, bool offset);
 const void *interleaved_kernel(int elem, bool trans_b, bool out_f32);
 const void *generic_kernel(int elem, bool trans_b, bool out_f32);
 const void *zero_fill_kernel(bool out_f32);
+// Split-K reduction into C: out_kind 0 FP16, 1 BF16, 2 FP32.
+const void *splitk_reduce_kernel(int out_kind);
 
 }  // namespace mcs

@@ -99,6 +99,8 @@ def derived(c: dict, n_xcc: int, simds: int) -> dict:
         out["mfma_flop"] = c["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512
     if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c:
         out["mfma_flop_bf16"] = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    if "SQ_INSTS_VALU_MFMA_MOPS_F8" in c:
+        out["mfma_flop_f8"] = c["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512
     return out
 
 

@@ -18,7 +18,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = mcs.header_functions()
-    assert set(names) == {"gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_ex", "gemm_kernel_info",
+    assert set(names) == {"gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_ex", "gemm_ex_splitk",
+                          "gemm_splitk_workspace_bytes", "gemm_splitk_suggest", "gemm_kernel_info",
                           "gemm_status_string"}
 
 
@@ -110,3 +111,44 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(mcs, "_lib", None)
     with pytest.raises(RuntimeError, match="no non-HIP fallback"):
         mcs.load(str(tmp_path / "absent.so"))
+
+
+def test_splitk_workspace_size(lib):
+    f16 = mcs.GEMM_DTYPE_F16
+    # K = 1024 is 16 K-steps of 64: 4 slices of 4 steps; rows of the FP32
+    # partials are rounded up to 4 floats
+    assert mcs.gemm_splitk_workspace_bytes(f16, 1024, 1000, 1024, 4) == 4 * 1024 * 1000 * 4
+    assert mcs.gemm_splitk_workspace_bytes(f16, 1024, 1001, 1024, 4) == 4 * 1024 * 1004 * 4
+    # 5 steps in 4 requested slices: 2 steps per slice, so 3 slices
+    assert mcs.gemm_splitk_workspace_bytes(f16, 64, 64, 320, 4) == 3 * 64 * 64 * 4
+    assert mcs.gemm_splitk_workspace_bytes(f16, 64, 64, 64, 8) == 0            # one K-step: no split
+    assert mcs.gemm_splitk_workspace_bytes(f16, 64, 64, 1024, 1) == 0
+    fp8 = mcs.GEMM_DTYPE_FP8_E4M3                                           # K-steps of 128
+    assert mcs.gemm_splitk_workspace_bytes(fp8, 256, 256, 1024, 4) == 4 * 256 * 256 * 4
+    with pytest.raises(mcs.GemmError):
+        mcs.gemm_splitk_workspace_bytes(f16, 64, 64, 64, 0)
+
+
+def test_splitk_validation_before_launch(lib):
+    args = (1024, 1024, 1024, P, 1024, P, 1024, 1, P, 1024, 0)
+    need = mcs.gemm_splitk_workspace_bytes(0, 1024, 1024, 1024, 4)
+    sk = mcs.gemm_ex_splitk
+    assert sk(0, *args, mcs.GEMM_SCHED_AUTO, 4, 0, need, 0) == mcs.GEMM_EINVAL          # no workspace
+    assert sk(0, *args, mcs.GEMM_SCHED_AUTO, 4, P, need - 16, 0) == mcs.GEMM_EINVAL     # too small
+    assert sk(0, *args, mcs.GEMM_SCHED_AUTO, 4, P + 4, need, 0) == mcs.GEMM_EINVAL      # misaligned
+    assert sk(0, *args, mcs.GEMM_SCHED_GENERIC, 4, P, need, 0) == mcs.GEMM_EINVAL
+    assert sk(0, *args, mcs.GEMM_SCHED_AUTO, 0, P, need, 0) == mcs.GEMM_EINVAL          # splits < 1
+    assert sk(0, *args, mcs.GEMM_SCHED_AUTO, 257, P, need, 0) == mcs.GEMM_EINVAL
+    bad = (1024, 1024, 1024, P + 2, 1024, P, 1024, 1, P, 1024, 0)                      # unaligned A
+    assert sk(0, *bad, mcs.GEMM_SCHED_PIPELINED, 4, P, need, 0) == mcs.GEMM_EINVAL
+    assert sk(0, 0, 8, 8, 0, 8, 0, 8, 1, 0, 8, 0, mcs.GEMM_SCHED_AUTO, 4, 0, 0, 0) == mcs.GEMM_OK  # empty
+
+
+def test_splitk_suggest(lib):
+    f16 = mcs.GEMM_DTYPE_F16
+    assert mcs.gemm_splitk_suggest(f16, 4096, 4096, 8192) == 1        # 256 tiles fill 256 CUs
+    assert mcs.gemm_splitk_suggest(f16, 512, 4096, 8192) == 4         # 32 tiles, 128 K-steps
+    assert mcs.gemm_splitk_suggest(f16, 1024, 1024, 1024) == 1        # 16 K-steps: too short
+    assert mcs.gemm_splitk_suggest(f16, 256, 256, 65536) == 32        # 1024 K-steps, 1 tile
+    assert mcs.gemm_splitk_suggest(f16, 512, 4096, 8192, 128) == 4
+    assert mcs.gemm_splitk_suggest(f16, 512, 4096, 8192, 64) == 2
