@@ -38,6 +38,12 @@ def _run(cmd):
     return err
 
 
+def device_asm(src: str, out: str) -> str:
+    """Write the gfx950 assembly of one source file of csrc/ to ``out``."""
+    _run([HIPCC, *COMMON, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out])
+    return out
+
+
 def build(asm_dir: str | None = None, jobs: int = 4) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
 
@@ -46,8 +52,7 @@ def build(asm_dir: str | None = None, jobs: int = 4) -> str:
         _run([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
         if asm_dir:
             os.makedirs(asm_dir, exist_ok=True)
-            _run([HIPCC, *COMMON, "--cuda-device-only", "-S", os.path.join(CSRC, src),
-                  "-o", os.path.join(asm_dir, src.replace(".hip", f"-{ARCH}.s"))])
+            device_asm(src, os.path.join(asm_dir, src.replace(".hip", f"-{ARCH}.s")))
         return obj
 
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:

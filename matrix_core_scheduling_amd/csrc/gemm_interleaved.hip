@@ -178,7 +178,7 @@ template <int kElem, bool kTransB, bool kOutF32>
 __global__ void __launch_bounds__(kInterThreads)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_interleaved_kernel(GemmParams pin) {
-    const GemmParams p = slice_view<elem_bytes(kElem), kTransB>(pin);
+    const GemmParams p = slice_view<elem_bytes(kElem), kTransB, true>(pin);
     __shared__ __attribute__((aligned(1024))) char smem[2 * kBuf];
 
     int tm, tn;
@@ -219,9 +219,10 @@ gemm_interleaved_kernel(GemmParams pin) {
     // the buffers are addressed statically, as the 8-wave kernel does, makes
     // the register allocator rotate the 256 accumulators through copies.)
     // The copies of K-step s+2 need the per-lane k mask only when that step
-    // is the partial last one.
-    constexpr int kSK = step_k(kElem);
-    const int tail = (p.K % kSK) ? (p.K + kSK - 1) / kSK - 1 : -1;   // the partial K-step, if any
+    // is the partial last one (p.steps is exactly ceil(K / step) here).
+    // Written as steps - 1 rather than from K: deriving it from K by a
+    // division made the allocator rotate the accumulators for B given N x K.
+    const int tail = (p.K % step_k(kElem)) ? p.steps - 1 : -1;   // the partial K-step, if any
     auto kstep = [&](int s, auto mask) {
         constexpr bool kMask = decltype(mask)::value;
         const uint32_t cur = (s & 1) ? kBuf : 0u, nxt = kBuf - cur;

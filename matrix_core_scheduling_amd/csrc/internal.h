@@ -29,14 +29,18 @@ struct GemmParams {
 
 // The view of the product one workgroup computes: the whole of it, or with
 // several K-slices (gridDim.y > 1) slice blockIdx.y of it, whose FP32 result
-// goes to the workspace.  `steps` is already the slice's step count.
-template <int kElemBytes, bool kTransB>
+// goes to the workspace.  `steps` is already a full slice's step count; with
+// kExactSteps it becomes this slice's own count of 128-byte K-steps (the last
+// slice may be shorter), so the last of them is the partial one if K is not a
+// whole number of K-steps.
+template <int kElemBytes, bool kTransB, bool kExactSteps = false>
 __device__ __forceinline__ GemmParams slice_view(const GemmParams &p) {
     if (gridDim.y == 1) return p;
     GemmParams q = p;
     const int y = blockIdx.y;
     const int64_t k0 = static_cast<int64_t>(y) * p.kslice;
     q.K = static_cast<int>(min(static_cast<int64_t>(p.K) - k0, static_cast<int64_t>(p.kslice)));
+    if constexpr (kExactSteps) q.steps = (q.K * kElemBytes + 127) / 128;
     q.A = static_cast<const char *>(p.A) + k0 * kElemBytes;
     q.B = static_cast<const char *>(p.B) + k0 * kElemBytes * (kTransB ? 1 : p.ldb);
     q.C = p.ws + static_cast<int64_t>(y) * p.M * p.ldws;

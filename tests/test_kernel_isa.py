@@ -1,0 +1,75 @@
+"""The main loops of the 256x256 kernels, read from the gfx950 assembly hipcc
+emits for them (CPU only: hipcc cross-compiles).
+
+Every loop of every instantiation must keep its accumulators where they are
+(no v_accvgpr_read/write/mov copies: the register allocator has rotated the
+4-wave kernel's 256 accumulators through copies after unrelated source
+changes, which costs several percent and shows in no correctness test), use
+no scratch memory, and issue the MFMA and barrier counts the schedule
+defines: per loop iteration the 8-wave kernel runs two K-steps (8 barriers),
+the 4-wave kernel one (2 barriers); a 128-byte K-step is 64 FP16/BF16 MFMAs
+16x16x32 or 32 FP8 MFMAs 16x16x128 per wave in the 8-wave kernel and twice
+that in the 4-wave kernel.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from matrix_core_scheduling_amd import build
+
+pytestmark = pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not found")
+
+# kernel -> (MFMAs per loop iteration for FP16/BF16, for FP8, barriers per iteration)
+EXPECT = {"gemm_pipelined_kernel": (128, 64, 8), "gemm_interleaved_kernel": (128, 64, 2)}
+SOURCES = {"gemm_pipelined_kernel": "gemm_pipelined.hip", "gemm_interleaved_kernel": "gemm_interleaved.hip"}
+
+
+def loops(asm: str):
+    """{(kernel symbol, loop header): [instruction mnemonics]} of every loop."""
+    out, fn, cur = {}, None, None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            fn, cur = m.group(1), None
+            continue
+        if re.match(r"^(\.LBB\w+|; %bb\.\d+):", line):
+            h = re.search(r"Loop Header", line)
+            i = re.search(r"in Loop: Header=(BB\w+)", line)
+            cur = (fn, line.split(":")[0].lstrip(".L")) if h else ((fn, i.group(1)) if i else None)
+            continue
+        t = line.strip()
+        if cur and fn and t and not t.startswith((";", ".")):
+            out.setdefault(cur, []).append(t.split()[0])
+    return out
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    d = tmp_path_factory.mktemp("isa")
+    return {k: open(build.device_asm(src, str(d / (src + ".s")))).read() for k, src in SOURCES.items()}
+
+
+@pytest.mark.parametrize("kernel", sorted(EXPECT))
+def test_main_loops(asm, kernel):
+    found = loops(asm[kernel])
+    per_fn = {}
+    for (fn, hdr), ops in found.items():
+        if kernel not in fn:
+            continue
+        per_fn.setdefault(fn, []).append((hdr, ops))
+    # one symbol per instantiation: 2 element types x 2 B layouts x 2 outputs (+ FP8 N x K x 2 outputs),
+    # times offset/in-phase for the 8-wave kernel
+    assert len(per_fn) == (20 if kernel == "gemm_pipelined_kernel" else 10), sorted(per_fn)
+    f16_mfma, f8_mfma, bars = EXPECT[kernel]
+    for fn, ls in per_fn.items():
+        fp8 = "ILi2E" in fn
+        for hdr, ops in ls:
+            where = f"{fn} loop {hdr}"
+            copies = [o for o in ops if o.startswith("v_accvgpr_")]
+            assert not copies, f"{where}: {len(copies)} accumulator copies"
+            assert not [o for o in ops if o.startswith("scratch_") or o.startswith("buffer_store")], where
+            assert sum(o.startswith("v_mfma") for o in ops) == (f8_mfma if fp8 else f16_mfma), where
+            assert ops.count("s_barrier") == bars, where
