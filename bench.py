@@ -50,7 +50,7 @@ def traffic_for(workload: str, schedule: str):
     on the current source of the kernel that runs; otherwise None."""
     from matrix_core_scheduling_amd import profiling
 
-    kernel = "pipelined" if schedule in ("auto", "pipelined") else schedule
+    kernel = schedule
     if kernel not in profiling.KERNEL_SOURCES:
         return None
     try:
@@ -103,7 +103,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS))
-    ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "interleaved", "generic"])
+    ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "interleaved", "tile128", "generic"])
     ap.add_argument("--splits", default="auto",
                     help="K-slices (gemm_ex_splitk) or 'auto' (gemm_splitk_suggest; 1 for the default shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -159,7 +159,14 @@ def main(argv=None) -> int:
     dtype = {"f16": mcs.GEMM_DTYPE_F16, "bf16": mcs.GEMM_DTYPE_BF16, "fp8": mcs.GEMM_DTYPE_FP8_E4M3}[w.dtype]
     sched = {"auto": mcs.GEMM_SCHED_AUTO, "pipelined": mcs.GEMM_SCHED_PIPELINED,
              "in_phase": mcs.GEMM_SCHED_IN_PHASE, "interleaved": mcs.GEMM_SCHED_INTERLEAVED,
-             "generic": mcs.GEMM_SCHED_GENERIC}[a.schedule]
+             "tile128": mcs.GEMM_SCHED_TILE128, "generic": mcs.GEMM_SCHED_GENERIC}[a.schedule]
+    # the kernel that runs (AUTO picks by the number of output tiles)
+    eff = a.schedule
+    if a.schedule == "auto":
+        eff = "tile128" if mcs.gemm_auto_schedule(w.M, w.N) == mcs.GEMM_SCHED_TILE128 else "pipelined"
+    eff_sched = {"pipelined": mcs.GEMM_SCHED_PIPELINED, "in_phase": mcs.GEMM_SCHED_IN_PHASE,
+                 "interleaved": mcs.GEMM_SCHED_INTERLEAVED, "tile128": mcs.GEMM_SCHED_TILE128,
+                 "generic": mcs.GEMM_SCHED_GENERIC}[eff]
     lda, ldb, ldc = w.K, (w.K if w.trans_b else w.N), w.N
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
@@ -220,8 +227,7 @@ def main(argv=None) -> int:
     # result of set 0 for the check below (same launch configuration)
     launch(0)
     torch.cuda.synchronize()
-    info = mcs.gemm_kernel_info(dtype, w.trans_b, out_type,
-                                mcs.GEMM_SCHED_PIPELINED if sched == mcs.GEMM_SCHED_AUTO else sched)
+    info = mcs.gemm_kernel_info(dtype, w.trans_b, out_type, eff_sched)
 
     cpu = None
     check = None
@@ -260,7 +266,7 @@ def main(argv=None) -> int:
             bad += int((~oracle.within_tolerance(cg[r0:r1], cref, sabs, out=w.out_type)).sum())
         check = {"rows": rows, "elements": rows * w.N, "outside_tolerance": bad, "pass": bad == 0}
 
-    traffic = traffic_for(w.name, a.schedule)
+    traffic = traffic_for(w.name, eff)
     peak = PEAK_TFLOPS[w.dtype]
     metric = METRIC if w.name == si.HEADLINE else (
         f"{ {'f16': 'FP16', 'bf16': 'BF16', 'fp8': 'FP8 E4M3'}[w.dtype]} GEMM TFLOP/s at "
@@ -282,7 +288,7 @@ def main(argv=None) -> int:
                    "accumulate": "f32", "out": w.out_type,
                    "b_layout": "N x K row-major" if w.trans_b else "K x N row-major",
                    "values": w.dist, "seed": w.seed, "rotating_sets": nrot,
-                   "schedule": a.schedule, "splits": splits},
+                   "schedule": a.schedule, "kernel": eff, "splits": splits},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "pct_of_unit_peak": round(100.0 * tflops / PEAK_TFLOPS_UNITS[w.dtype], 2),
         "batch_median_ms": round(batch_med, 6),

@@ -72,18 +72,25 @@ enum gemm_dtype {
 
 /* Kernel schedule selector for gemm_ex. */
 enum gemm_schedule {
-    GEMM_SCHED_AUTO = 0,       /* what gemm_f16 / gemm_bf16 use: PIPELINED when
-                                  the operands allow it, else GENERIC */
+    GEMM_SCHED_AUTO = 0,       /* what gemm_f16 / gemm_bf16 / gemm_fp8 use:
+                                  when the operands allow it PIPELINED, or
+                                  TILE128 for products with fewer than 128
+                                  output tiles of 256x256
+                                  (gemm_auto_schedule); else GENERIC */
     GEMM_SCHED_PIPELINED = 1,  /* 8 waves, two groups held one stage apart */
     GEMM_SCHED_IN_PHASE = 2,   /* same kernel and stages, groups kept in phase
                                   (no entry/exit offset): the ablation baseline */
     GEMM_SCHED_GENERIC = 3,    /* plain LDS-tiled FMA kernel, any alignment */
-    GEMM_SCHED_INTERLEAVED = 4 /* 4 waves, one per SIMD, each interleaving its
+    GEMM_SCHED_INTERLEAVED = 4, /* 4 waves, one per SIMD, each interleaving its
                                   own MFMA, LDS reads and copies ("Porting
                                   High-Performance HIP Kernels to FlyDSL",
                                   section "A More Complex Kernel"); same tile,
                                   loader, LDS layout and epilogue as PIPELINED:
                                   the ablation of warp-pipelining itself */
+    GEMM_SCHED_TILE128 = 5     /* 128x128 output tiles, 4 waves, a ring of four
+                                  K-step buffers in LDS: for products with few
+                                  256x256 tiles; same operand conditions as
+                                  PIPELINED */
 };
 
 /*
@@ -125,7 +132,7 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K,
 /*
  * gemm_ex -- the same product with the operand type (gemm_dtype) and the
  * kernel schedule (gemm_schedule) chosen by the caller.  PIPELINED,
- * IN_PHASE and INTERLEAVED need 16-byte aligned A, B, C, rows of A and B
+ * IN_PHASE, INTERLEAVED and TILE128 need 16-byte aligned A, B, C, rows of A and B
  * (lda, ldb times the element size) and of K elements that are whole 16-byte
  * chunks, ldc a multiple of 8, and an even N when B is K x N (FP8: B given
  * N x K); asking for them otherwise returns GEMM_EINVAL (nothing is
@@ -137,14 +144,21 @@ int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K,
             void *C, int64_t ldc, int out_type, int schedule,
             hipStream_t stream);
 
+/* The tiled schedule AUTO runs for an M x N product whose operands the tiled
+ * kernels can take: GEMM_SCHED_PIPELINED, or GEMM_SCHED_TILE128 when there
+ * are fewer than 128 output tiles of 256x256 (half of MI355X's compute
+ * units).  GEMM_EINVAL for negative sizes.  No device call. */
+int gemm_auto_schedule(int64_t M, int64_t N);
+
 /*
  * Split K for products with few output tiles (shapes whose 256x256 tiles
  * cannot fill the GPU; the pages' kernels take one workgroup per output tile,
  * this entry point is not from them).  gemm_ex_splitk computes the same C as
  * gemm_ex in two kernels on `stream`: the K range is cut into at most
  * `splits` slices of whole K-steps, each slice's FP32 partial product is
- * written to `workspace` by the 256x256 kernel of `schedule` (AUTO means
- * PIPELINED), and a second kernel sums the slices in order and writes C
+ * written to `workspace` by the tiled kernel of `schedule` (AUTO: the one
+ * gemm_auto_schedule names), and a second kernel sums the slices in order
+ * and writes C
  * rounded to out_type.  The caller owns the workspace (device memory, 16-byte
  * aligned, at least the size gemm_splitk_workspace_bytes reports); the
  * library allocates nothing.  Calls that share a workspace must not overlap.
@@ -166,12 +180,13 @@ int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K,
 int gemm_splitk_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int splits,
                                 int64_t *bytes);
 
-/* A split count for gemm_ex_splitk: 1 unless the 256x256 tiles fill fewer
- * than `cus` compute units (0 = 256, MI355X) and every slice keeps at least
- * 32 K-steps; then as many slices as the idle CUs allow.  (Each slice pays
- * the pipeline's fill and drain and the workspace traffic: on MI355X the
- * 512x4096x8192 FP16 product runs 123.7 us unsplit and 53.0 us with 4
- * slices, while 1024^3, with 16 K-steps, gains nothing.) */
+/* A split count for gemm_ex_splitk with AUTO: 1 unless the output tiles of
+ * the kernel AUTO picks fill fewer than `cus` compute units (0 = 256,
+ * MI355X) and every slice keeps at least 64 K-steps of 128 bytes; then as
+ * many slices as the idle CUs allow.  (Each slice pays the pipeline's fill
+ * and drain and the workspace traffic: on MI355X the 512x4096x8192 FP16
+ * product on 128x128 tiles runs 54.1 us unsplit and 44.7 us with 2 slices,
+ * while 1024^3, with 16 K-steps, only loses.) */
 int gemm_splitk_suggest(int dtype, int64_t M, int64_t N, int64_t K, int cus);
 
 /* Static description of one compiled kernel variant (from the code object). */

@@ -1,7 +1,8 @@
 """Python binding of libmcs_gemm.so, the gfx950 warp-pipelined FP16/BF16/FP8 GEMM.
 
 The functions ``gemm_f16``, ``gemm_bf16``, ``gemm_fp8``, ``gemm_ex``,
-``gemm_ex_splitk``, ``gemm_splitk_workspace_bytes``, ``gemm_splitk_suggest``,
+``gemm_ex_splitk``, ``gemm_splitk_workspace_bytes``, ``gemm_auto_schedule``,
+``gemm_splitk_suggest``,
 ``gemm_kernel_info`` and ``gemm_status_string`` mirror the C ABI in
 ``include/mcs_gemm.h`` one to one
 (sizes, raw device pointers as integers, a raw ``hipStream_t``).  ``gemm``
@@ -25,6 +26,7 @@ GEMM_OK, GEMM_EINVAL, GEMM_EUNSUPPORTED, GEMM_EHIP = 0, -1, -3, -4
 GEMM_OUT_SAME, GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1, 2
 GEMM_DTYPE_F16, GEMM_DTYPE_BF16, GEMM_DTYPE_FP8_E4M3 = 0, 1, 2
 GEMM_SCHED_AUTO, GEMM_SCHED_PIPELINED, GEMM_SCHED_IN_PHASE, GEMM_SCHED_GENERIC, GEMM_SCHED_INTERLEAVED = 0, 1, 2, 3, 4
+GEMM_SCHED_TILE128 = 5
 
 
 class GemmError(RuntimeError):
@@ -63,6 +65,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gemm_ex_splitk.restype = ci
     lib.gemm_splitk_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(i64)]
     lib.gemm_splitk_workspace_bytes.restype = ci
+    lib.gemm_auto_schedule.argtypes = [i64, i64]
+    lib.gemm_auto_schedule.restype = ci
     lib.gemm_splitk_suggest.argtypes = [ci, i64, i64, i64, ci]
     lib.gemm_splitk_suggest.restype = ci
     lib.gemm_kernel_info.argtypes = [ci, ci, ci, ci, ctypes.POINTER(GemmKernelAttrs)]
@@ -110,6 +114,10 @@ def gemm_splitk_workspace_bytes(dtype: int, M: int, N: int, K: int, splits: int)
     if st != GEMM_OK:
         raise GemmError(st, "gemm_splitk_workspace_bytes")
     return n.value
+
+
+def gemm_auto_schedule(M: int, N: int) -> int:
+    return load().gemm_auto_schedule(M, N)
 
 
 def gemm_splitk_suggest(dtype: int, M: int, N: int, K: int, cus: int = 0) -> int:

@@ -171,12 +171,15 @@ struct TileWindows {
     bool bLive[2];
 };
 
-template <int kElem, bool kTransB, int kWaves>
+// kTile: output tile edge (256: two halves per operand; 128: one, half 0);
+// kBOff: byte offset of the B halves within an LDS buffer.
+template <int kElem, bool kTransB, int kWaves, int kTile = kTileM, uint32_t kBOff = kOffB>
 struct Loader {
     static constexpr int P = 16 / kWaves;   // pieces per wave per half
     static constexpr int kEB = elem_bytes(kElem), kStepK = step_k(kElem);
     static_assert(P * kWaves == 16, "waves must divide the 16 pieces of a half");
     static_assert(kTransB || kElem != kElemFP8, "FP8 B is taken given N x K");
+    static_assert(kTile == 256 || kTile == 128, "tile edge");
 
     uint32_t lds0;                   // LDS byte address of buffer 0
     uint32_t cpA[P], cpB[P];         // copy voffsets
@@ -213,8 +216,8 @@ struct Loader {
     // Windows of output tile (tm, tn); tm >= tiles_m gives the no-tile value.
     __device__ __forceinline__ TileWindows windows(int tm, int tn) const {
         TileWindows w;
-        w.m0 = tm * kTileM;
-        w.n0 = tn * kTileN;
+        w.m0 = tm * kTile;
+        w.n0 = tn * kTile;
         const bool live = w.m0 < p.M;
         const uint32_t kb = static_cast<uint32_t>(kEB) * static_cast<uint32_t>(p.K);
         const char *A = static_cast<const char *>(p.A), *B = static_cast<const char *>(p.B);
@@ -270,7 +273,7 @@ struct Loader {
     template <bool kMask = true, int I0 = 0, int I1 = P>
     __device__ __forceinline__ void copy_b(const TileWindows &w, int s, uint32_t buf, int h) const {
         const int kv = p.K - s * kStepK;                      // k left (may be <= 0)
-        const uint32_t dst = lds0 + buf + kOffB + h * kHalf + P * wave * 1024;
+        const uint32_t dst = lds0 + buf + kBOff + h * kHalf + P * wave * 1024;
         if constexpr (kTransB) {
             const i32x4 rs = step_rsrc(w.bAddr[h], w.bEnd[h], w.bKB[h], s);
             static_for<I0, I1>([&](auto i) {
@@ -327,6 +330,67 @@ struct FragOffsets {
         for (int nt = 0; nt < 4; ++nt) {
             const int ch = col0 / 8 + 2 * nt + ((l16 & 3) >> 1);
             tr[nt] = (8 * lg + (l16 >> 2)) * 256 + ((ch ^ fb) * 16) + 8 * (l16 & 1);
+        }
+    }
+};
+
+// Fragment reads of one wave's 64x64 block of a 128x128 quadrant: A rows
+// 64wm.. of an A half, B columns 64wn.. of a B half (the B halves at byte
+// offset kBOff of an LDS buffer).  A fragment is four 16-row (16-column)
+// tiles x two 16-byte k-chunks per lane, read as eight pieces.  The read
+// bases of a K-step are computed once and kept opaque to the compiler, so
+// every piece is a base plus an immediate offset.
+template <bool kTransB, uint32_t kBOff>
+struct Block64Reader {
+    FragOffsets fa, fb;
+
+    __device__ __forceinline__ void init(int wm, int wn, int lane) {
+        fa.rows(64 * wm, lane);
+        if constexpr (kTransB)
+            fb.rows(64 * wn, lane);
+        else
+            fb.cols_tr(64 * wn, lane);
+    }
+
+    struct Bases {
+        uint32_t a[2][2];    // [buffer cur/nxt][ks]: A fragment rows, A half 0
+        uint32_t b[2][2];    // [buffer][ks]: B fragment rows (B given N x K), B half 0
+        uint32_t buf[2];     // LDS byte address of buffer cur / nxt (uniform)
+    };
+
+    __device__ __forceinline__ Bases bases_at(uint32_t lds0, uint32_t cur, uint32_t nxt) const {
+        Bases r;
+        for (int u = 0; u < 2; ++u) {
+            r.buf[u] = lds0 + (u ? nxt : cur);
+            for (int ks = 0; ks < 2; ++ks) {
+                r.a[u][ks] = r.buf[u] + kOffA + fa.row[ks];
+                asm volatile("" : "+v"(r.a[u][ks]));
+                if constexpr (kTransB) {
+                    r.b[u][ks] = r.buf[u] + kBOff + fb.row[ks];
+                    asm volatile("" : "+v"(r.b[u][ks]));
+                }
+            }
+        }
+        return r;
+    }
+
+    // Piece j (k-chunk j >> 2, 16-row tile j & 3) of a fragment of A half h.
+    __device__ __forceinline__ i32x4 read_a(const Bases &bs, int u, int h, int j) const {
+        return lds_read128(bs.a[u][j >> 2] + h * kHalf + (j & 3) * 2048);
+    }
+
+    // Piece j (k-chunk j >> 2, 16-column tile j & 3) of a fragment of B half h.
+    __device__ __forceinline__ i32x4 read_b(const Bases &bs, int u, int h, int j) const {
+        const int ks = j >> 2, nt = j & 3;
+        if constexpr (kTransB) {
+            return lds_read128(bs.b[u][ks] + h * kHalf + nt * 2048);
+        } else {
+            // one address add per piece; the k-row offsets are immediates
+            uint32_t base = bs.buf[u] + kBOff + h * kHalf + fb.tr[nt];
+            asm volatile("" : "+v"(base));
+            const i32x2 lo = lds_read64_tr(base + (32 * ks + 0) * 256);
+            const i32x2 hi = lds_read64_tr(base + (32 * ks + 4) * 256);
+            return i32x4{lo.x, lo.y, hi.x, hi.y};
         }
     }
 };

@@ -53,7 +53,7 @@ int validate(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t 
     if (dtype < GEMM_DTYPE_F16 || dtype > GEMM_DTYPE_FP8_E4M3) return GEMM_EINVAL;
     if (trans_b != 0 && trans_b != 1) return GEMM_EINVAL;
     if (!out_ok(dtype, out_type)) return GEMM_EINVAL;
-    if (schedule < GEMM_SCHED_AUTO || schedule > GEMM_SCHED_INTERLEAVED) return GEMM_EINVAL;
+    if (schedule < GEMM_SCHED_AUTO || schedule > GEMM_SCHED_TILE128) return GEMM_EINVAL;
     if (M < 0 || N < 0 || K < 0) return GEMM_EINVAL;
     if (M > kIntMax || N > kIntMax || K > kIntMax) return GEMM_EUNSUPPORTED;
     if (M == 0 || N == 0) return GEMM_OK;
@@ -72,13 +72,14 @@ int launch(const void *fn, dim3 grid, dim3 block, GemmParams &prm, hipStream_t s
     return to_status(hipLaunchKernel(fn, grid, block, args, 0, stream));
 }
 
-// One of the 256x256 kernels over `slices` K-slices of kslice elements each
-// (slices == 1: the whole product into C).  prm holds A, B, C, sizes and
+// One of the tiled MFMA kernels over `slices` K-slices of kslice elements
+// each (slices == 1: the whole product into C).  prm holds A, B, C, sizes and
 // leading dimensions; tiles, steps and the slice fields are filled here.
 int launch_tiles(int elem, int trans_b, bool out_f32, int schedule, GemmParams &prm, int64_t kslice,
                  int slices, hipStream_t stream) {
-    const int64_t tm = (prm.M + mcs::kTileM - 1) / mcs::kTileM;
-    const int64_t tn = (prm.N + mcs::kTileN - 1) / mcs::kTileN;
+    const int64_t edge = schedule == GEMM_SCHED_TILE128 ? mcs::kTile128 : mcs::kTileM;
+    const int64_t tm = (prm.M + edge - 1) / edge;
+    const int64_t tn = (prm.N + edge - 1) / edge;
     if (tm * tn > kIntMax) return GEMM_EUNSUPPORTED;
     const int64_t nk = (kslice + mcs::step_k(elem) - 1) / mcs::step_k(elem);
     prm.tiles_m = static_cast<int>(tm);
@@ -92,6 +93,11 @@ int launch_tiles(int elem, int trans_b, bool out_f32, int schedule, GemmParams &
                       dim3(mcs::kInterThreads), prm, stream);
     }
     prm.steps = static_cast<int>(nk < 2 ? 2 : (nk + 1) / 2 * 2);
+    if (schedule == GEMM_SCHED_TILE128) {
+        if (elem != mcs::kElemFP8) prm.steps = static_cast<int>(nk);   // one K-step per iteration
+        return launch(mcs::tile128_kernel(elem, trans_b != 0, out_f32), grid,
+                      dim3(mcs::kTile128Threads), prm, stream);
+    }
     return launch(mcs::pipelined_kernel(elem, trans_b != 0, out_f32, schedule == GEMM_SCHED_PIPELINED),
                   grid, dim3(mcs::kPipeThreads), prm, stream);
 }
@@ -109,6 +115,17 @@ void split_plan(int elem, int64_t K, int splits, int64_t &kslice, int &slices) {
 }
 
 int64_t ws_row(int64_t N) { return (N + 3) / 4 * 4; }
+
+// The tiled kernel AUTO runs for aligned operands: the 256x256 warp-pipelined
+// kernel, or the 128x128-tile kernel when the product has fewer 256x256 tiles
+// than half of MI355X's 256 compute units (measured: 1024^3 22.1 -> 10.6 us,
+// 2048x2048x8192 124.7 -> 70.1 us; 3072x3072x4096, 144 tiles, stays faster on
+// the 256x256 kernel, 75.0 against 99.8 us).
+constexpr int64_t kChipCUs = 256;
+int auto_tiled_schedule(int64_t M, int64_t N) {
+    const int64_t tiles = ((M + mcs::kTileM - 1) / mcs::kTileM) * ((N + mcs::kTileN - 1) / mcs::kTileN);
+    return tiles < kChipCUs / 2 ? GEMM_SCHED_TILE128 : GEMM_SCHED_PIPELINED;
+}
 
 }  // namespace
 
@@ -140,7 +157,7 @@ extern "C" int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A
     }
 
     const bool fast = pipelined_ok(elem, N, K, A, lda, B, ldb, trans_b, C, ldc);
-    if (schedule == GEMM_SCHED_AUTO) schedule = fast ? GEMM_SCHED_PIPELINED : GEMM_SCHED_GENERIC;
+    if (schedule == GEMM_SCHED_AUTO) schedule = fast ? auto_tiled_schedule(M, N) : GEMM_SCHED_GENERIC;
     if (schedule != GEMM_SCHED_GENERIC && !fast) return GEMM_EINVAL;
 
     if (schedule == GEMM_SCHED_GENERIC) {
@@ -167,12 +184,18 @@ extern "C" int gemm_splitk_workspace_bytes(int dtype, int64_t M, int64_t N, int6
     return GEMM_OK;
 }
 
+extern "C" int gemm_auto_schedule(int64_t M, int64_t N) {
+    if (M < 0 || N < 0) return GEMM_EINVAL;
+    return auto_tiled_schedule(M, N);
+}
+
 extern "C" int gemm_splitk_suggest(int dtype, int64_t M, int64_t N, int64_t K, int cus) {
     if (dtype < GEMM_DTYPE_F16 || dtype > GEMM_DTYPE_FP8_E4M3 || M <= 0 || N <= 0 || K <= 0) return 1;
-    if (cus <= 0) cus = 256;
-    const int64_t tiles = ((M + mcs::kTileM - 1) / mcs::kTileM) * ((N + mcs::kTileN - 1) / mcs::kTileN);
+    if (cus <= 0) cus = kChipCUs;
+    const int64_t edge = auto_tiled_schedule(M, N) == GEMM_SCHED_TILE128 ? mcs::kTile128 : mcs::kTileM;
+    const int64_t tiles = ((M + edge - 1) / edge) * ((N + edge - 1) / edge);
     const int64_t steps = (K + mcs::step_k(elem_of(dtype)) - 1) / mcs::step_k(elem_of(dtype));
-    int64_t s = steps / 32;                          // at least 32 K-steps per slice
+    int64_t s = steps / 64;                          // at least 64 K-steps per slice
     if (cus / tiles < s) s = cus / tiles;            // no more workgroups than CUs
     return static_cast<int>(s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s));
 }
@@ -197,7 +220,7 @@ extern "C" int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K, const 
         : GEMM_EINVAL;
     const int64_t need = static_cast<int64_t>(slices) * M * ws_row(N) * 4;
     if (!workspace || !aligned16(workspace) || workspace_bytes < need) return GEMM_EINVAL;
-    if (schedule == GEMM_SCHED_AUTO) schedule = GEMM_SCHED_PIPELINED;
+    if (schedule == GEMM_SCHED_AUTO) schedule = auto_tiled_schedule(M, N);
 
     GemmParams prm{};
     prm.A = A;
@@ -262,6 +285,10 @@ extern "C" int gemm_kernel_info(int dtype, int trans_b, int out_type, int schedu
         fn = mcs::interleaved_kernel(elem, trans_b != 0, out_f32);
         threads = mcs::kInterThreads;
         tm = mcs::kTileM; tn = mcs::kTileN; tk = mcs::step_k(elem);
+    } else if (schedule == GEMM_SCHED_TILE128) {
+        fn = mcs::tile128_kernel(elem, trans_b != 0, out_f32);
+        threads = mcs::kTile128Threads;
+        tm = tn = mcs::kTile128; tk = mcs::step_k(elem);
     } else if (schedule == GEMM_SCHED_GENERIC) {
         fn = mcs::generic_kernel(elem, trans_b != 0, out_f32);
         threads = mcs::kGenThreads;

@@ -66,63 +66,21 @@ constexpr int kWaves = kInterThreads / 64;
 constexpr int kCopyWait = 16;              // vmcnt before each barrier
 
 template <int kElem, bool kTransB>
-struct Interleave : Loader<kElem, kTransB, kWaves> {
+struct Interleave : Loader<kElem, kTransB, kWaves>, Block64Reader<kTransB, kOffB> {
     using Loader<kElem, kTransB, kWaves>::lds0;
-    FragOffsets fa, fb;
+    using Reader = Block64Reader<kTransB, kOffB>;
+    using typename Reader::Bases;
+    using Reader::read_a;
+    using Reader::read_b;
 
     __device__ __forceinline__ Interleave(const GemmParams &prm, int tm, int tn)
         : Loader<kElem, kTransB, kWaves>(prm, tm, tn) {
-        const int lane = threadIdx.x & 63;
-        const int wm = this->wave & 1, wn = this->wave >> 1;
-        fa.rows(64 * wm, lane);
-        if constexpr (kTransB)
-            fb.rows(64 * wn, lane);
-        else
-            fb.cols_tr(64 * wn, lane);
+        this->init(this->wave & 1, this->wave >> 1, threadIdx.x & 63);
     }
 
-    // LDS read bases of one K-step, VGPRs kept opaque to the compiler so
-    // that every fragment read is the base plus an immediate offset.
-    struct Bases {
-        uint32_t a[2][2];    // [buffer cur/nxt][ks]: A fragment rows, A half 0
-        uint32_t b[2][2];    // [buffer][ks]: B fragment rows (B given N x K), B half 0
-        uint32_t buf[2];     // LDS byte address of buffer cur / nxt (uniform)
-    };
-
+    // LDS read bases of one K-step (buffers cur and nxt).
     __device__ __forceinline__ Bases bases(uint32_t cur, uint32_t nxt) const {
-        Bases r;
-        for (int u = 0; u < 2; ++u) {
-            r.buf[u] = lds0 + (u ? nxt : cur);
-            for (int ks = 0; ks < 2; ++ks) {
-                r.a[u][ks] = r.buf[u] + kOffA + fa.row[ks];
-                asm volatile("" : "+v"(r.a[u][ks]));
-                if constexpr (kTransB) {
-                    r.b[u][ks] = r.buf[u] + kOffB + fb.row[ks];
-                    asm volatile("" : "+v"(r.b[u][ks]));
-                }
-            }
-        }
-        return r;
-    }
-
-    // Piece j (k-slice j >> 2, 16-row tile j & 3) of a fragment of A half h.
-    __device__ __forceinline__ i32x4 read_a(const Bases &bs, int u, int h, int j) const {
-        return lds_read128(bs.a[u][j >> 2] + h * kHalf + (j & 3) * 2048);
-    }
-
-    // Piece j (k-slice j >> 2, 16-column tile j & 3) of a fragment of B half h.
-    __device__ __forceinline__ i32x4 read_b(const Bases &bs, int u, int h, int j) const {
-        const int ks = j >> 2, nt = j & 3;
-        if constexpr (kTransB) {
-            return lds_read128(bs.b[u][ks] + h * kHalf + nt * 2048);
-        } else {
-            // one address add per piece; the k-row offsets are immediates
-            uint32_t base = bs.buf[u] + kOffB + h * kHalf + fb.tr[nt];
-            asm volatile("" : "+v"(base));
-            const i32x2 lo = lds_read64_tr(base + (32 * ks + 0) * 256);
-            const i32x2 hi = lds_read64_tr(base + (32 * ks + 4) * 256);
-            return i32x4{lo.x, lo.y, hi.x, hi.y};
-        }
+        return this->bases_at(lds0, cur, nxt);
     }
 
     // One cluster: acc += a . b over the K-step while fragment `nf` (operand

@@ -55,6 +55,8 @@ constexpr int elem_bytes(int elem) { return elem == kElemFP8 ? 1 : 2; }
 constexpr int step_k(int elem) { return kStepBytes / elem_bytes(elem); }
 // Within-wave interleaved kernel: the same 256x256x64 tile with 4 waves.
 constexpr int kInterThreads = 256;
+// 128x128-tile kernel: 4 waves.
+constexpr int kTile128 = 128, kTile128Threads = 256;
 // Generic kernel: 64x64 tiles of 256 threads.
 constexpr int kGenTile = 64, kGenThreads = 256;
 
@@ -64,6 +66,7 @@ constexpr int kGenTile = 64, kGenThreads = 256;
 // A 16-bit output is FP16 for FP16 operands and BF16 otherwise.
 const void *pipelined_kernel(int elem, bool trans_b, bool out_f32, bool offset);
 const void *interleaved_kernel(int elem, bool trans_b, bool out_f32);
+const void *tile128_kernel(int elem, bool trans_b, bool out_f32);
 const void *generic_kernel(int elem, bool trans_b, bool out_f32);
 const void *zero_fill_kernel(bool out_f32);
 // Split-K reduction into C: out_kind 0 FP16, 1 BF16, 2 FP32.

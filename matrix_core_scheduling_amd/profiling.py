@@ -32,6 +32,7 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = {
     "pipelined": ("gemm_pipelined.hip", "device.h", "internal.h"),
     "interleaved": ("gemm_interleaved.hip", "device.h", "internal.h"),
+    "tile128": ("gemm_tile128.hip", "device.h", "internal.h"),
 }
 
 

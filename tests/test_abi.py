@@ -19,7 +19,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = mcs.header_functions()
     assert set(names) == {"gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_ex", "gemm_ex_splitk",
-                          "gemm_splitk_workspace_bytes", "gemm_splitk_suggest", "gemm_kernel_info",
+                          "gemm_splitk_workspace_bytes", "gemm_auto_schedule", "gemm_splitk_suggest",
+                          "gemm_kernel_info",
                           "gemm_status_string"}
 
 
@@ -85,6 +86,7 @@ def test_ex_rejects_bad_dtype_and_schedule(lib):
     good = (4, 4, 8, P, 8, P, 8, 0, P, 8, 0)
     assert mcs.gemm_ex(7, *good, 0, 0) == mcs.GEMM_EINVAL
     assert mcs.gemm_ex(0, *good, 9, 0) == mcs.GEMM_EINVAL
+    assert mcs.gemm_ex(0, *good, 6, 0) == mcs.GEMM_EINVAL
     assert mcs.gemm_ex(0, *good, -1, 0) == mcs.GEMM_EINVAL
 
 
@@ -95,9 +97,11 @@ def test_pipelined_schedule_refuses_unaligned_operands(lib):
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_IN_PHASE, 0) == mcs.GEMM_EINVAL
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
+    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_TILE128, 0) == mcs.GEMM_EINVAL
     args = (256, 256, 60, P, 64, P, 64, 1, P, 256, 0)             # K % 8 != 0
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
     assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
+    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_TILE128, 0) == mcs.GEMM_EINVAL
     fp8 = mcs.GEMM_DTYPE_FP8_E4M3
     args = (256, 256, 136, P, 256, P, 256, 1, P, 256, mcs.GEMM_OUT_BF16)  # FP8: K % 16 != 0
     assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
@@ -105,6 +109,7 @@ def test_pipelined_schedule_refuses_unaligned_operands(lib):
     assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
     args = (256, 256, 128, P, 128, P, 256, 0, P, 256, mcs.GEMM_OUT_BF16)  # FP8, B given K x N
     assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
+    assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_TILE128, 0) == mcs.GEMM_EINVAL
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
@@ -144,11 +149,25 @@ def test_splitk_validation_before_launch(lib):
     assert sk(0, 0, 8, 8, 0, 8, 0, 8, 1, 0, 8, 0, mcs.GEMM_SCHED_AUTO, 4, 0, 0, 0) == mcs.GEMM_OK  # empty
 
 
+def test_auto_schedule(lib):
+    P, T = mcs.GEMM_SCHED_PIPELINED, mcs.GEMM_SCHED_TILE128
+    assert mcs.gemm_auto_schedule(4096, 4096) == P                   # 256 tiles of 256x256
+    assert mcs.gemm_auto_schedule(3072, 3072) == P                   # 144
+    assert mcs.gemm_auto_schedule(2048, 4096) == P                   # 128: half the CUs
+    assert mcs.gemm_auto_schedule(2048, 3840) == T                   # 120
+    assert mcs.gemm_auto_schedule(1024, 1024) == T
+    assert mcs.gemm_auto_schedule(512, 4096) == T
+    assert mcs.gemm_auto_schedule(1, 1) == T
+    assert mcs.gemm_auto_schedule(-1, 8) == mcs.GEMM_EINVAL
+
+
 def test_splitk_suggest(lib):
-    f16 = mcs.GEMM_DTYPE_F16
+    f16, fp8 = mcs.GEMM_DTYPE_F16, mcs.GEMM_DTYPE_FP8_E4M3
     assert mcs.gemm_splitk_suggest(f16, 4096, 4096, 8192) == 1        # 256 tiles fill 256 CUs
-    assert mcs.gemm_splitk_suggest(f16, 512, 4096, 8192) == 4         # 32 tiles, 128 K-steps
+    assert mcs.gemm_splitk_suggest(f16, 512, 4096, 8192) == 2         # 128 tiles of 128x128, 128 K-steps
+    assert mcs.gemm_splitk_suggest(fp8, 512, 4096, 8192) == 1         # 64 K-steps of 128 FP8 elements
+    assert mcs.gemm_splitk_suggest(f16, 1024, 1024, 8192) == 2        # 64 tiles, 128 K-steps
     assert mcs.gemm_splitk_suggest(f16, 1024, 1024, 1024) == 1        # 16 K-steps: too short
-    assert mcs.gemm_splitk_suggest(f16, 256, 256, 65536) == 32        # 1024 K-steps, 1 tile
-    assert mcs.gemm_splitk_suggest(f16, 512, 4096, 8192, 128) == 4
-    assert mcs.gemm_splitk_suggest(f16, 512, 4096, 8192, 64) == 2
+    assert mcs.gemm_splitk_suggest(f16, 256, 256, 65536) == 16        # 4 tiles, 1024 K-steps
+    assert mcs.gemm_splitk_suggest(f16, 256, 256, 65536, 32) == 8
+    assert mcs.gemm_splitk_suggest(f16, 512, 4096, 8192, 128) == 1

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 FP8_NAN = 0x7F
 SCHEDS = {"pipelined": mcs.GEMM_SCHED_PIPELINED, "in_phase": mcs.GEMM_SCHED_IN_PHASE,
-          "interleaved": mcs.GEMM_SCHED_INTERLEAVED}
+          "interleaved": mcs.GEMM_SCHED_INTERLEAVED, "tile128": mcs.GEMM_SCHED_TILE128}
 
 
 def operands(dist, M, N, K, trans_b, seed, lda=None, ldb=None, nan_pad=False):
@@ -44,7 +44,7 @@ SHAPES = [(256, 256, 256), (1, 1, 16), (17, 33, 16), (300, 520, 208), (513, 257,
           (258, 130, 136), (200, 96, 1000)]
 
 
-@pytest.mark.parametrize("sched", ["pipelined", "in_phase", "interleaved"])
+@pytest.mark.parametrize("sched", ["pipelined", "in_phase", "interleaved", "tile128"])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 @pytest.mark.parametrize("trans_b", [0, 1])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -70,7 +70,7 @@ def test_shapes_every_element(shape, trans_b, out, sched):
 INT_SHAPES = [(256, 256, 32), (512, 256, 128), (256, 512, 192), (512, 512, 448), (1024, 1024, 512)]
 
 
-@pytest.mark.parametrize("sched", ["pipelined", "interleaved", "generic"])
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved", "tile128", "generic"])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 @pytest.mark.parametrize("shape", INT_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_integer_regime_bit_exact(shape, out, sched):
@@ -112,6 +112,8 @@ def test_interleaved_matches_pipelined_bitwise(out):
         p = run("fp8", M, N, K, a, b, 1, out=out, schedule=mcs.GEMM_SCHED_PIPELINED)[1]
         i = run("fp8", M, N, K, a, b, 1, out=out, schedule=mcs.GEMM_SCHED_INTERLEAVED)[1]
         assert np.array_equal(p, i), (M, N, K)
+        t = run("fp8", M, N, K, a, b, 1, out=out, schedule=mcs.GEMM_SCHED_TILE128)[1]
+        assert np.array_equal(p, t), (M, N, K)
 
 
 def test_nan_operand_propagates():
@@ -136,7 +138,8 @@ def test_misaligned_operand_takes_generic_path_and_is_correct():
 
 def test_fp8_kernels_have_no_spills():
     for out in (mcs.GEMM_OUT_BF16, mcs.GEMM_OUT_F32):
-        for sched, threads in ((mcs.GEMM_SCHED_PIPELINED, 512), (mcs.GEMM_SCHED_INTERLEAVED, 256)):
+        for sched, threads in ((mcs.GEMM_SCHED_PIPELINED, 512), (mcs.GEMM_SCHED_INTERLEAVED, 256),
+                               (mcs.GEMM_SCHED_TILE128, 256)):
             info = mcs.gemm_kernel_info(mcs.GEMM_DTYPE_FP8_E4M3, 1, out, sched)
             assert info["local_bytes"] == 0, info
             assert info["shared_bytes"] == 128 * 1024, info

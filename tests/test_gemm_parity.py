@@ -15,7 +15,8 @@ from tests.gpu_util import assert_bit_exact, assert_within_tolerance, run
 pytestmark = pytest.mark.gpu
 
 SCHEDS = {"pipelined": mcs.GEMM_SCHED_PIPELINED, "in_phase": mcs.GEMM_SCHED_IN_PHASE,
-          "interleaved": mcs.GEMM_SCHED_INTERLEAVED, "generic": mcs.GEMM_SCHED_GENERIC}
+          "interleaved": mcs.GEMM_SCHED_INTERLEAVED, "generic": mcs.GEMM_SCHED_GENERIC,
+          "tile128": mcs.GEMM_SCHED_TILE128}
 
 
 def operands(elem, dist, M, N, K, trans_b, seed, lda=None, ldb=None, nan_pad=False):
@@ -54,7 +55,7 @@ def pipelined_eligible(N, K, trans_b):
     return K % 8 == 0 and (trans_b or N % 2 == 0)
 
 
-@pytest.mark.parametrize("sched", ["pipelined", "in_phase", "interleaved"])
+@pytest.mark.parametrize("sched", ["pipelined", "in_phase", "interleaved", "tile128"])
 @pytest.mark.parametrize("out", ["same", "f32"])
 @pytest.mark.parametrize("trans_b", [0, 1])
 @pytest.mark.parametrize("elem", ["f16", "bf16"])
@@ -98,7 +99,7 @@ def test_generic_kernel_every_element(elem, trans_b):
 INT_SHAPES = [(256, 256, 32), (512, 256, 64), (256, 512, 192), (512, 512, 448), (1024, 1024, 512)]
 
 
-@pytest.mark.parametrize("sched", ["pipelined", "interleaved"])
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved", "tile128"])
 @pytest.mark.parametrize("out", ["same", "f32"])
 @pytest.mark.parametrize("trans_b", [0, 1])
 @pytest.mark.parametrize("elem", ["f16", "bf16"])
@@ -216,6 +217,38 @@ def test_interleaved_matches_pipelined_bitwise(elem, trans_b, out):
         assert np.array_equal(p, i), (M, N, K)
 
 
+@pytest.mark.parametrize("out", ["same", "f32"])
+@pytest.mark.parametrize("trans_b", [0, 1])
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+def test_tile128_matches_pipelined_bitwise(elem, trans_b, out):
+    """The 128x128-tile kernel runs the same MFMA sequence per output element
+    as the 256x256 kernels (K-steps in order, two k-chunks each), so the
+    results agree bit for bit."""
+    for (M, N, K) in [(1024, 768, 2048), (300, 520, 200), (513, 264, 1000), (129, 136, 64)]:
+        a, b = operands(elem, "normal", M, N, K, trans_b, seed=M + K)
+        p = run(elem, M, N, K, a, b, trans_b, out=out, schedule=mcs.GEMM_SCHED_PIPELINED)[1]
+        t = run(elem, M, N, K, a, b, trans_b, out=out, schedule=mcs.GEMM_SCHED_TILE128)[1]
+        assert np.array_equal(p, t), (M, N, K)
+
+
+@pytest.mark.parametrize("name", [n for n, w in si.WORKLOADS.items() if w.M * w.N * w.K <= 2 ** 31
+                                  or w.M <= 512])
+def test_workload_tile128(name):
+    """Workloads with few 256x256 tiles through the 128x128-tile kernel:
+    every element (sampled points for the 512x4096x8192 share)."""
+    w = si.WORKLOADS[name]
+    a, b = w.operands(0)
+    c, _ = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, schedule=mcs.GEMM_SCHED_TILE128)
+    if w.M * w.N * w.K <= 2 ** 31:
+        cref, sabs = oracle.gemm(a, b, w.dtype, w.trans_b)
+        assert_within_tolerance(c, cref, sabs, name, out=w.out_type)
+    else:
+        ii, jj = sample_points(w.M, w.N, 3000, seed=w.seed + 2)
+        cref, sabs = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
+        assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name,
+                                out=w.out_type)
+
+
 @pytest.mark.parametrize("name", [n for n, w in si.WORKLOADS.items() if w.M * w.N >= 4096 * 4096])
 def test_workload_interleaved(name):
     """Full-size workloads through the 4-wave kernel: sampled oracle parity and
@@ -287,7 +320,8 @@ def test_kernels_have_no_spills():
     for dt in (mcs.GEMM_DTYPE_F16, mcs.GEMM_DTYPE_BF16):
         for out in (mcs.GEMM_OUT_SAME, mcs.GEMM_OUT_F32):
             for tb in (0, 1):
-                for sched, threads in ((mcs.GEMM_SCHED_PIPELINED, 512), (mcs.GEMM_SCHED_INTERLEAVED, 256)):
+                for sched, threads in ((mcs.GEMM_SCHED_PIPELINED, 512), (mcs.GEMM_SCHED_INTERLEAVED, 256),
+                                       (mcs.GEMM_SCHED_TILE128, 256)):
                     info = mcs.gemm_kernel_info(dt, tb, out, sched)
                     assert info["local_bytes"] == 0, info
                     assert info["shared_bytes"] == 128 * 1024, info

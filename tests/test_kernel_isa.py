@@ -1,15 +1,16 @@
 """The main loops of the 256x256 kernels, read from the gfx950 assembly hipcc
 emits for them (CPU only: hipcc cross-compiles).
 
-Every loop of every instantiation must keep its accumulators where they are
-(no v_accvgpr_read/write/mov copies: the register allocator has rotated the
-4-wave kernel's 256 accumulators through copies after unrelated source
-changes, which costs several percent and shows in no correctness test), use
-no scratch memory, and issue the MFMA and barrier counts the schedule
-defines: per loop iteration the 8-wave kernel runs two K-steps (8 barriers),
-the 4-wave kernel one (2 barriers); a 128-byte K-step is 64 FP16/BF16 MFMAs
-16x16x32 or 32 FP8 MFMAs 16x16x128 per wave in the 8-wave kernel and twice
-that in the 4-wave kernel.
+Every loop of every instantiation must keep its accumulators and fragments
+where they are (no v_accvgpr_read/write/mov copies: the register allocator
+has rotated the 4-wave kernel's 256 accumulators through copies after
+unrelated source changes, which costs several percent and shows in no
+correctness test), use no scratch memory, and issue the MFMA and barrier
+counts the schedule defines.  Per loop iteration the 8-wave kernel runs two
+K-steps (8 barriers), the 4-wave kernel one (2 barriers), the 128x128-tile
+kernel one (1 barrier; FP8: two); a 128-byte K-step is 64 FP16/BF16 MFMAs
+16x16x32 or 32 FP8 MFMAs 16x16x128 per wave in the 8-wave kernel, twice
+that in the 4-wave kernel and half of it in the 128x128-tile kernel.
 """
 import os
 import re
@@ -22,9 +23,12 @@ from matrix_core_scheduling_amd import build
 
 pytestmark = pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc not found")
 
-# kernel -> (MFMAs per loop iteration for FP16/BF16, for FP8, barriers per iteration)
-EXPECT = {"gemm_pipelined_kernel": (128, 64, 8), "gemm_interleaved_kernel": (128, 64, 2)}
-SOURCES = {"gemm_pipelined_kernel": "gemm_pipelined.hip", "gemm_interleaved_kernel": "gemm_interleaved.hip"}
+# kernel -> (MFMAs per loop iteration for FP16/BF16, for FP8, barriers per iteration for each,
+#            instantiations)
+EXPECT = {"gemm_pipelined_kernel": (128, 64, 8, 8, 20), "gemm_interleaved_kernel": (128, 64, 2, 2, 10),
+          "gemm_tile128_kernel": (32, 32, 1, 2, 10)}
+SOURCES = {"gemm_pipelined_kernel": "gemm_pipelined.hip", "gemm_interleaved_kernel": "gemm_interleaved.hip",
+           "gemm_tile128_kernel": "gemm_tile128.hip"}
 
 
 def loops(asm: str):
@@ -62,8 +66,8 @@ def test_main_loops(asm, kernel):
         per_fn.setdefault(fn, []).append((hdr, ops))
     # one symbol per instantiation: 2 element types x 2 B layouts x 2 outputs (+ FP8 N x K x 2 outputs),
     # times offset/in-phase for the 8-wave kernel
-    assert len(per_fn) == (20 if kernel == "gemm_pipelined_kernel" else 10), sorted(per_fn)
-    f16_mfma, f8_mfma, bars = EXPECT[kernel]
+    f16_mfma, f8_mfma, f16_bars, f8_bars, count = EXPECT[kernel]
+    assert len(per_fn) == count, sorted(per_fn)
     for fn, ls in per_fn.items():
         fp8 = "ILi2E" in fn
         for hdr, ops in ls:
@@ -72,4 +76,4 @@ def test_main_loops(asm, kernel):
             assert not copies, f"{where}: {len(copies)} accumulator copies"
             assert not [o for o in ops if o.startswith("scratch_") or o.startswith("buffer_store")], where
             assert sum(o.startswith("v_mfma") for o in ops) == (f8_mfma if fp8 else f16_mfma), where
-            assert ops.count("s_barrier") == bars, where
+            assert ops.count("s_barrier") == (f8_bars if fp8 else f16_bars), where

@@ -62,12 +62,12 @@ CASES = [  # (elem, trans_b, out, M, N, K, splits)
 ]
 
 
-@pytest.mark.parametrize("sched", ["pipelined", "in_phase", "interleaved"])
+@pytest.mark.parametrize("sched", ["pipelined", "in_phase", "interleaved", "tile128"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
 def test_splitk_every_element(case, sched):
     elem, trans_b, out, M, N, K, splits = case
     schedule = {"pipelined": mcs.GEMM_SCHED_PIPELINED, "in_phase": mcs.GEMM_SCHED_IN_PHASE,
-                "interleaved": mcs.GEMM_SCHED_INTERLEAVED}[sched]
+                "interleaved": mcs.GEMM_SCHED_INTERLEAVED, "tile128": mcs.GEMM_SCHED_TILE128}[sched]
     a, b = operands(elem, "normal", M, N, K, trans_b, seed=300 + M + K + splits)
     cref, sabs = oracle.gemm(a, b, elem, trans_b)
     ldc = (N + 7) // 8 * 8 + 8
@@ -100,8 +100,9 @@ def test_splitk_schedules_agree_bitwise():
     M, N, K = 768, 1024, 3072
     a, b = operands("bf16", "normal", M, N, K, 1, seed=9)
     outs = [run_splitk("bf16", M, N, K, a, b, 1, "same", s, 6)[1]
-            for s in (mcs.GEMM_SCHED_PIPELINED, mcs.GEMM_SCHED_IN_PHASE, mcs.GEMM_SCHED_INTERLEAVED)]
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+            for s in (mcs.GEMM_SCHED_PIPELINED, mcs.GEMM_SCHED_IN_PHASE, mcs.GEMM_SCHED_INTERLEAVED,
+                      mcs.GEMM_SCHED_TILE128)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
 def test_splitk_shard_workload_sampled():
