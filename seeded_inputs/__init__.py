@@ -245,3 +245,61 @@ WORKLOADS = {
     "f16_512x4096x8192": Workload("f16_512x4096x8192", "f16", 512, 4096, 8192, 1, "uniform", "same", 1007),
 }
 HEADLINE = "f16_4096x4096x8192"
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """One synthetic attention workload: Q (B,H,Sq,D), K and V (B,H,Sk,D), all
+    of one operand type, row-major with D contiguous; scale 1/sqrt(D)."""
+    name: str
+    dtype: str          # "f16" | "bf16"
+    B: int
+    H: int
+    Sq: int
+    Sk: int
+    D: int
+    causal: bool
+    dist: str
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def flops(self) -> int:
+        """2 products of 2*Sq*Sk*D each per head; causal counts the allowed
+        (query, key) pairs only."""
+        pairs = self.Sq * self.Sk
+        if self.causal:
+            off = self.Sk - self.Sq
+            pairs = sum(max(0, min(self.Sk, i + off + 1)) for i in range(self.Sq))
+        return 4 * self.B * self.H * pairs * self.D
+
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once and O written once (operand type), plus the FP32 lse."""
+        return 2 * self.B * self.H * self.D * (2 * self.Sq + 2 * self.Sk) + 4 * self.B * self.H * self.Sq
+
+    def operands(self, rotation: int = 0):
+        """(Q, K, V) bit patterns for rotation set ``rotation``."""
+        q = matrix_bits(self.dtype, self.dist, self.B * self.H * self.Sq, self.D, seed=self.seed,
+                        stream=3 * rotation).reshape(self.B, self.H, self.Sq, self.D)
+        k = matrix_bits(self.dtype, self.dist, self.B * self.H * self.Sk, self.D, seed=self.seed,
+                        stream=3 * rotation + 1).reshape(self.B, self.H, self.Sk, self.D)
+        v = matrix_bits(self.dtype, self.dist, self.B * self.H * self.Sk, self.D, seed=self.seed,
+                        stream=3 * rotation + 2).reshape(self.B, self.H, self.Sk, self.D)
+        return q, k, v
+
+
+# Attention workloads: a small case the oracle finishes in seconds, and
+# 4 sequences x 32 heads x 4096 tokens at head size 128 (16k tokens of a
+# 4096-wide model), plain, causal and BF16.  Values normal(0, 1).
+ATTN_WORKLOADS = {
+    "attn_f16_b1h4s512d128": AttnWorkload("attn_f16_b1h4s512d128", "f16", 1, 4, 512, 512, 128, False, "normal", 2001),
+    "attn_f16_b4h32s4096d128": AttnWorkload("attn_f16_b4h32s4096d128", "f16", 4, 32, 4096, 4096, 128, False,
+                                            "normal", 2002),
+    "attn_f16_b4h32s4096d128_causal": AttnWorkload("attn_f16_b4h32s4096d128_causal", "f16", 4, 32, 4096, 4096,
+                                                   128, True, "normal", 2003),
+    "attn_bf16_b4h32s4096d128": AttnWorkload("attn_bf16_b4h32s4096d128", "bf16", 4, 32, 4096, 4096, 128, False,
+                                             "normal", 2004),
+}
