@@ -1,13 +1,15 @@
-"""Python binding of libmcs_gemm.so, the gfx950 warp-pipelined FP16/BF16/FP8 GEMM.
+"""Python binding of libmcs_gemm.so: the gfx950 warp-pipelined FP16/BF16/FP8 GEMM
+and the attention forward pass built in the same stage abstraction.
 
 The functions ``gemm_f16``, ``gemm_bf16``, ``gemm_fp8``, ``gemm_ex``,
 ``gemm_ex_splitk``, ``gemm_splitk_workspace_bytes``, ``gemm_auto_schedule``,
 ``gemm_splitk_suggest``,
-``gemm_kernel_info`` and ``gemm_status_string`` mirror the C ABI in
-``include/mcs_gemm.h`` one to one
+``gemm_kernel_info``, ``gemm_status_string`` and ``attention_fwd`` mirror the
+C ABI in ``include/mcs_gemm.h`` and ``include/mcs_attention.h`` one to one
 (sizes, raw device pointers as integers, a raw ``hipStream_t``).  ``gemm``
 marshals torch tensors onto them: torch provides device memory and the
-current stream, every step of the product runs in the library's HIP kernels.
+current stream, every step of the product runs in the library's HIP kernels;
+``attention`` does the same for the attention forward pass.
 
 There is no fallback: if the library is not built, every call raises.
 Build it with ``python -m matrix_core_scheduling_amd.build``.
@@ -21,6 +23,7 @@ import re
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_PKG, "libmcs_gemm.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "mcs_gemm.h")
+ATTN_HEADER = os.path.join(os.path.dirname(_PKG), "include", "mcs_attention.h")
 
 GEMM_OK, GEMM_EINVAL, GEMM_EUNSUPPORTED, GEMM_EHIP = 0, -1, -3, -4
 GEMM_OUT_SAME, GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1, 2
@@ -71,16 +74,23 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gemm_splitk_suggest.restype = ci
     lib.gemm_kernel_info.argtypes = [ci, ci, ci, ci, ctypes.POINTER(GemmKernelAttrs)]
     lib.gemm_kernel_info.restype = ci
+    lib.attention_fwd.argtypes = [ci, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, ctypes.c_float, ci, vp]
+    lib.attention_fwd.restype = ci
     lib.gemm_status_string.argtypes = [ci]
     lib.gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
 
-def header_functions(path: str = HEADER) -> list[str]:
-    """Names of the functions include/mcs_gemm.h declares."""
-    text = open(path).read()
-    return re.findall(r"^(?:int|const char \*)\s*(\w+)\s*\(", text, flags=re.M)
+def header_functions(paths=(HEADER, ATTN_HEADER)) -> list[str]:
+    """Names of the functions the headers under include/ declare."""
+    if isinstance(paths, str):
+        paths = (paths,)
+    names = []
+    for path in paths:
+        text = open(path).read()
+        names += re.findall(r"^(?:int|const char \*)\s*(\w+)\s*\(", text, flags=re.M)
+    return names
 
 
 # ---- the C ABI, one to one --------------------------------------------------
@@ -134,6 +144,11 @@ def gemm_kernel_info(dtype: int, trans_b: int, out_type: int, schedule: int) -> 
 
 def gemm_status_string(status: int) -> str:
     return load().gemm_status_string(status).decode()
+
+
+def attention_fwd(dtype, batch, heads, seq_q, seq_k, head_dim, Q, K, V, O, lse, scale, causal, stream) -> int:
+    return load().attention_fwd(dtype, batch, heads, seq_q, seq_k, head_dim, Q, K, V, O, lse, scale,
+                                causal, stream)
 
 
 # ---- torch marshalling ---------------------------------------------------
@@ -193,3 +208,37 @@ def gemm(A, B, trans_b: bool = False, out=None, out_dtype=None,
     if st != GEMM_OK:
         raise GemmError(st, "gemm")
     return out
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+              with_lse: bool = True, stream=None):
+    """Attention forward through ``attention_fwd``: q (B, H, Sq, D), k and v
+    (B, H, Sk, D) contiguous float16 or bfloat16 CUDA tensors, D = 128.
+    Returns (out, lse) -- out like q, lse float32 (B, H, Sq) or None -- both
+    allocated by torch unless given.  Runs on the current stream (or
+    ``stream``) and does not synchronise."""
+    import math
+
+    import torch
+
+    dtypes = {torch.float16: GEMM_DTYPE_F16, torch.bfloat16: GEMM_DTYPE_BF16}
+    if q.dtype not in dtypes or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must all be float16 or all bfloat16")
+    if q.dim() != 4 or k.shape != v.shape or k.dim() != 4 or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q (B,H,Sq,D), k and v (B,H,Sk,D) expected")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k and v must be contiguous")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if with_lse and lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    st = attention_fwd(dtypes[q.dtype], B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                       out.data_ptr(), lse.data_ptr() if lse is not None else None, scale, int(bool(causal)),
+                       _stream_handle(stream))
+    if st != GEMM_OK:
+        raise GemmError(st, "attention")
+    return out, lse

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["gemm_pipelined.hip", "gemm_interleaved.hip", "gemm_tile128.hip", "gemm_generic.hip",
-           "gemm_api.hip"]
+           "gemm_api.hip", "attention_fwd.hip"]
 
 # Packed-FP32 instructions stay off: hipcc would otherwise form v_pk_* FP32
 # arithmetic from ordinary float code.

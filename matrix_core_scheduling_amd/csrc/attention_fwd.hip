@@ -1,0 +1,384 @@
+// Attention forward pass for gfx950 in the stage abstraction of the GEMM
+// kernel: "Two Waves, One Stage Apart: Warp-Pipelining Triton GEMMs on AMD
+// Instinct", section "Beyond GEMM: FlashAttention" (Figure 11) describes the
+// loop -- per block of keys a QK product, the two halves of an online
+// softmax, a PV product and the movement of the next key/value blocks, the
+// QK of block i+1 issued before the PV of block i, one wave group's matrix
+// work overlapping the other group's softmax.  That page gives the schedule
+// for MI450 only, with no measurements; this is its MI355X form.
+//
+// Workgroup: 8 waves, 256 query rows of one (batch, head); wave w owns rows
+// 32w..32w+31 (two 16-row MFMA tiles).  Group A = waves 0-3, group B = waves
+// 4-7; each SIMD holds one wave of each.  Head size 128, keys in blocks of
+// 64.  Per block each wave runs 32 MFMAs 16x16x32 for S = Q K^T (its 32 rows
+// x 64 keys) and 32 for O += P V (32 rows x 128), FP32 accumulation.
+//
+// Stages of one trip (i = 0 .. blocks-2), each ended by a workgroup barrier;
+// group B runs one stage behind group A (an extra barrier on entry for B and
+// on exit for A, as in the GEMM), so each MFMA stage of one group overlaps a
+// softmax stage of the other:
+//   0  MFMA   S(i+1) = Q K(i+1)^T                 (K fragments read in stage 3)
+//   1  VALU   O *= alpha(i); V(i) fragments; row max of S(i+1): m(i+1),
+//             alpha(i+1) = 2^(m(i) - m(i+1)); copies of block i+3; wait for
+//             block i+2
+//   2  MFMA   O += P(i) V(i)
+//   3  VALU   P(i+1) = 2^(c S(i+1) - m(i+1)) rounded to the operand type,
+//             l = alpha(i+1) l + row sums; K(i+2) fragments
+// with c = scale * log2(e).  A prologue computes S(0), P(0); a drain applies
+// alpha and P V of the last block; then O / l is stored with
+// lse = (m + log2 l) ln 2.
+//
+// LDS: a ring of four blocks [K | V] of 16 KiB each (64 keys x 256 bytes),
+// filled by buffer_load ... lds (all 8 waves, two 1-KiB pieces of K and two
+// of V each per block); keys past the end read as zeros and are masked.  K
+// rows store 16-byte chunk c at c ^ (row & 15) (the ds_read_b128 of 16 rows
+// at one chunk is conflict-free); V rows at c ^ 2(row & 7) (each half-wave
+// of a transposing ds_read_b64_tr_b16 touches 8 rows x 32 bytes, distinct
+// banks).  Waits:
+//   * copy -> read: block i+2 is copied during trip i-1 (stage 1) and each
+//     wave waits vmcnt(4) (only the copies of block i+3 may fly) at the end
+//     of stage 1 of trip i; its K is read in stage 3 of trip i (the other
+//     group's wait is two stages earlier), its V later.
+//   * read -> refill: block i+3 goes into the slot of block i-1, whose V was
+//     read in stage 1 of trip i-1 (lgkmcnt(0) before that stage's barrier),
+//     four stages before the copies.
+//
+// The probabilities are packed straight from the S accumulators: a lane
+// holds 4 consecutive keys of one row per 16-key tile, so the PV MFMA takes
+// keys {4g..4g+3, 16+4g..16+4g+3} of a 32-key chunk in lane group g, and the
+// V fragment is read with the same key order (transposing reads of k-rows
+// 4g+e and 16+4g+e).
+#include "device.h"
+
+#include "mcs_attention.h"
+
+#include <cmath>
+
+namespace mcs {
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kRowBytes = kHeadDim * 2;                    // one K / V / Q row
+constexpr int kQRows = 256;                                // query rows per workgroup
+constexpr int kKeys = 64;                                  // keys per block
+constexpr int kAttnWaves = 8;
+constexpr uint32_t kKVTile = kKeys * kRowBytes;            // 16 KiB
+constexpr uint32_t kKVSlot = 2 * kKVTile;                  // K | V
+constexpr int kKVSlots = 4;
+
+struct AttnParams {
+    const char *Q, *K, *V;
+    char *O;
+    float *lse;
+    int Sq, Sk;
+    int nq;        // query blocks per (batch, head)
+    int groups;    // batch * heads
+    float c;       // scale * log2(e)
+    int off;       // Sk - Sq (causal masks aligned at the bottom right)
+};
+
+// Workgroup -> (batch*head, query block): each XCD takes a contiguous range,
+// so the query blocks of one head share that XCD's L2 copy of K and V.
+__device__ __forceinline__ void attn_coords(const AttnParams &p, int wg, int &bh, int &qb) {
+    const int total = p.nq * p.groups;
+    const int xcd = wg & 7, j = wg >> 3;
+    const int q = total >> 3, r = total & 7;
+    const int v = xcd * q + min(xcd, r) + j;
+    bh = v / p.nq;
+    qb = v - bh * p.nq;
+}
+
+template <int kElem>
+__device__ __forceinline__ i32x2 pack4(f32x4 v) {
+    if constexpr (kElem == kElemBF16)
+        return __builtin_bit_cast(i32x2, __builtin_convertvector(v, bf16x4));
+    else
+        return __builtin_bit_cast(i32x2, __builtin_convertvector(v, f16x4));
+}
+
+template <int kElem, bool kCausal>
+__global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[kKVSlots * kKVSlot];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool groupB = wave >= kAttnWaves / 2;
+    const int g = lane >> 4, r16 = lane & 15;
+
+    int bh, qb;
+    attn_coords(p, blockIdx.x, bh, qb);
+    const int q0 = qb * kQRows;
+    const int wrow = q0 + 32 * wave;                           // this wave's first query row
+    const int64_t qbase = static_cast<int64_t>(bh) * p.Sq * kRowBytes;
+    const int64_t kbase = static_cast<int64_t>(bh) * p.Sk * kRowBytes;
+
+    // key blocks: every key, or (causal) those the workgroup's last row sees
+    int kend = p.Sk;
+    if constexpr (kCausal) kend = max(0, min(p.Sk, min(p.Sq, q0 + kQRows) + p.off));
+    const int nblk = (kend + kKeys - 1) / kKeys;
+
+    // Q fragments (MFMA row operand): rows wrow + 16mt + r16, d 32dc + 8g ..
+    i32x4 qf[2][4];
+    for (int mt = 0; mt < 2; ++mt) {
+        const int row = wrow + 16 * mt + r16;
+        const char *src = p.Q + qbase + static_cast<int64_t>(min(row, p.Sq - 1)) * kRowBytes + 16 * g;
+        for (int dc = 0; dc < 4; ++dc) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(src + 64 * dc);
+            qf[mt][dc] = row < p.Sq ? v : i32x4{0, 0, 0, 0};
+        }
+    }
+
+    f32x4 o[2][2][4];                                          // [mt][d half][16-column tile]
+    for (int mt = 0; mt < 2; ++mt)
+        for (int h = 0; h < 2; ++h)
+            for (int t = 0; t < 4; ++t) o[mt][h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, alpha[2] = {1.f, 1.f};
+
+    if (nblk > 0) {
+        const uint32_t lds0 = lds_address(smem);
+        // copy lanes: wave w moves pieces 2w, 2w+1 (4 rows x 256 bytes each)
+        // of the K and of the V block; lane (x, pch) fills physical chunk pch
+        // of row x of a piece
+        uint32_t cpK[2], cpV[2];
+        {
+            const int x = lane >> 4, pch = lane & 15;
+            for (int i = 0; i < 2; ++i) {
+                const int row = 4 * (2 * wave + i) + x;
+                cpK[i] = static_cast<uint32_t>(row * kRowBytes + (pch ^ (row & 15)) * 16);
+                cpV[i] = static_cast<uint32_t>(row * kRowBytes + (pch ^ (2 * (row & 7))) * 16);
+            }
+        }
+        auto copy_block = [&](int j) {
+            const int rows = j < nblk ? min(kKeys, p.Sk - j * kKeys) : 0;
+            const uint32_t nrec = rows > 0 ? static_cast<uint32_t>(rows * kRowBytes) : 0u;
+            const int64_t at = kbase + static_cast<int64_t>(j) * kKVTile;
+            const i32x4 rk = make_rsrc(p.K + at, nrec);
+            const i32x4 rv = make_rsrc(p.V + at, nrec);
+            const uint32_t dst = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + 2 * wave * 1024;
+            copy16<0>(rk, dst, cpK[0]);
+            copy16<1024>(rk, dst, cpK[1]);
+            copy16<kKVTile>(rv, dst, cpV[0]);
+            copy16<kKVTile + 1024>(rv, dst, cpV[1]);
+        };
+
+        // fragment read offsets within a slot
+        uint32_t kofs[4], vofs[4 * 2];
+        for (int dc = 0; dc < 4; ++dc)
+            kofs[dc] = static_cast<uint32_t>(r16 * kRowBytes + (((4 * dc + g) ^ r16) * 16));
+        {
+            const int rr = 4 * (g & 1) + (r16 >> 2);               // (k-row) & 7 of this lane's reads
+            const int base = (4 * g + (r16 >> 2)) * kRowBytes + 16 * ((r16 & 3) >> 1) + 8 * (r16 & 1);
+            for (int dt = 0; dt < 8; ++dt) vofs[dt] = static_cast<uint32_t>(base + 32 * (dt ^ rr));
+        }
+
+        i32x4 kf[4][4];     // K block fragments [16-key tile][32-d chunk]
+        i32x4 vf[8][2];     // V block fragments [16-d tile][32-key chunk]
+        i32x4 pf[2][2];     // P [mt][32-key chunk], operand type
+        f32x4 s[2][4];      // S [mt][16-key tile]
+
+        auto read_k = [&](int j) {
+            const uint32_t b = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot;
+            for (int kt = 0; kt < 4; ++kt)
+                for (int dc = 0; dc < 4; ++dc) kf[kt][dc] = lds_read128(b + kt * 16 * kRowBytes + kofs[dc]);
+        };
+        auto read_v = [&](int j) {
+            const uint32_t b = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + kKVTile;
+            for (int c = 0; c < 2; ++c)
+                for (int dt = 0; dt < 8; ++dt) {
+                    const i32x2 lo = lds_read64_tr(b + (32 * c) * kRowBytes + vofs[dt]);
+                    const i32x2 hi = lds_read64_tr(b + (32 * c + 16) * kRowBytes + vofs[dt]);
+                    vf[dt][c] = i32x4{lo.x, lo.y, hi.x, hi.y};
+                }
+        };
+        auto qk = [&]() {
+            for (int dc = 0; dc < 4; ++dc)
+                for (int mt = 0; mt < 2; ++mt)
+                    for (int kt = 0; kt < 4; ++kt)
+                        s[mt][kt] = mfma<kElem>(kf[kt][dc], qf[mt][dc],
+                                                dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mt][kt]);
+        };
+        auto pv = [&]() {
+            for (int c = 0; c < 2; ++c)
+                for (int mt = 0; mt < 2; ++mt)
+                    for (int dt = 0; dt < 8; ++dt)
+                        o[mt][dt >> 2][dt & 3] = mfma<kElem>(vf[dt][c], pf[mt][c], o[mt][dt >> 2][dt & 3]);
+        };
+        // keys past the end, and (causal) keys above the diagonal, score -inf
+        auto mask = [&](int j) {
+            const int k0 = j * kKeys;
+            bool need = k0 + kKeys > p.Sk;
+            if constexpr (kCausal) need = need || (k0 + kKeys - 1 > wrow + p.off);
+            if (need) {
+                for (int mt = 0; mt < 2; ++mt) {
+                    const int lim = kCausal ? min(p.Sk, wrow + 16 * mt + r16 + p.off + 1) : p.Sk;
+                    const int t = lim - k0 - 4 * g;               // first masked 16kt + e of this lane
+                    for (int kt = 0; kt < 4; ++kt)
+                        for (int e = 0; e < 4; ++e)
+                            if (16 * kt + e >= t) s[mt][kt][e] = -INFINITY;
+                }
+            }
+        };
+        // first half: row maxima of S, the new running max and alpha
+        auto softmax_max = [&]() {
+            for (int mt = 0; mt < 2; ++mt) {
+                float mx = s[mt][0][0];
+                for (int kt = 0; kt < 4; ++kt)
+                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[mt][kt][e]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mn = fmaxf(m[mt], mx * p.c);
+                const float ref = mn == -INFINITY ? 0.f : mn;
+                alpha[mt] = __builtin_amdgcn_exp2f(m[mt] - ref);
+                m[mt] = mn;
+            }
+        };
+        // second half: P = 2^(c S - m) in the operand type, running row sums
+        auto softmax_exp = [&]() {
+            for (int mt = 0; mt < 2; ++mt) {
+                const float ref = m[mt] == -INFINITY ? 0.f : m[mt];
+                float sum = 0.f;
+                f32x4 pr[4];
+                for (int kt = 0; kt < 4; ++kt)
+                    for (int e = 0; e < 4; ++e) {
+                        pr[kt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][kt][e], p.c, -ref));
+                        sum += pr[kt][e];
+                    }
+                l[mt] = l[mt] * alpha[mt] + sum;
+                for (int c = 0; c < 2; ++c) {
+                    const i32x2 lo = pack4<kElem>(pr[2 * c]), hi = pack4<kElem>(pr[2 * c + 1]);
+                    pf[mt][c] = i32x4{lo.x, lo.y, hi.x, hi.y};
+                }
+            }
+        };
+        auto rescale = [&]() {
+            for (int mt = 0; mt < 2; ++mt)
+                for (int h = 0; h < 2; ++h)
+                    for (int t = 0; t < 4; ++t) o[mt][h][t] *= alpha[mt];
+        };
+
+        // ---- prologue (both groups in step): blocks 0-2 in flight, S(0), P(0)
+        for (int j = 0; j < 3; ++j) copy_block(j);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<8>();                    // block 0 (this wave's pieces)
+        rendezvous();                       // ... and everyone's
+        read_k(0);
+        wait_lgkmcnt<0>();
+        qk();
+        mask(0);
+        softmax_max();
+        softmax_exp();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<4>();                    // block 1
+        rendezvous();
+        read_k(1);
+        wait_lgkmcnt<0>();
+        if (groupB) rendezvous();           // group B falls one stage behind
+
+#pragma unroll 1
+        for (int i = 0; i + 1 < nblk; ++i) {
+            // stage 0: S(i+1)
+            qk();
+            rendezvous();
+            // stage 1: rescale O, V(i) fragments, row max of S(i+1), copies of block i+3
+            rescale();
+            read_v(i);
+            copy_block(i + 3);
+            mask(i + 1);
+            softmax_max();
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<4>();                // block i+2
+            wait_lgkmcnt<0>();
+            rendezvous();
+            // stage 2: O += P(i) V(i)
+            pv();
+            rendezvous();
+            // stage 3: P(i+1), row sums, K(i+2) fragments (read after S is
+            // consumed, so S and the K fragments are not live together)
+            softmax_exp();
+            __builtin_amdgcn_sched_barrier(0);
+            read_k(i + 2);
+            wait_lgkmcnt<0>();
+            rendezvous();
+        }
+        // ---- drain: the last block's alpha and P V
+        rescale();
+        read_v(nblk - 1);
+        wait_lgkmcnt<0>();
+        rendezvous();
+        pv();
+        if (!groupB) rendezvous();          // group A closes the offset
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<0>();                    // zero-window copies past the end
+    }
+
+    // ---- O / l and lse
+    GemmParams out{};
+    out.C = p.O + qbase;
+    out.ldc = kHeadDim;
+    out.N = kHeadDim;
+    out.M = p.Sq;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        float lt = l[mt];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        for (int h = 0; h < 2; ++h)
+            for (int t = 0; t < 4; ++t) o[mt][h][t] *= inv;
+        const int row = wrow + 16 * mt + r16;
+        if (row >= p.Sq) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) store_strip<kElem == kElemBF16, false>(out, o[mt][h], row, 64 * h, lane);
+        if (p.lse && g == 0)
+            p.lse[static_cast<int64_t>(bh) * p.Sq + row] =
+                lt > 0.f ? (m[mt] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+int attn_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_EHIP; }
+
+}  // namespace
+}  // namespace mcs
+
+extern "C" int attention_fwd(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                             int64_t head_dim, const void *Q, const void *K, const void *V, void *O,
+                             float *lse, float scale, int causal, hipStream_t stream) {
+    using namespace mcs;
+    auto aligned16 = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; };
+    if (dtype != GEMM_DTYPE_F16 && dtype != GEMM_DTYPE_BF16) return GEMM_EINVAL;
+    if (causal != 0 && causal != 1) return GEMM_EINVAL;
+    if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim < 0) return GEMM_EINVAL;
+    if (!(scale > 0.f) || !std::isfinite(scale)) return GEMM_EINVAL;
+    if (head_dim != kHeadDim) return GEMM_EUNSUPPORTED;
+    if (batch == 0 || heads == 0 || seq_q == 0) return GEMM_OK;
+    if (!Q || !O || !aligned16(Q) || !aligned16(O)) return GEMM_EINVAL;
+    if (seq_k > 0 && (!K || !V || !aligned16(K) || !aligned16(V))) return GEMM_EINVAL;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return GEMM_EINVAL;
+    // row indices and per-head element offsets stay below 2^31
+    if (seq_q >= (int64_t(1) << 23) || seq_k >= (int64_t(1) << 23)) return GEMM_EUNSUPPORTED;
+    const int64_t groups = batch * heads;
+    const int64_t nq = (seq_q + kQRows - 1) / kQRows;
+    if (groups > 0x7FFFFFFF || nq * groups > 0x7FFFFFFF) return GEMM_EUNSUPPORTED;
+
+    AttnParams prm{};
+    prm.Q = static_cast<const char *>(Q);
+    prm.K = static_cast<const char *>(K);
+    prm.V = static_cast<const char *>(V);
+    prm.O = static_cast<char *>(O);
+    prm.lse = lse;
+    prm.Sq = static_cast<int>(seq_q);
+    prm.Sk = static_cast<int>(seq_k);
+    prm.nq = static_cast<int>(nq);
+    prm.groups = static_cast<int>(groups);
+    prm.c = scale * 1.4426950408889634f;
+    prm.off = static_cast<int>(seq_k - seq_q);
+    const void *fn = nullptr;
+    if (dtype == GEMM_DTYPE_F16)
+        fn = causal ? reinterpret_cast<const void *>(&attention_fwd_kernel<kElemF16, true>)
+                    : reinterpret_cast<const void *>(&attention_fwd_kernel<kElemF16, false>);
+    else
+        fn = causal ? reinterpret_cast<const void *>(&attention_fwd_kernel<kElemBF16, true>)
+                    : reinterpret_cast<const void *>(&attention_fwd_kernel<kElemBF16, false>);
+    void *args[] = {&prm};
+    return attn_status(hipLaunchKernel(fn, dim3(static_cast<unsigned>(nq * groups)), dim3(kAttnWaves * 64),
+                                       args, 0, stream));
+}

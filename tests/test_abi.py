@@ -20,7 +20,7 @@ def test_header_declares_the_entry_points():
     names = mcs.header_functions()
     assert set(names) == {"gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_ex", "gemm_ex_splitk",
                           "gemm_splitk_workspace_bytes", "gemm_auto_schedule", "gemm_splitk_suggest",
-                          "gemm_kernel_info",
+                          "gemm_kernel_info", "attention_fwd",
                           "gemm_status_string"}
 
 
@@ -171,3 +171,36 @@ def test_splitk_suggest(lib):
     assert mcs.gemm_splitk_suggest(f16, 256, 256, 65536) == 16        # 4 tiles, 1024 K-steps
     assert mcs.gemm_splitk_suggest(f16, 256, 256, 65536, 32) == 8
     assert mcs.gemm_splitk_suggest(f16, 512, 4096, 8192, 128) == 1
+
+
+def test_attention_argument_errors(lib):
+    """Every refusal happens before any device call (none of these launch)."""
+    f16, bf16 = mcs.GEMM_DTYPE_F16, mcs.GEMM_DTYPE_BF16
+    good = dict(dtype=f16, batch=1, heads=2, seq_q=64, seq_k=64, head_dim=128, Q=P, K=P, V=P, O=P, lse=P,
+                scale=0.125, causal=0, stream=0)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return mcs.attention_fwd(a["dtype"], a["batch"], a["heads"], a["seq_q"], a["seq_k"], a["head_dim"],
+                                 a["Q"], a["K"], a["V"], a["O"], a["lse"], a["scale"], a["causal"], a["stream"])
+
+    assert call(dtype=mcs.GEMM_DTYPE_FP8_E4M3) == mcs.GEMM_EINVAL
+    assert call(dtype=7) == mcs.GEMM_EINVAL
+    assert call(causal=2) == mcs.GEMM_EINVAL
+    assert call(seq_q=-1) == mcs.GEMM_EINVAL
+    assert call(batch=-2) == mcs.GEMM_EINVAL
+    assert call(scale=0.0) == mcs.GEMM_EINVAL
+    assert call(scale=-1.0) == mcs.GEMM_EINVAL
+    assert call(scale=float("nan")) == mcs.GEMM_EINVAL
+    assert call(scale=float("inf")) == mcs.GEMM_EINVAL
+    assert call(head_dim=64) == mcs.GEMM_EUNSUPPORTED
+    assert call(Q=0) == mcs.GEMM_EINVAL
+    assert call(O=P + 8) == mcs.GEMM_EINVAL                          # misaligned
+    assert call(K=P + 2) == mcs.GEMM_EINVAL
+    assert call(V=0) == mcs.GEMM_EINVAL
+    assert call(lse=P + 2) == mcs.GEMM_EINVAL
+    assert call(seq_q=1 << 23) == mcs.GEMM_EUNSUPPORTED
+    # empty problems enqueue nothing
+    assert call(batch=0, Q=0, K=0, V=0, O=0) == mcs.GEMM_OK
+    assert call(seq_q=0, Q=0, K=0, V=0, O=0) == mcs.GEMM_OK
+    assert call(dtype=bf16, heads=0) == mcs.GEMM_OK

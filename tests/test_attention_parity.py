@@ -1,0 +1,141 @@
+"""GPU parity of the attention forward pass: attention_fwd (through the C ABI)
+against the float64 oracle, every element of O and every lse at small and
+ragged sizes, sampled rows at the full 4 x 32 x 4096 x 128 size.
+
+Bar (oracle.attention.within_tolerance): |O - Oref| <= (u + e) A + u |Oref|
+with A = sum_j P_ij |V_jd|, u the operand type's rounding unit (the kernel
+rounds P to it) and e the FP32 score / sum error bound; lse within its FP32
+bound; rows with no visible key give O = 0 and lse = -inf exactly."""
+import math
+
+import numpy as np
+import pytest
+
+import matrix_core_scheduling_amd as mcs
+import oracle
+import oracle.attention as at
+import seeded_inputs as si
+from tests.gpu_util import TORCH_DT, _torch, upload
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": mcs.GEMM_DTYPE_F16, "bf16": mcs.GEMM_DTYPE_BF16}
+
+
+def qkv(elem, B, H, Sq, Sk, D, seed, dist="normal"):
+    q = si.matrix_bits(elem, dist, B * H * Sq, D, seed=seed, stream=0).reshape(B, H, Sq, D)
+    k = si.matrix_bits(elem, dist, B * H * max(Sk, 1), D, seed=seed, stream=1).reshape(B, H, max(Sk, 1), D)
+    v = si.matrix_bits(elem, dist, B * H * max(Sk, 1), D, seed=seed, stream=2).reshape(B, H, max(Sk, 1), D)
+    return q, k[:, :, :Sk].copy(), v[:, :, :Sk].copy()
+
+
+def run_attention(elem, q, k, v, scale, causal, o_fill=-5.0):
+    """O (float64), lse (float64) and raw O bits from attention_fwd."""
+    torch = _torch()
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    print(f"[gpu] attention elem={elem} B={B} H={H} Sq={Sq} Sk={Sk} D={D} causal={causal}", flush=True)
+    Q, _ = upload(q.reshape(-1, D), elem)
+    K, _ = upload(k.reshape(-1, D) if Sk else np.zeros((1, D), np.uint16), elem)
+    V, _ = upload(v.reshape(-1, D) if Sk else np.zeros((1, D), np.uint16), elem)
+    O = torch.full((B * H * Sq * D,), o_fill, dtype=TORCH_DT[elem], device="cuda")
+    L = torch.full((B * H * Sq,), 7.0, dtype=torch.float32, device="cuda")
+    st = mcs.attention_fwd(DT[elem], B, H, Sq, Sk, D, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                           L.data_ptr(), scale, int(causal), torch.cuda.current_stream().cuda_stream)
+    assert st == mcs.GEMM_OK, mcs.gemm_status_string(st)
+    torch.cuda.synchronize()
+    bits = O.cpu().view(torch.int16).numpy().view(np.uint16).reshape(B, H, Sq, D)
+    return oracle.decode(bits, elem), L.cpu().double().numpy().reshape(B, H, Sq), bits
+
+
+def check(elem, q, k, v, scale, causal, rows=None, what=""):
+    o, lse, _ = run_attention(elem, q, k, v, scale, causal)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    oref, lref, a, sabs = at.attention(q, k, v, elem, scale, causal, rows=rows)
+    if rows is not None:
+        o, lse = o[:, :, rows], lse[:, :, rows]
+    ok = at.within_tolerance(o, oref, a, sabs, D, Sk, elem)
+    bad = np.argwhere(~ok)
+    assert ok.all(), (f"{what}: {bad.shape[0]} of {ok.size} outside; first {bad[:3].tolist()} "
+                      f"got {o[tuple(bad[0])]} want {oref[tuple(bad[0])]}")
+    okl = at.lse_within_tolerance(lse, lref, sabs, D, Sk)
+    bad = np.argwhere(~okl)
+    assert okl.all(), f"{what}: lse {bad[:3].tolist()} got {lse[tuple(bad[0])]} want {lref[tuple(bad[0])]}"
+    return o, lse
+
+
+SHAPES = [  # (B, H, Sq, Sk)
+    (1, 1, 1, 1), (1, 2, 17, 33), (1, 1, 64, 64), (2, 3, 300, 200), (1, 2, 256, 256), (1, 1, 512, 64),
+    (1, 2, 100, 700), (1, 1, 257, 513), (2, 1, 96, 1000),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes_every_element(shape, elem, causal):
+    B, H, Sq, Sk = shape
+    q, k, v = qkv(elem, B, H, Sq, Sk, 128, seed=Sq * 7 + Sk)
+    check(elem, q, k, v, 1 / math.sqrt(128), causal, what=f"{shape} {elem} causal={causal}")
+
+
+def test_uniform_values_and_other_scales():
+    for dist, scale in (("uniform", 0.3), ("normal", 0.02), ("normal", 0.25)):
+        q, k, v = qkv("f16", 1, 2, 192, 320, 128, seed=3, dist=dist)
+        check("f16", q, k, v, scale, False, what=f"{dist} scale={scale}")
+
+
+def test_rows_without_keys_and_no_keys():
+    """Causal with more queries than keys: the first Sq - Sk rows see no key
+    (O = 0, lse = -inf); Sk = 0: every row."""
+    q, k, v = qkv("f16", 1, 2, 300, 40, 128, seed=8)
+    o, lse = check("f16", q, k, v, 0.1, True, what="Sq > Sk causal")
+    assert np.array_equal(o[:, :, :260], np.zeros_like(o[:, :, :260]))
+    assert np.isneginf(lse[:, :, :260]).all() and np.isfinite(lse[:, :, 260:]).all()
+    q, k, v = qkv("bf16", 2, 1, 70, 0, 128, seed=9)
+    o, lse, _ = run_attention("bf16", q, k, v, 0.1, False)
+    assert np.array_equal(o, np.zeros_like(o)) and np.isneginf(lse).all()
+
+
+def test_identical_keys_give_the_mean_of_v():
+    """A closed form on the GPU: equal keys weigh every visible V row alike."""
+    q, k, v = qkv("f16", 1, 1, 128, 192, 128, seed=10)
+    k[:] = k[:, :, :1]
+    o, _ = check("f16", q, k, v, 0.125, False, what="identical keys")
+    mean = oracle.decode(v, "f16").mean(axis=2)
+    assert np.allclose(o[0, 0], np.broadcast_to(mean[0, 0], o[0, 0].shape), rtol=2 ** -9, atol=2e-3)
+
+
+def test_deterministic():
+    q, k, v = qkv("bf16", 1, 4, 512, 512, 128, seed=12)
+    b1 = run_attention("bf16", q, k, v, 0.09, True)[2]
+    b2 = run_attention("bf16", q, k, v, 0.09, True)[2]
+    assert np.array_equal(b1, b2)
+
+
+def test_torch_binding_matches_abi():
+    torch = _torch()
+    q, k, v = qkv("f16", 2, 2, 200, 330, 128, seed=14)
+    o_abi, lse_abi, _ = run_attention("f16", q, k, v, 1 / math.sqrt(128), True)
+    t = [upload(x.reshape(-1, 128), "f16")[0].view(x.shape) for x in (q, k, v)]
+    o, lse = mcs.attention(*t, causal=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(oracle.decode(o.cpu().view(torch.int16).numpy().view(np.uint16), "f16"), o_abi)
+    assert np.array_equal(lse.cpu().double().numpy(), lse_abi)
+
+
+@pytest.mark.parametrize("name", [n for n in si.ATTN_WORKLOADS])
+def test_attention_workload(name):
+    """The workloads in the configuration bench.py runs: every element for the
+    small one, 24 sampled query rows (block edges included) of every head for
+    the full-size ones."""
+    w = si.ATTN_WORKLOADS[name]
+    q, k, v = w.operands(0)
+    if w.B * w.H * w.Sq * w.Sk <= 2 ** 22:
+        check(w.dtype, q, k, v, w.scale, w.causal, what=name)
+        return
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([rng.integers(0, w.Sq, 16), [0, 63, 64, 255, 256, w.Sq - 257, w.Sq - 1]]))
+    o, lse = check(w.dtype, q, k, v, w.scale, w.causal, rows=rows, what=name)
+    assert np.isfinite(o).all()
