@@ -17,6 +17,11 @@ events on the stream they are enqueued on.  Throughput = 2MNK / time.
 The CPU baseline runs the oracle (a plain binary64 triple loop) on a bounded
 block of output rows of the same workload, on the host's cores, and the GPU
 result on those rows is checked against it.
+
+The attention workloads (--workload attn_...) time attention_fwd over the
+whole batch instead: one launch per step, throughput = 4 B H (allowed query
+-key pairs) D / time; the CPU baseline runs the float64 attention oracle on a
+bounded sample of query rows.
 """
 from __future__ import annotations
 
@@ -97,12 +102,136 @@ def copy_calibration(mib: int) -> int:
     return 0
 
 
+def bench_attention(a, w) -> int:
+    """One attention_fwd launch per step over the whole (B, H) batch."""
+    import numpy as np
+    import torch
+
+    import matrix_core_scheduling_amd as mcs
+
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    dev = torch.device("cuda:0")
+    set_bytes = 2 * w.B * w.H * w.D * (w.Sq + 2 * w.Sk)
+    nrot = max(1, math.ceil(2 * MALL_BYTES / set_bytes))
+    print(f"[bench] workload {w.name}: generating {nrot} input sets", file=sys.stderr, flush=True)
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.reshape(-1).view(np.int16)).to(dev).view(tdt)
+
+    host0, sets = None, []
+    for r in range(nrot):
+        q, k, v = w.operands(r)
+        if r == 0:
+            host0 = (q, k, v)
+        sets.append(tuple(to_dev(x) for x in (q, k, v)))
+    outs = [torch.empty(w.B * w.H * w.Sq * w.D, dtype=tdt, device=dev) for _ in range(nrot)]
+    lses = [torch.empty(w.B * w.H * w.Sq, dtype=torch.float32, device=dev) for _ in range(nrot)]
+    dtype = {"f16": mcs.GEMM_DTYPE_F16, "bf16": mcs.GEMM_DTYPE_BF16}[w.dtype]
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def launch(i):
+        Q, K, V = sets[i % nrot]
+        st = mcs.attention_fwd(dtype, w.B, w.H, w.Sq, w.Sk, w.D, Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                               outs[i % nrot].data_ptr(), lses[i % nrot].data_ptr(), w.scale, int(w.causal), sh)
+        if st != mcs.GEMM_OK:
+            raise mcs.GemmError(st, "attention_fwd")
+
+    print(f"[bench] warm-up {a.warmup}", file=sys.stderr, flush=True)
+    for i in range(a.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(a.steps):
+        launch(a.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / a.steps
+    tflops = w.flops / (ms_step * 1e-3) / 1e12
+    launch(0)
+    torch.cuda.synchronize()
+
+    cpu = check = None
+    if not a.no_cpu_baseline:
+        import oracle.attention as at
+
+        q, k, v = host0
+        threads = host_threads()
+        os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+        # the oracle on query rows of the first heads: probe, then a ~cpu_seconds sample
+        t = time.perf_counter()
+        at.attention(q[:1, :1], k[:1, :1], v[:1, :1], w.dtype, w.scale, w.causal, rows=np.arange(64))
+        per_head = max(time.perf_counter() - t, 1e-3)
+        heads = int(max(1, min(w.B * w.H, a.cpu_seconds / per_head)))
+        rows = np.arange(64)
+        rng = np.random.default_rng(w.seed)
+        rows = np.unique(np.concatenate([rows, rng.integers(0, w.Sq, 64)]))
+        hb = [(h // w.H, h % w.H) for h in range(heads)]
+        print(f"[bench] CPU oracle on {rows.size} query rows x {heads} heads", file=sys.stderr, flush=True)
+        t = time.perf_counter()
+        refs = [at.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], w.dtype, w.scale,
+                             w.causal, rows=rows) for b, h in hb]
+        cpu_s = time.perf_counter() - t
+        mask = at.allowed_keys(w.Sq, w.Sk, w.causal)[rows]
+        flops = 4.0 * heads * mask.sum() * w.D
+        cpu = {"value": round(flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"{rows.size} query rows (rows 0-63 and 64 seeded random ones) of each of the first "
+                         f"{heads} (batch, head) pairs of the same workload, {cpu_s:.1f} s on {cpu_model()}"}
+        import oracle
+
+        og = outs[0].view(w.B, w.H, w.Sq, w.D).cpu().view(torch.int16).numpy().view(np.uint16)
+        og = oracle.decode(og, w.dtype)
+        lg = lses[0].view(w.B, w.H, w.Sq).cpu().double().numpy()
+        bad = 0
+        for (b, h), (oref, lref, aa, sabs) in zip(hb, refs):
+            bad += int((~at.within_tolerance(og[b:b + 1, h:h + 1, rows], oref, aa, sabs, w.D, w.Sk,
+                                             w.dtype)).sum())
+            bad += int((~at.lse_within_tolerance(lg[b:b + 1, h:h + 1, rows], lref, sabs, w.D, w.Sk)).sum())
+        n = heads * rows.size * (w.D + 1)
+        check = {"rows": heads * rows.size, "elements": n, "outside_tolerance": bad, "pass": bad == 0}
+
+    traffic = traffic_for(w.name, "attention")
+    peak = PEAK_TFLOPS[w.dtype]
+    name = {"f16": "FP16", "bf16": "BF16"}[w.dtype]
+    line = {
+        "metric": f"{name} attention forward TFLOP/s at B={w.B},H={w.H},Sq={w.Sq},Sk={w.Sk},D={w.D}"
+                  f"{',causal' if w.causal else ''} and % of MI355X MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "D": w.D,
+                   "causal": w.causal, "operands": w.dtype, "accumulate": "f32", "values": w.dist,
+                   "seed": w.seed, "rotating_sets": nrot, "kernel": "attention"},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "check": check,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if (check is None or check["pass"]) else 3
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS))
+    ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS) + sorted(si.ATTN_WORKLOADS))
     ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "interleaved", "tile128", "generic"])
     ap.add_argument("--splits", default="auto",
                     help="K-slices (gemm_ex_splitk) or 'auto' (gemm_splitk_suggest; 1 for the default shape)")
@@ -132,6 +261,8 @@ def main(argv=None) -> int:
         from matrix_core_scheduling_amd import build
         build.build()
     mcs.load()
+    if a.workload in si.ATTN_WORKLOADS:
+        return bench_attention(a, si.ATTN_WORKLOADS[a.workload])
 
     w = si.WORKLOADS[a.workload]
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.dtype]

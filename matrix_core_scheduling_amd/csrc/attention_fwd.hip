@@ -88,6 +88,18 @@ __device__ __forceinline__ void attn_coords(const AttnParams &p, int wg, int &bh
     qb = v - bh * p.nq;
 }
 
+// Combine the values of lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes
+// that hold one row of an MFMA accumulator tile) with VALU lane swaps: each
+// swap exchanges 16-lane (32-lane) halves between two copies of x, and the
+// pairwise result is the same in every lane of a pair.
+template <typename F>
+__device__ __forceinline__ float row_reduce(float x, F op) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int kElem>
 __device__ __forceinline__ i32x2 pack4(f32x4 v) {
     if constexpr (kElem == kElemBF16)
@@ -223,8 +235,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                 float mx = s[mt][0][0];
                 for (int kt = 0; kt < 4; ++kt)
                     for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[mt][kt][e]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = row_reduce(mx, [](float a, float b) { return fmaxf(a, b); });
                 const float mn = fmaxf(m[mt], mx * p.c);
                 const float ref = mn == -INFINITY ? 0.f : mn;
                 alpha[mt] = __builtin_amdgcn_exp2f(m[mt] - ref);
@@ -236,20 +247,24 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             for (int mt = 0; mt < 2; ++mt) {
                 const float ref = m[mt] == -INFINITY ? 0.f : m[mt];
                 float sum = 0.f;
-                f32x4 pr[4];
-                for (int kt = 0; kt < 4; ++kt)
-                    for (int e = 0; e < 4; ++e) {
-                        pr[kt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][kt][e], p.c, -ref));
-                        sum += pr[kt][e];
-                    }
-                l[mt] = l[mt] * alpha[mt] + sum;
                 for (int c = 0; c < 2; ++c) {
-                    const i32x2 lo = pack4<kElem>(pr[2 * c]), hi = pack4<kElem>(pr[2 * c + 1]);
-                    pf[mt][c] = i32x4{lo.x, lo.y, hi.x, hi.y};
+                    i32x2 h[2];
+                    for (int u = 0; u < 2; ++u) {
+                        f32x4 pr;
+                        for (int e = 0; e < 4; ++e) {
+                            pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][2 * c + u][e], p.c, -ref));
+                            sum += pr[e];
+                        }
+                        h[u] = pack4<kElem>(pr);
+                    }
+                    pf[mt][c] = i32x4{h[0].x, h[0].y, h[1].x, h[1].y};
                 }
+                l[mt] = l[mt] * alpha[mt] + sum;
             }
         };
+        // O *= alpha, skipped when no row of the wave changed its max
         auto rescale = [&]() {
+            if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f) == 0) return;
             for (int mt = 0; mt < 2; ++mt)
                 for (int h = 0; h < 2; ++h)
                     for (int t = 0; t < 4; ++t) o[mt][h][t] *= alpha[mt];
@@ -318,9 +333,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
     out.M = p.Sq;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        float lt = l[mt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = row_reduce(l[mt], [](float a, float b) { return a + b; });
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         for (int h = 0; h < 2; ++h)
             for (int t = 0; t < 4; ++t) o[mt][h][t] *= inv;

@@ -33,6 +33,7 @@ KERNEL_SOURCES = {
     "pipelined": ("gemm_pipelined.hip", "device.h", "internal.h"),
     "interleaved": ("gemm_interleaved.hip", "device.h", "internal.h"),
     "tile128": ("gemm_tile128.hip", "device.h", "internal.h"),
+    "attention": ("attention_fwd.hip", "device.h", "internal.h"),
 }
 
 
@@ -119,7 +120,7 @@ def traffic_key(workload: str, schedule: str = "pipelined") -> str:
 
 def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, schedule="pipelined",
             copy_kernel="copyBuffer") -> dict:
-    kernel = "gemm_" + schedule
+    kernel = "attention_fwd" if schedule == "attention" else "gemm_" + schedule
     copy_bytes = copy_mib * 2 ** 20
     cf = counters([copy_fetch_dir], copy_kernel)
     cw = counters([copy_write_dir], copy_kernel)

@@ -81,7 +81,9 @@ def test_shapes_every_element(shape, elem, causal):
 
 
 def test_uniform_values_and_other_scales():
-    for dist, scale in (("uniform", 0.3), ("normal", 0.02), ("normal", 0.25)):
+    # scale 4: scores span hundreds in log2 units, so a running max that is not
+    # the true row max overflows the exponentials
+    for dist, scale in (("uniform", 0.3), ("normal", 0.02), ("normal", 0.25), ("normal", 4.0)):
         q, k, v = qkv("f16", 1, 2, 192, 320, 128, seed=3, dist=dist)
         check("f16", q, k, v, scale, False, what=f"{dist} scale={scale}")
 
