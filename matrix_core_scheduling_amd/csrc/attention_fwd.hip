@@ -65,6 +65,7 @@ constexpr int kAttnWaves = 8;
 constexpr uint32_t kKVTile = kKeys * kRowBytes;            // 16 KiB
 constexpr uint32_t kKVSlot = 2 * kKVTile;                  // K | V
 constexpr int kKVSlots = 4;
+constexpr float kLazy = 8.f;                               // shift slack of the online softmax
 
 struct AttnParams {
     const char *Q, *K, *V;
@@ -229,21 +230,36 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                 }
             }
         };
-        // first half: row maxima of S, the new running max and alpha
+        // The two softmax halves are pure arithmetic, which the compiler would
+        // otherwise move across the stage walls; each half starts from values
+        // passed through an empty asm, so its work stays in its stage.
+        auto pin_s = [&]() {
+            for (int mt = 0; mt < 2; ++mt)
+                for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[mt][kt]));
+        };
+        // first half: row maxima of S and the running shift m.  m moves only
+        // when a row's maximum exceeds it by more than kLazy (log2 units): the
+        // exponentials then stay below 2^kLazy, and O and l are rescaled by
+        // alpha = 2^(m_old - m_new) only in those rows (lazy rescaling).
         auto softmax_max = [&]() {
+            pin_s();
             for (int mt = 0; mt < 2; ++mt) {
                 float mx = s[mt][0][0];
                 for (int kt = 0; kt < 4; ++kt)
                     for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[mt][kt][e]);
-                mx = row_reduce(mx, [](float a, float b) { return fmaxf(a, b); });
-                const float mn = fmaxf(m[mt], mx * p.c);
-                const float ref = mn == -INFINITY ? 0.f : mn;
-                alpha[mt] = __builtin_amdgcn_exp2f(m[mt] - ref);
-                m[mt] = mn;
+                mx = row_reduce(mx, [](float a, float b) { return fmaxf(a, b); }) * p.c;
+                if (mx > m[mt] + kLazy) {
+                    alpha[mt] = __builtin_amdgcn_exp2f(m[mt] - mx);
+                    m[mt] = mx;
+                } else {
+                    alpha[mt] = 1.f;
+                }
+                asm volatile("" : "+v"(m[mt]), "+v"(alpha[mt]));
             }
         };
         // second half: P = 2^(c S - m) in the operand type, running row sums
         auto softmax_exp = [&]() {
+            pin_s();
             for (int mt = 0; mt < 2; ++mt) {
                 const float ref = m[mt] == -INFINITY ? 0.f : m[mt];
                 float sum = 0.f;
@@ -294,9 +310,9 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             qk();
             rendezvous();
             // stage 1: rescale O, V(i) fragments, row max of S(i+1), copies of block i+3
-            rescale();
             read_v(i);
             copy_block(i + 3);
+            rescale();                      // by alpha(i), before softmax_max sets alpha(i+1)
             mask(i + 1);
             softmax_max();
             __builtin_amdgcn_sched_barrier(0);
