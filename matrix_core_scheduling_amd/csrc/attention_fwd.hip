@@ -188,19 +188,27 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         i32x4 pf[2][2];     // P [mt][32-key chunk], operand type
         f32x4 s[2][4];      // S [mt][16-key tile]
 
+        // One address add per lane base (kept opaque to the compiler); the
+        // rest of every read's address is its immediate offset.
         auto read_k = [&](int j) {
             const uint32_t b = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot;
-            for (int kt = 0; kt < 4; ++kt)
-                for (int dc = 0; dc < 4; ++dc) kf[kt][dc] = lds_read128(b + kt * 16 * kRowBytes + kofs[dc]);
+            for (int dc = 0; dc < 4; ++dc) {
+                uint32_t a = b + kofs[dc];
+                asm volatile("" : "+v"(a));
+                for (int kt = 0; kt < 4; ++kt) kf[kt][dc] = lds_read128(a + kt * 16 * kRowBytes);
+            }
         };
         auto read_v = [&](int j) {
             const uint32_t b = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + kKVTile;
-            for (int c = 0; c < 2; ++c)
-                for (int dt = 0; dt < 8; ++dt) {
-                    const i32x2 lo = lds_read64_tr(b + (32 * c) * kRowBytes + vofs[dt]);
-                    const i32x2 hi = lds_read64_tr(b + (32 * c + 16) * kRowBytes + vofs[dt]);
+            for (int dt = 0; dt < 8; ++dt) {
+                uint32_t a = b + vofs[dt];
+                asm volatile("" : "+v"(a));
+                for (int c = 0; c < 2; ++c) {
+                    const i32x2 lo = lds_read64_tr(a + (32 * c) * kRowBytes);
+                    const i32x2 hi = lds_read64_tr(a + (32 * c + 16) * kRowBytes);
                     vf[dt][c] = i32x4{lo.x, lo.y, hi.x, hi.y};
                 }
+            }
         };
         auto qk = [&]() {
             for (int dc = 0; dc < 4; ++dc)
@@ -304,8 +312,8 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         wait_lgkmcnt<0>();
         if (groupB) rendezvous();           // group B falls one stage behind
 
-#pragma unroll 1
-        for (int i = 0; i + 1 < nblk; ++i) {
+        // one trip; kMasked: block i+1 may hold keys some row must not see
+        auto trip = [&](int i, auto masked) {
             // stage 0: S(i+1)
             qk();
             rendezvous();
@@ -313,7 +321,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             read_v(i);
             copy_block(i + 3);
             rescale();                      // by alpha(i), before softmax_max sets alpha(i+1)
-            mask(i + 1);
+            if constexpr (decltype(masked)::value) mask(i + 1);
             softmax_max();
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<4>();                // block i+2
@@ -329,7 +337,16 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             read_k(i + 2);
             wait_lgkmcnt<0>();
             rendezvous();
-        }
+        };
+        // leading blocks no row of the workgroup needs masked: every key
+        // exists and (causal) every key is visible to the first row
+        int nplain = p.Sk / kKeys;
+        if constexpr (kCausal) nplain = min(nplain, max(0, (q0 + p.off + 1) / kKeys));
+        int i = 0;
+#pragma unroll 1
+        for (; i + 1 < min(nplain, nblk); ++i) trip(i, std::false_type{});
+#pragma unroll 1
+        for (; i + 1 < nblk; ++i) trip(i, std::true_type{});
         // ---- drain: the last block's alpha and P V
         rescale();
         read_v(nblk - 1);
