@@ -60,6 +60,17 @@ int attention_fwd(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int64_
                   int64_t head_dim, const void *Q, const void *K, const void *V, void *O,
                   float *lse, float scale, int causal, hipStream_t stream);
 
+/*
+ * attention_fwd_ex -- the same with the stage schedule chosen: AUTO or
+ * GEMM_SCHED_PIPELINED (the two wave groups one stage apart, what
+ * attention_fwd runs) or GEMM_SCHED_IN_PHASE (the same stages with the
+ * groups in step: the ablation of the offset).  Other schedules:
+ * GEMM_EINVAL.  Results are bitwise identical across the two.
+ */
+int attention_fwd_ex(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                     int64_t head_dim, const void *Q, const void *K, const void *V, void *O,
+                     float *lse, float scale, int causal, int schedule, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,7 +4,8 @@ and the attention forward pass built in the same stage abstraction.
 The functions ``gemm_f16``, ``gemm_bf16``, ``gemm_fp8``, ``gemm_ex``,
 ``gemm_ex_splitk``, ``gemm_splitk_workspace_bytes``, ``gemm_auto_schedule``,
 ``gemm_splitk_suggest``,
-``gemm_kernel_info``, ``gemm_status_string`` and ``attention_fwd`` mirror the
+``gemm_kernel_info``, ``gemm_status_string``, ``attention_fwd`` and
+``attention_fwd_ex`` mirror the
 C ABI in ``include/mcs_gemm.h`` and ``include/mcs_attention.h`` one to one
 (sizes, raw device pointers as integers, a raw ``hipStream_t``).  ``gemm``
 marshals torch tensors onto them: torch provides device memory and the
@@ -76,6 +77,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.gemm_kernel_info.restype = ci
     lib.attention_fwd.argtypes = [ci, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, ctypes.c_float, ci, vp]
     lib.attention_fwd.restype = ci
+    lib.attention_fwd_ex.argtypes = [ci, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, ctypes.c_float, ci, ci, vp]
+    lib.attention_fwd_ex.restype = ci
     lib.gemm_status_string.argtypes = [ci]
     lib.gemm_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -208,6 +211,12 @@ def gemm(A, B, trans_b: bool = False, out=None, out_dtype=None,
     if st != GEMM_OK:
         raise GemmError(st, "gemm")
     return out
+
+
+def attention_fwd_ex(dtype, batch, heads, seq_q, seq_k, head_dim, Q, K, V, O, lse, scale, causal, schedule,
+                     stream) -> int:
+    return load().attention_fwd_ex(dtype, batch, heads, seq_q, seq_k, head_dim, Q, K, V, O, lse, scale,
+                                   causal, schedule, stream)
 
 
 def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,

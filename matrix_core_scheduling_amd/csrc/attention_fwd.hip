@@ -109,7 +109,9 @@ __device__ __forceinline__ i32x2 pack4(f32x4 v) {
         return __builtin_bit_cast(i32x2, __builtin_convertvector(v, f16x4));
 }
 
-template <int kElem, bool kCausal>
+// kOffset = false keeps the two groups in phase (no entry / exit barrier):
+// the same stages and arithmetic, the ablation of the offset.
+template <int kElem, bool kCausal, bool kOffset>
 __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[kKVSlots * kKVSlot];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -310,7 +312,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         rendezvous();
         read_k(1);
         wait_lgkmcnt<0>();
-        if (groupB) rendezvous();           // group B falls one stage behind
+        if (kOffset && groupB) rendezvous();    // group B falls one stage behind
 
         // one trip; kMasked: block i+1 may hold keys some row must not see
         auto trip = [&](int i, auto masked) {
@@ -353,7 +355,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         wait_lgkmcnt<0>();
         rendezvous();
         pv();
-        if (!groupB) rendezvous();          // group A closes the offset
+        if (kOffset && !groupB) rendezvous();   // group A closes the offset
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                    // zero-window copies past the end
     }
@@ -385,13 +387,17 @@ int attn_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_EHIP; }
 }  // namespace
 }  // namespace mcs
 
-extern "C" int attention_fwd(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
-                             int64_t head_dim, const void *Q, const void *K, const void *V, void *O,
-                             float *lse, float scale, int causal, hipStream_t stream) {
+namespace {
+
+int attention_launch(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k, int64_t head_dim,
+                     const void *Q, const void *K, const void *V, void *O, float *lse, float scale, int causal,
+                     int schedule, hipStream_t stream) {
     using namespace mcs;
     auto aligned16 = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; };
     if (dtype != GEMM_DTYPE_F16 && dtype != GEMM_DTYPE_BF16) return GEMM_EINVAL;
     if (causal != 0 && causal != 1) return GEMM_EINVAL;
+    if (schedule != GEMM_SCHED_AUTO && schedule != GEMM_SCHED_PIPELINED && schedule != GEMM_SCHED_IN_PHASE)
+        return GEMM_EINVAL;
     if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim < 0) return GEMM_EINVAL;
     if (!(scale > 0.f) || !std::isfinite(scale)) return GEMM_EINVAL;
     if (head_dim != kHeadDim) return GEMM_EUNSUPPORTED;
@@ -417,14 +423,33 @@ extern "C" int attention_fwd(int dtype, int64_t batch, int64_t heads, int64_t se
     prm.groups = static_cast<int>(groups);
     prm.c = scale * 1.4426950408889634f;
     prm.off = static_cast<int>(seq_k - seq_q);
+    const bool offset = schedule != GEMM_SCHED_IN_PHASE;
     const void *fn = nullptr;
-    if (dtype == GEMM_DTYPE_F16)
-        fn = causal ? reinterpret_cast<const void *>(&attention_fwd_kernel<kElemF16, true>)
-                    : reinterpret_cast<const void *>(&attention_fwd_kernel<kElemF16, false>);
-    else
-        fn = causal ? reinterpret_cast<const void *>(&attention_fwd_kernel<kElemBF16, true>)
-                    : reinterpret_cast<const void *>(&attention_fwd_kernel<kElemBF16, false>);
+#define MCS_ATTN(E, C, F) \
+    if ((dtype == GEMM_DTYPE_BF16) == (E == kElemBF16) && (causal != 0) == C && offset == F) \
+        fn = reinterpret_cast<const void *>(&attention_fwd_kernel<E, C, F>);
+    MCS_ATTN(kElemF16, false, true) MCS_ATTN(kElemF16, true, true)
+    MCS_ATTN(kElemBF16, false, true) MCS_ATTN(kElemBF16, true, true)
+    MCS_ATTN(kElemF16, false, false) MCS_ATTN(kElemF16, true, false)
+    MCS_ATTN(kElemBF16, false, false) MCS_ATTN(kElemBF16, true, false)
+#undef MCS_ATTN
     void *args[] = {&prm};
     return attn_status(hipLaunchKernel(fn, dim3(static_cast<unsigned>(nq * groups)), dim3(kAttnWaves * 64),
                                        args, 0, stream));
+}
+
+}  // namespace
+
+extern "C" int attention_fwd(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                             int64_t head_dim, const void *Q, const void *K, const void *V, void *O,
+                             float *lse, float scale, int causal, hipStream_t stream) {
+    return attention_launch(dtype, batch, heads, seq_q, seq_k, head_dim, Q, K, V, O, lse, scale, causal,
+                            GEMM_SCHED_AUTO, stream);
+}
+
+extern "C" int attention_fwd_ex(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
+                                int64_t head_dim, const void *Q, const void *K, const void *V, void *O,
+                                float *lse, float scale, int causal, int schedule, hipStream_t stream) {
+    return attention_launch(dtype, batch, heads, seq_q, seq_k, head_dim, Q, K, V, O, lse, scale, causal,
+                            schedule, stream);
 }

@@ -116,6 +116,25 @@ def test_deterministic():
     assert np.array_equal(b1, b2)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_in_phase_schedule_is_bitwise_identical(causal):
+    """Same stages and arithmetic with the groups in step: the offset changes
+    only timing."""
+    torch = _torch()
+    q, k, v = qkv("f16", 1, 3, 520, 777, 128, seed=15)
+    _, lse0, b0 = run_attention("f16", q, k, v, 0.08, causal)
+    Q, K, V = (upload(x.reshape(-1, 128), "f16")[0] for x in (q, k, v))
+    O = torch.empty_like(Q)
+    L = torch.empty(3 * 520, dtype=torch.float32, device="cuda")
+    st = mcs.attention_fwd_ex(mcs.GEMM_DTYPE_F16, 1, 3, 520, 777, 128, Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                              O.data_ptr(), L.data_ptr(), 0.08, int(causal), mcs.GEMM_SCHED_IN_PHASE,
+                              torch.cuda.current_stream().cuda_stream)
+    assert st == mcs.GEMM_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(O.cpu().view(torch.int16).numpy().view(np.uint16).reshape(b0.shape), b0)
+    assert np.array_equal(L.cpu().double().numpy().reshape(lse0.shape), lse0)
+
+
 def test_torch_binding_matches_abi():
     torch = _torch()
     q, k, v = qkv("f16", 2, 2, 200, 330, 128, seed=14)
