@@ -17,13 +17,14 @@
 // group B runs one stage behind group A (an extra barrier on entry for B and
 // on exit for A, as in the GEMM), so each MFMA stage of one group overlaps a
 // softmax stage of the other:
-//   0  MFMA   S(i+1) = Q K(i+1)^T                 (K fragments read in stage 3)
-//   1  VALU   O *= alpha(i); V(i) fragments; row max of S(i+1): m(i+1),
-//             alpha(i+1) = 2^(m(i) - m(i+1)); copies of block i+3; wait for
-//             block i+2
-//   2  MFMA   O += P(i) V(i)
+//   0  MFMA   S(i+1) = Q K(i+1)^T; once half the K fragments are used, the
+//             first half of the V(i) fragments is read into their registers;
+//             wait for block i+2
+//   1  VALU   O *= alpha(i); rest of V(i); row max of S(i+1): m(i+1),
+//             alpha(i+1) = 2^(m(i) - m(i+1)); copies of block i+3
+//   2  MFMA   O += P(i) V(i); first half of the K(i+2) fragments likewise
 //   3  VALU   P(i+1) = 2^(c S(i+1) - m(i+1)) rounded to the operand type,
-//             l = alpha(i+1) l + row sums; K(i+2) fragments
+//             l = alpha(i+1) l + row sums; rest of K(i+2)
 // with c = scale * log2(e).  A prologue computes S(0), P(0); a drain applies
 // alpha and P V of the last block; then O / l is stored with
 // lse = (m + log2 l) ln 2.
@@ -36,12 +37,12 @@
 // of a transposing ds_read_b64_tr_b16 touches 8 rows x 32 bytes, distinct
 // banks).  Waits:
 //   * copy -> read: block i+2 is copied during trip i-1 (stage 1) and each
-//     wave waits vmcnt(4) (only the copies of block i+3 may fly) at the end
-//     of stage 1 of trip i; its K is read in stage 3 of trip i (the other
-//     group's wait is two stages earlier), its V later.
+//     wave waits vmcnt(0) (block i+3 is not issued yet) at the end of stage 0
+//     of trip i; its K is read from stage 2 of trip i on (the other group's
+//     wait is then two stages back), its V in trip i+2.
 //   * read -> refill: block i+3 goes into the slot of block i-1, whose V was
-//     read in stage 1 of trip i-1 (lgkmcnt(0) before that stage's barrier),
-//     four stages before the copies.
+//     last read in stage 1 of trip i-1 (lgkmcnt(0) before that stage's
+//     barrier), four stages before the copies.
 //
 // The probabilities are packed straight from the S accumulators: a lane
 // holds 4 consecutive keys of one row per 16-key tile, so the PV MFMA takes
@@ -192,39 +193,55 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
 
         // One address add per lane base (kept opaque to the compiler); the
         // rest of every read's address is its immediate offset.
-        auto read_k = [&](int j) {
+        // K fragments of d-chunks dc0 .. dc1-1, V fragments of key chunks c0 .. c1-1
+        auto read_k = [&](int j, int dc0, int dc1) {
             const uint32_t b = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot;
-            for (int dc = 0; dc < 4; ++dc) {
+            for (int dc = dc0; dc < dc1; ++dc) {
                 uint32_t a = b + kofs[dc];
                 asm volatile("" : "+v"(a));
                 for (int kt = 0; kt < 4; ++kt) kf[kt][dc] = lds_read128(a + kt * 16 * kRowBytes);
             }
         };
-        auto read_v = [&](int j) {
+        auto read_v = [&](int j, int c0, int c1) {
             const uint32_t b = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + kKVTile;
             for (int dt = 0; dt < 8; ++dt) {
                 uint32_t a = b + vofs[dt];
                 asm volatile("" : "+v"(a));
-                for (int c = 0; c < 2; ++c) {
+                for (int c = c0; c < c1; ++c) {
                     const i32x2 lo = lds_read64_tr(a + (32 * c) * kRowBytes);
                     const i32x2 hi = lds_read64_tr(a + (32 * c + 16) * kRowBytes);
                     vf[dt][c] = i32x4{lo.x, lo.y, hi.x, hi.y};
                 }
             }
         };
-        auto qk = [&]() {
-            for (int dc = 0; dc < 4; ++dc)
+        // The MFMA stages run `mid` once half of their fragments are consumed:
+        // reads into the registers those fragments held.
+        auto qk = [&](auto mid) {
+            for (int dc = 0; dc < 4; ++dc) {
                 for (int mt = 0; mt < 2; ++mt)
                     for (int kt = 0; kt < 4; ++kt)
                         s[mt][kt] = mfma<kElem>(kf[kt][dc], qf[mt][dc],
                                                 dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mt][kt]);
+                if (dc == 1) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    mid();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         };
-        auto pv = [&]() {
-            for (int c = 0; c < 2; ++c)
+        auto pv = [&](auto mid) {
+            for (int c = 0; c < 2; ++c) {
                 for (int mt = 0; mt < 2; ++mt)
                     for (int dt = 0; dt < 8; ++dt)
                         o[mt][dt >> 2][dt & 3] = mfma<kElem>(vf[dt][c], pf[mt][c], o[mt][dt >> 2][dt & 3]);
+                if (c == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    mid();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         };
+        auto nothing = [] {};
         // keys past the end, and (causal) keys above the diagonal, score -inf
         auto mask = [&](int j) {
             const int k0 = j * kKeys;
@@ -254,9 +271,14 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         auto softmax_max = [&]() {
             pin_s();
             for (int mt = 0; mt < 2; ++mt) {
-                float mx = s[mt][0][0];
-                for (int kt = 0; kt < 4; ++kt)
-                    for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[mt][kt][e]);
+                // a tree of three-input maxima (depth 3, not a chain of 15)
+                const f32x4 *x = s[mt];
+                const float t0 = fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]);
+                const float t1 = fmaxf(fmaxf(x[0][3], x[1][0]), x[1][1]);
+                const float t2 = fmaxf(fmaxf(x[1][2], x[1][3]), x[2][0]);
+                const float t3 = fmaxf(fmaxf(x[2][1], x[2][2]), x[2][3]);
+                const float t4 = fmaxf(fmaxf(x[3][0], x[3][1]), x[3][2]);
+                float mx = fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), x[3][3]));
                 mx = row_reduce(mx, [](float a, float b) { return fmaxf(a, b); }) * p.c;
                 if (mx > m[mt] + kLazy) {
                     alpha[mt] = __builtin_amdgcn_exp2f(m[mt] - mx);
@@ -272,20 +294,19 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             pin_s();
             for (int mt = 0; mt < 2; ++mt) {
                 const float ref = m[mt] == -INFINITY ? 0.f : m[mt];
-                float sum = 0.f;
+                float part[4];                          // per 16-key tile, then a tree
                 for (int c = 0; c < 2; ++c) {
                     i32x2 h[2];
                     for (int u = 0; u < 2; ++u) {
                         f32x4 pr;
-                        for (int e = 0; e < 4; ++e) {
+                        for (int e = 0; e < 4; ++e)
                             pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][2 * c + u][e], p.c, -ref));
-                            sum += pr[e];
-                        }
+                        part[2 * c + u] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
                         h[u] = pack4<kElem>(pr);
                     }
                     pf[mt][c] = i32x4{h[0].x, h[0].y, h[1].x, h[1].y};
                 }
-                l[mt] = l[mt] * alpha[mt] + sum;
+                l[mt] = l[mt] * alpha[mt] + ((part[0] + part[1]) + (part[2] + part[3]));
             }
         };
         // O *= alpha, skipped when no row of the wave changed its max
@@ -301,42 +322,43 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<8>();                    // block 0 (this wave's pieces)
         rendezvous();                       // ... and everyone's
-        read_k(0);
+        read_k(0, 0, 4);
         wait_lgkmcnt<0>();
-        qk();
+        qk(nothing);
         mask(0);
         softmax_max();
         softmax_exp();
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<4>();                    // block 1
         rendezvous();
-        read_k(1);
+        read_k(1, 0, 4);
         wait_lgkmcnt<0>();
         if (kOffset && groupB) rendezvous();    // group B falls one stage behind
 
         // one trip; kMasked: block i+1 may hold keys some row must not see
         auto trip = [&](int i, auto masked) {
-            // stage 0: S(i+1)
-            qk();
+            // stage 0: S(i+1); first half of the V(i) fragments; wait for block i+2
+            qk([&] { read_v(i, 0, 1); });
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<0>();                // block i+2 (block i+3 is not issued yet)
             rendezvous();
-            // stage 1: rescale O, V(i) fragments, row max of S(i+1), copies of block i+3
-            read_v(i);
+            // stage 1: rescale O, rest of V(i), row max of S(i+1), copies of block i+3
+            read_v(i, 1, 2);
             copy_block(i + 3);
             rescale();                      // by alpha(i), before softmax_max sets alpha(i+1)
             if constexpr (decltype(masked)::value) mask(i + 1);
             softmax_max();
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<4>();                // block i+2
             wait_lgkmcnt<0>();
             rendezvous();
-            // stage 2: O += P(i) V(i)
-            pv();
+            // stage 2: O += P(i) V(i); first half of the K(i+2) fragments
+            pv([&] { read_k(i + 2, 0, 2); });
             rendezvous();
             // stage 3: P(i+1), row sums, K(i+2) fragments (read after S is
             // consumed, so S and the K fragments are not live together)
             softmax_exp();
             __builtin_amdgcn_sched_barrier(0);
-            read_k(i + 2);
+            read_k(i + 2, 2, 4);
             wait_lgkmcnt<0>();
             rendezvous();
         };
@@ -351,10 +373,10 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         for (; i + 1 < nblk; ++i) trip(i, std::true_type{});
         // ---- drain: the last block's alpha and P V
         rescale();
-        read_v(nblk - 1);
+        read_v(nblk - 1, 0, 2);
         wait_lgkmcnt<0>();
         rendezvous();
-        pv();
+        pv(nothing);
         if (kOffset && !groupB) rendezvous();   // group A closes the offset
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                    // zero-window copies past the end
