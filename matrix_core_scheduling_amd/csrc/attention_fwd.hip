@@ -17,14 +17,16 @@
 // group B runs one stage behind group A (an extra barrier on entry for B and
 // on exit for A, as in the GEMM), so each MFMA stage of one group overlaps a
 // softmax stage of the other:
-//   0  MFMA   S(i+1) = Q K(i+1)^T; once half the K fragments are used, the
-//             first half of the V(i) fragments is read into their registers;
-//             wait for block i+2
-//   1  VALU   O *= alpha(i); rest of V(i); row max of S(i+1): m(i+1),
+//   0  MFMA   S(i+1) = Q K(i+1)^T; the V(i) fragments are read into the
+//             registers of the K fragments as those are used (half after
+//             the first two d-chunks, half after the last); wait for block i+2
+//   1  VALU   O *= alpha(i); row max of S(i+1): m(i+1),
 //             alpha(i+1) = 2^(m(i) - m(i+1)); copies of block i+3
-//   2  MFMA   O += P(i) V(i); first half of the K(i+2) fragments likewise
+//   2  MFMA   O += P(i) V(i); the K(i+2) fragments read the same way
 //   3  VALU   P(i+1) = 2^(c S(i+1) - m(i+1)) rounded to the operand type,
-//             l = alpha(i+1) l + row sums; rest of K(i+2)
+//             l = alpha(i+1) l + row sums
+// (the operand reads sit in the MFMA stages: the softmax stages, not the
+// matrix stages, are the long ones)
 // with c = scale * log2(e).  A prologue computes S(0), P(0); a drain applies
 // alpha and P V of the last block; then O / l is stored with
 // lse = (m + log2 l) ln 2.
@@ -38,11 +40,11 @@
 // banks).  Waits:
 //   * copy -> read: block i+2 is copied during trip i-1 (stage 1) and each
 //     wave waits vmcnt(0) (block i+3 is not issued yet) at the end of stage 0
-//     of trip i; its K is read from stage 2 of trip i on (the other group's
-//     wait is then two stages back), its V in trip i+2.
+//     of trip i; its K is read in stage 2 of trip i (the other group's wait
+//     is then two stages back), its V in trip i+2.
 //   * read -> refill: block i+3 goes into the slot of block i-1, whose V was
-//     last read in stage 1 of trip i-1 (lgkmcnt(0) before that stage's
-//     barrier), four stages before the copies.
+//     last read in stage 0 of trip i-1 (lgkmcnt(0) before stage 1's
+//     barrier), five stages before the copies.
 //
 // The probabilities are packed straight from the S accumulators: a lane
 // holds 4 consecutive keys of one row per 16-key tile, so the PV MFMA takes
@@ -216,29 +218,27 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         };
         // The MFMA stages run `mid` once half of their fragments are consumed:
         // reads into the registers those fragments held.
-        auto qk = [&](auto mid) {
+        auto qk = [&](auto mid, auto tail) {
             for (int dc = 0; dc < 4; ++dc) {
                 for (int mt = 0; mt < 2; ++mt)
                     for (int kt = 0; kt < 4; ++kt)
                         s[mt][kt] = mfma<kElem>(kf[kt][dc], qf[mt][dc],
                                                 dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mt][kt]);
-                if (dc == 1) {
+                if (dc == 1 || dc == 3) {
                     __builtin_amdgcn_sched_barrier(0);
-                    mid();
+                    if (dc == 1) mid(); else tail();
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
-        auto pv = [&](auto mid) {
+        auto pv = [&](auto mid, auto tail) {
             for (int c = 0; c < 2; ++c) {
                 for (int mt = 0; mt < 2; ++mt)
                     for (int dt = 0; dt < 8; ++dt)
                         o[mt][dt >> 2][dt & 3] = mfma<kElem>(vf[dt][c], pf[mt][c], o[mt][dt >> 2][dt & 3]);
-                if (c == 0) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    mid();
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (c == 0) mid(); else tail();
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
         auto nothing = [] {};
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         rendezvous();                       // ... and everyone's
         read_k(0, 0, 4);
         wait_lgkmcnt<0>();
-        qk(nothing);
+        qk(nothing, nothing);
         mask(0);
         softmax_max();
         softmax_exp();
@@ -338,12 +338,11 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         // one trip; kMasked: block i+1 may hold keys some row must not see
         auto trip = [&](int i, auto masked) {
             // stage 0: S(i+1); first half of the V(i) fragments; wait for block i+2
-            qk([&] { read_v(i, 0, 1); });
+            qk([&] { read_v(i, 0, 1); }, [&] { read_v(i, 1, 2); });
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<0>();                // block i+2 (block i+3 is not issued yet)
             rendezvous();
             // stage 1: rescale O, rest of V(i), row max of S(i+1), copies of block i+3
-            read_v(i, 1, 2);
             copy_block(i + 3);
             rescale();                      // by alpha(i), before softmax_max sets alpha(i+1)
             if constexpr (decltype(masked)::value) mask(i + 1);
@@ -352,13 +351,11 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             wait_lgkmcnt<0>();
             rendezvous();
             // stage 2: O += P(i) V(i); first half of the K(i+2) fragments
-            pv([&] { read_k(i + 2, 0, 2); });
+            pv([&] { read_k(i + 2, 0, 2); }, [&] { read_k(i + 2, 2, 4); });
             rendezvous();
             // stage 3: P(i+1), row sums, K(i+2) fragments (read after S is
             // consumed, so S and the K fragments are not live together)
             softmax_exp();
-            __builtin_amdgcn_sched_barrier(0);
-            read_k(i + 2, 2, 4);
             wait_lgkmcnt<0>();
             rendezvous();
         };
@@ -376,7 +373,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         read_v(nblk - 1, 0, 2);
         wait_lgkmcnt<0>();
         rendezvous();
-        pv(nothing);
+        pv(nothing, nothing);
         if (kOffset && !groupB) rendezvous();   // group A closes the offset
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                    // zero-window copies past the end
