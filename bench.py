@@ -174,9 +174,10 @@ def bench_attention(a, w) -> int:
             at.attention(q[:1, :1], k[:1, :1], v[:1, :1], w.dtype, w.scale, w.causal, rows=np.arange(128))
             per_head = max(time.perf_counter() - t, 1e-3)
         heads = int(max(1, min(w.B * w.H, a.cpu_seconds / per_head)))
-        rows = np.arange(64)
+        # with every head in the sample, widen the row sample to fill the time budget
+        extra = int(max(64, min(w.Sq, 128 * a.cpu_seconds / (per_head * heads)) - 64))
         rng = np.random.default_rng(w.seed)
-        rows = np.unique(np.concatenate([rows, rng.integers(0, w.Sq, 64)]))
+        rows = np.unique(np.concatenate([np.arange(64), rng.integers(0, w.Sq, extra)]))
         hb = [(h // w.H, h % w.H) for h in range(heads)]
         print(f"[bench] CPU oracle on {rows.size} query rows x {heads} heads", file=sys.stderr, flush=True)
         t = time.perf_counter()
@@ -186,7 +187,7 @@ def bench_attention(a, w) -> int:
         mask = at.allowed_keys(w.Sq, w.Sk, w.causal)[rows]
         flops = 4.0 * heads * mask.sum() * w.D
         cpu = {"value": round(flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-               "sample": f"{rows.size} query rows (rows 0-63 and 64 seeded random ones) of each of the first "
+               "sample": f"{rows.size} query rows (rows 0-63 and seeded random ones) of each of the first "
                          f"{heads} (batch, head) pairs of the same workload, {cpu_s:.1f} s on {cpu_model()}"}
         import oracle
 
