@@ -50,9 +50,9 @@ PEAK_TFLOPS_UNITS = {"f16": 256 * 4 * 1024 * 2.4e9 / 1e12, "bf16": 256 * 4 * 102
 PAGES_TFLOPS = {"f16_4096x4096x8192": 1437.0, "fp8_8192": 3292.0}
 MALL_BYTES = 256 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-def traffic_for(workload: str, schedule: str):
-    """HBM bytes per launch from the committed counter runs, if they were taken
-    on the current source of the kernel that runs; otherwise None."""
+def counter_record(workload: str, schedule: str):
+    """The committed counter record (profiles/traffic.json) of this kernel on
+    this workload, if it was taken on the kernel's current source; else None."""
     from matrix_core_scheduling_amd import profiling
 
     kernel = schedule
@@ -65,7 +65,21 @@ def traffic_for(workload: str, schedule: str):
         return None
     if not t or t.get("kernel_source_sha256") != profiling.kernel_source_hash(kernel):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
+
+
+def traffic_for(workload: str, schedule: str):
+    """HBM bytes per launch from the committed counter runs, or None."""
+    t = counter_record(workload, schedule)
+    return t.get("hbm_bytes_per_launch") if t else None
+
+
+def mfma_busy_for(workload: str, schedule: str):
+    """MFMA-busy fraction and clock of the committed counter run, or None."""
+    t = counter_record(workload, schedule)
+    if not t or "mfma_busy" not in t:
+        return None
+    return {"mfma_busy": t["mfma_busy"], "clock_GHz": t["clock_GHz"], "source": "profiles/traffic.json"}
 
 
 def host_threads() -> int:
@@ -226,7 +240,8 @@ def bench_attention(a, w) -> int:
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": traffic},
+                     "frac": round(tflops / peak, 4), "traffic": traffic,
+                     "mfma_busy": mfma_busy_for(w.name, "attention")},
         "cpu_baseline": cpu,
         "check": check,
     }
@@ -433,7 +448,8 @@ def main(argv=None) -> int:
         "batch_median_ms": round(batch_med, 6),
         "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
+                     "mfma_busy": mfma_busy_for(w.name, eff)},
         "kernel": {"vgprs": info["num_regs"], "scratch_bytes_per_lane": info["local_bytes"],
                    "lds_bytes": info["shared_bytes"], "threads": info["block_threads"]},
         "cpu_baseline": cpu,

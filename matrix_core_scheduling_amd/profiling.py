@@ -119,7 +119,7 @@ def traffic_key(workload: str, schedule: str = "pipelined") -> str:
 
 
 def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, schedule="pipelined",
-            copy_kernel="copyBuffer") -> dict:
+            copy_kernel="copyBuffer", busy_dir=None) -> dict:
     kernel = "attention_fwd" if schedule == "attention" else "gemm_" + schedule
     copy_bytes = copy_mib * 2 ** 20
     cf = counters([copy_fetch_dir], copy_kernel)
@@ -134,10 +134,17 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, sche
     g_w = next(iter(counters([write_dir], kernel).values()))
     fetch = g_f["FETCH_SIZE"] * 1024 * f_scale
     write = g_w["WRITE_SIZE"] * 1024 * w_scale
-    return {"fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
-            "hbm_bytes_per_launch": round(fetch + write), "fetch_scale": round(f_scale, 5),
-            "write_scale": round(w_scale, 5), "copy_calibration_mib": copy_mib,
-            "kernel_source_sha256": kernel_source_hash(schedule)}
+    r = {"fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
+         "hbm_bytes_per_launch": round(fetch + write), "fetch_scale": round(f_scale, 5),
+         "write_scale": round(w_scale, 5), "copy_calibration_mib": copy_mib,
+         "kernel_source_sha256": kernel_source_hash(schedule)}
+    if busy_dir:
+        ag = agent(busy_dir)
+        cs = next(iter(counters([busy_dir], kernel).values()))
+        d = derived(cs, int(ag.get("Num_Xcc", 8)), int(ag.get("Simd_Count", 1024)))
+        r["mfma_busy"] = round(d["mfma_busy"], 4)
+        r["clock_GHz"] = round(d["clock_GHz"], 3)
+    return r
 
 
 def main(argv=None) -> int:
@@ -156,6 +163,7 @@ def main(argv=None) -> int:
     t.add_argument("--workload", required=True)
     t.add_argument("--schedule", default="pipelined", choices=sorted(KERNEL_SOURCES))
     t.add_argument("--update", default=None, help="JSON file to add the result to")
+    t.add_argument("--busy", default=None, help="counter run with GRBM_GUI_ACTIVE and SQ_VALU_MFMA_BUSY_CYCLES")
     a = ap.parse_args(argv)
 
     if a.cmd == "stats":
@@ -177,7 +185,7 @@ def main(argv=None) -> int:
                 print(f"| (derived) {n} | {v:.6g} |")
             print()
     elif a.cmd == "traffic":
-        r = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.schedule)
+        r = traffic(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib, a.schedule, busy_dir=a.busy)
         print(json.dumps(r, indent=1))
         if a.update:
             data = {}
