@@ -10,7 +10,9 @@ counts the schedule defines.  Per loop iteration the 8-wave kernel runs two
 K-steps (8 barriers), the 4-wave kernel one (2 barriers), the 128x128-tile
 kernel one (1 barrier; FP8: two); a 128-byte K-step is 64 FP16/BF16 MFMAs
 16x16x32 or 32 FP8 MFMAs 16x16x128 per wave in the 8-wave kernel, twice
-that in the 4-wave kernel and half of it in the 128x128-tile kernel.
+that in the 4-wave kernel and half of it in the 128x128-tile kernel.  The
+attention kernel's trips run 64 MFMAs (QK and PV of one 64-key block) and 4
+barriers.  No kernel of these files uses scratch memory at all.
 """
 import os
 import re
@@ -26,9 +28,9 @@ pytestmark = pytest.mark.skipif(not os.path.exists(build.HIPCC), reason="hipcc n
 # kernel -> (MFMAs per loop iteration for FP16/BF16, for FP8, barriers per iteration for each,
 #            instantiations)
 EXPECT = {"gemm_pipelined_kernel": (128, 64, 8, 8, 20), "gemm_interleaved_kernel": (128, 64, 2, 2, 10),
-          "gemm_tile128_kernel": (32, 32, 1, 2, 10)}
+          "gemm_tile128_kernel": (32, 32, 1, 2, 10), "attention_fwd_kernel": (64, None, 4, None, 8)}
 SOURCES = {"gemm_pipelined_kernel": "gemm_pipelined.hip", "gemm_interleaved_kernel": "gemm_interleaved.hip",
-           "gemm_tile128_kernel": "gemm_tile128.hip"}
+           "gemm_tile128_kernel": "gemm_tile128.hip", "attention_fwd_kernel": "attention_fwd.hip"}
 
 
 def loops(asm: str):
@@ -65,7 +67,7 @@ def test_main_loops(asm, kernel):
             continue
         per_fn.setdefault(fn, []).append((hdr, ops))
     # one symbol per instantiation: 2 element types x 2 B layouts x 2 outputs (+ FP8 N x K x 2 outputs),
-    # times offset/in-phase for the 8-wave kernel
+    # times offset/in-phase for the 8-wave kernel; attention: 2 types x causal or not x offset or not
     f16_mfma, f8_mfma, f16_bars, f8_bars, count = EXPECT[kernel]
     assert len(per_fn) == count, sorted(per_fn)
     for fn, ls in per_fn.items():
@@ -77,3 +79,10 @@ def test_main_loops(asm, kernel):
             assert not [o for o in ops if o.startswith("scratch_") or o.startswith("buffer_store")], where
             assert sum(o.startswith("v_mfma") for o in ops) == (f8_mfma if fp8 else f16_mfma), where
             assert ops.count("s_barrier") == (f8_bars if fp8 else f16_bars), where
+
+
+@pytest.mark.parametrize("kernel", sorted(EXPECT))
+def test_no_scratch_anywhere(asm, kernel):
+    sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm[kernel])
+    assert sizes and all(int(x) == 0 for x in sizes), sizes
+    assert not re.findall(r"\.vgpr_spill_count:\s+[1-9]", asm[kernel])
