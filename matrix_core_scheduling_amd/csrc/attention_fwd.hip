@@ -82,7 +82,10 @@ struct AttnParams {
 };
 
 // Workgroup -> (batch*head, query block): each XCD takes a contiguous range,
-// so the query blocks of one head share that XCD's L2 copy of K and V.
+// so the query blocks of one head share that XCD's L2 copy of K and V.  With
+// causal masks the last query blocks of a head see the most keys; they are
+// dispatched first (kReverse), so the light blocks fill the tail.
+template <bool kReverse>
 __device__ __forceinline__ void attn_coords(const AttnParams &p, int wg, int &bh, int &qb) {
     const int total = p.nq * p.groups;
     const int xcd = wg & 7, j = wg >> 3;
@@ -90,6 +93,7 @@ __device__ __forceinline__ void attn_coords(const AttnParams &p, int wg, int &bh
     const int v = xcd * q + min(xcd, r) + j;
     bh = v / p.nq;
     qb = v - bh * p.nq;
+    if constexpr (kReverse) qb = p.nq - 1 - qb;
 }
 
 // Combine the values of lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes
@@ -123,7 +127,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
     const int g = lane >> 4, r16 = lane & 15;
 
     int bh, qb;
-    attn_coords(p, blockIdx.x, bh, qb);
+    attn_coords<kCausal>(p, blockIdx.x, bh, qb);
     const int q0 = qb * kQRows;
     const int wrow = q0 + 32 * wave;                           // this wave's first query row
     const int64_t qbase = static_cast<int64_t>(bh) * p.Sq * kRowBytes;
