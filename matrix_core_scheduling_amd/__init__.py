@@ -46,13 +46,15 @@ class GemmKernelAttrs(ctypes.Structure):
 
 
 _lib = None
+_stagger_lib = None
+
+# The race-stress build of the same sources (compiled with MCS_STAGGER: random
+# sleeps at every workgroup barrier, NaN-filled LDS at kernel start).  Only the
+# tests load it, through load_stagger(); it exports the same C ABI.
+STAGGER_LIBRARY = os.path.join(_PKG, "libmcs_gemm_stagger.so")
 
 
-def load(path: str = LIBRARY) -> ctypes.CDLL:
-    """Load the library (once).  Raises if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
+def _open(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m matrix_core_scheduling_amd.build` "
                            "(there is no non-HIP fallback)")
@@ -81,8 +83,23 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.attention_fwd_ex.restype = ci
     lib.gemm_status_string.argtypes = [ci]
     lib.gemm_status_string.restype = ctypes.c_char_p
-    _lib = lib
     return lib
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        _lib = _open(path)
+    return _lib
+
+
+def load_stagger() -> ctypes.CDLL:
+    """Load the race-stress build (once): the same C ABI, for tests only."""
+    global _stagger_lib
+    if _stagger_lib is None:
+        _stagger_lib = _open(STAGGER_LIBRARY)
+    return _stagger_lib
 
 
 def header_functions(paths=(HEADER, ATTN_HEADER)) -> list[str]:

@@ -1,7 +1,12 @@
 """Build libmcs_gemm.so (the gfx950 GEMM kernels and their C ABI) in-tree with hipcc.
 
-    python -m matrix_core_scheduling_amd.build            # build the library
+    python -m matrix_core_scheduling_amd.build            # build the libraries
     python -m matrix_core_scheduling_amd.build --asm DIR  # also write device assembly
+
+Two libraries come out of the same sources: libmcs_gemm.so, the product, and
+libmcs_gemm_stagger.so, the race-stress build (compiled with MCS_STAGGER:
+random sleeps at every workgroup barrier and NaN-filled LDS at kernel start),
+which only the tests load.
 """
 from __future__ import annotations
 
@@ -16,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmcs_gemm.so")
+STAGGER_LIB = os.path.join(PKG, "libmcs_gemm_stagger.so")
 OBJDIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -39,28 +45,36 @@ def _run(cmd):
     return err
 
 
-def device_asm(src: str, out: str) -> str:
-    """Write the gfx950 assembly of one source file of csrc/ to ``out``."""
-    _run([HIPCC, *COMMON, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out])
+def device_asm(src: str, out: str, defines=()) -> str:
+    """Write the gfx950 assembly of one source file of csrc/ to ``out``
+    (``defines``: extra -D options, e.g. ["-DMCS_STAGGER=1"] for the race-stress build)."""
+    _run([HIPCC, *COMMON, *defines, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out])
     return out
 
 
 def build(asm_dir: str | None = None, jobs: int = 4) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+    """Compile both libraries; return the product library's path."""
+    variants = [(LIB, OBJDIR, []), (STAGGER_LIB, os.path.join(OBJDIR, "stagger"), ["-DMCS_STAGGER=1"])]
+    for _, objdir, _ in variants:
+        os.makedirs(objdir, exist_ok=True)
 
-    def compile_one(src):
-        obj = os.path.join(OBJDIR, src.replace(".hip", ".o"))
-        _run([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
-        if asm_dir:
+    def compile_one(job):
+        src, objdir, defs = job
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        _run([HIPCC, *COMMON, *defs, "-c", os.path.join(CSRC, src), "-o", obj])
+        if asm_dir and not defs:
             os.makedirs(asm_dir, exist_ok=True)
             device_asm(src, os.path.join(asm_dir, src.replace(".hip", f"-{ARCH}.s")))
         return obj
 
+    jobs_list = [(src, objdir, defs) for _, objdir, defs in variants for src in SOURCES]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
+        objs = list(ex.map(compile_one, jobs_list))
+    for i, (lib, _, _) in enumerate(variants):
+        tmp = lib + f".tmp{os.getpid()}"
+        mine = objs[i * len(SOURCES):(i + 1) * len(SOURCES)]
+        _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *mine, "-o", tmp])
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -79,6 +79,7 @@ struct AttnParams {
     int groups;    // batch * heads
     float c;       // scale * log2(e)
     int off;       // Sk - Sq (causal masks aligned at the bottom right)
+    uint32_t stagger_seed;   // race-stress pauses (read only by the race-stress build)
 };
 
 // Workgroup -> (batch*head, query block): each XCD takes a contiguous range,
@@ -157,6 +158,8 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
 
     if (nblk > 0) {
         const uint32_t lds0 = lds_address(smem);
+        stagger_poison_lds<kKVSlots * kKVSlot, kAttnWaves * 64>(lds0);
+        Stagger sg(p.stagger_seed);
         // copy lanes: wave w moves pieces 2w, 2w+1 (4 rows x 256 bytes each)
         // of the K and of the V block; lane (x, pch) fills physical chunk pch
         // of row x of a piece
@@ -325,7 +328,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         for (int j = 0; j < 3; ++j) copy_block(j);
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<8>();                    // block 0 (this wave's pieces)
-        rendezvous();                       // ... and everyone's
+        rendezvous(sg);                     // ... and everyone's
         read_k(0, 0, 4);
         wait_lgkmcnt<0>();
         qk(nothing, nothing);
@@ -334,10 +337,10 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         softmax_exp();
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<4>();                    // block 1
-        rendezvous();
+        rendezvous(sg);
         read_k(1, 0, 4);
         wait_lgkmcnt<0>();
-        if (kOffset && groupB) rendezvous();    // group B falls one stage behind
+        if (kOffset && groupB) rendezvous(sg);  // group B falls one stage behind
 
         // one trip; kMasked: block i+1 may hold keys some row must not see
         auto trip = [&](int i, auto masked) {
@@ -345,7 +348,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             qk([&] { read_v(i, 0, 1); }, [&] { read_v(i, 1, 2); });
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<0>();                // block i+2 (block i+3 is not issued yet)
-            rendezvous();
+            rendezvous(sg);
             // stage 1: rescale O, rest of V(i), row max of S(i+1), copies of block i+3
             copy_block(i + 3);
             rescale();                      // by alpha(i), before softmax_max sets alpha(i+1)
@@ -353,15 +356,15 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             softmax_max();
             __builtin_amdgcn_sched_barrier(0);
             wait_lgkmcnt<0>();
-            rendezvous();
+            rendezvous(sg);
             // stage 2: O += P(i) V(i); first half of the K(i+2) fragments
             pv([&] { read_k(i + 2, 0, 2); }, [&] { read_k(i + 2, 2, 4); });
-            rendezvous();
+            rendezvous(sg);
             // stage 3: P(i+1), row sums, K(i+2) fragments (read after S is
             // consumed, so S and the K fragments are not live together)
             softmax_exp();
             wait_lgkmcnt<0>();
-            rendezvous();
+            rendezvous(sg);
         };
         // leading blocks no row of the workgroup needs masked: every key
         // exists and (causal) every key is visible to the first row
@@ -376,9 +379,9 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         rescale();
         read_v(nblk - 1, 0, 2);
         wait_lgkmcnt<0>();
-        rendezvous();
+        rendezvous(sg);
         pv(nothing, nothing);
-        if (kOffset && !groupB) rendezvous();   // group A closes the offset
+        if (kOffset && !groupB) rendezvous(sg); // group A closes the offset
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                    // zero-window copies past the end
     }
@@ -446,6 +449,7 @@ int attention_launch(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int
     prm.groups = static_cast<int>(groups);
     prm.c = scale * 1.4426950408889634f;
     prm.off = static_cast<int>(seq_k - seq_q);
+    prm.stagger_seed = next_stagger_seed();
     const bool offset = schedule != GEMM_SCHED_IN_PHASE;
     const void *fn = nullptr;
 #define MCS_ATTN(E, C, F) \

@@ -52,11 +52,91 @@ __device__ __forceinline__ void wait_lgkmcnt() {
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
 }
 
-// Stage boundary: scheduling wall, workgroup rendezvous, scheduling wall.
-__device__ __forceinline__ void rendezvous() {
+// ---- race-stress build ---------------------------------------------------
+//
+// Compiled with MCS_STAGGER (a separate test library, never the product
+// one), every wave idles for a pseudo-random 0..15 sleeps of 64 cycles on
+// both sides of every workgroup barrier, and the workgroup's LDS starts out
+// filled with 0xFF bytes (a NaN in FP16, BF16, FP8 E4M3 and FP32).  A wait
+// or barrier missing from a schedule then shows up as a result that differs
+// from the unperturbed run, or as NaN, instead of hiding behind the waves'
+// usual timing; the arithmetic and its order are unchanged, so a correct
+// schedule gives bitwise the same result.  The sleeps add no memory
+// instruction and no s_waitcnt.  In the product build a Stagger is empty and
+// every pause compiles to nothing.
+struct Stagger {
+#ifdef MCS_STAGGER
+    uint32_t x;   // wave-uniform generator state (an SGPR)
+
+    __device__ __forceinline__ explicit Stagger(uint32_t seed) {
+        const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        uint32_t h = seed ^ (blockIdx.x * 0x9E3779B9u) ^ (blockIdx.y * 0x85EBCA6Bu) ^ (wave * 0xC2B2AE35u);
+        h ^= h >> 16;   // murmur3 finaliser
+        h *= 0x85EBCA6Bu;
+        h ^= h >> 13;
+        h *= 0xC2B2AE35u;
+        h ^= h >> 16;
+        x = __builtin_amdgcn_readfirstlane(h);
+    }
+
+    // The sleep loop sits inside one asm statement, so the compiler sees no
+    // new control flow and allocates registers as in the product build.
+    __device__ __forceinline__ void pause() {
+        x = x * 1664525u + 1013904223u;   // LCG step; the top four bits pick the count
+        uint32_t n = __builtin_amdgcn_readfirstlane(x >> 28);
+        asm volatile(
+            "s_cmp_eq_u32 %0, 0\n\t"
+            "s_cbranch_scc1 1f\n"
+            "0:\n\t"
+            "s_sleep 1\n\t"
+            "s_sub_u32 %0, %0, 1\n\t"
+            "s_cmp_lg_u32 %0, 0\n\t"
+            "s_cbranch_scc1 0b\n"
+            "1:"
+            : "+s"(n)
+            :
+            : "scc");
+    }
+#else
+    __device__ __forceinline__ explicit Stagger(uint32_t) {}
+    __device__ __forceinline__ void pause() {}
+#endif
+};
+
+// Race-stress build: fill kBytes of LDS from lds0 with 0xFF, then meet, so
+// no copy lands before the fill is complete.  Nothing in the product build.
+template <uint32_t kBytes, int kThreads>
+__device__ __forceinline__ void stagger_poison_lds(uint32_t lds0) {
+#ifdef MCS_STAGGER
+    static_assert(kBytes % (16 * kThreads) == 0, "whole 16-byte stores per thread");
+#pragma unroll
+    for (uint32_t i = 0; i < kBytes / (16u * kThreads); ++i) {
+        const uint32_t off = (i * kThreads + threadIdx.x) * 16u;
+        *reinterpret_cast<lds_i32x4 *>(static_cast<uintptr_t>(lds0 + off)) = i32x4{-1, -1, -1, -1};
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#else
+    (void)lds0;
+#endif
+}
+
+// Stage boundary: scheduling wall, workgroup rendezvous, scheduling wall
+// (with the race-stress pauses on both sides of the barrier).
+__device__ __forceinline__ void rendezvous(Stagger &sg) {
+    sg.pause();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    sg.pause();
+}
+
+// A barrier only some waves take (the entry and exit offsets of two wave
+// groups), with the race-stress pause before it.
+__device__ __forceinline__ void group_barrier(Stagger &sg) {
+    sg.pause();
+    __builtin_amdgcn_s_barrier();
 }
 
 // 128-bit buffer resource: base, stride 0, num_records bytes, GFX9 config word.
@@ -187,8 +267,9 @@ struct Loader {
     int wave;
     const GemmParams &p;
     TileWindows win;                 // the tile being computed
+    mutable Stagger sg;              // race-stress pauses (empty in the product build)
 
-    __device__ __forceinline__ Loader(const GemmParams &prm, int tm, int tn) : p(prm) {
+    __device__ __forceinline__ Loader(const GemmParams &prm, int tm, int tn) : p(prm), sg(prm.stagger_seed) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -68,6 +68,7 @@ int validate(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t 
 int to_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_EHIP; }
 
 int launch(const void *fn, dim3 grid, dim3 block, GemmParams &prm, hipStream_t stream) {
+    prm.stagger_seed = mcs::next_stagger_seed();
     void *args[] = {&prm};
     return to_status(hipLaunchKernel(fn, grid, block, args, 0, stream));
 }

@@ -125,11 +125,11 @@ struct Interleave : Loader<kElem, kTransB, kWaves>, Block64Reader<kTransB, kOffB
 
 // This wave's copies for the reads after the barrier have landed, and its own
 // LDS reads are complete (their halves are refilled after the barrier).
-__device__ __forceinline__ void wait_and_rendezvous() {
+__device__ __forceinline__ void wait_and_rendezvous(Stagger &sg) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<kCopyWait>();
     wait_lgkmcnt<0>();
-    rendezvous();
+    rendezvous(sg);
 }
 
 template <int kElem, bool kTransB, bool kOutF32>
@@ -143,6 +143,7 @@ gemm_interleaved_kernel(GemmParams pin) {
     tile_coords(p, blockIdx.x, tm, tn);
     Interleave<kElem, kTransB> il(p, tm, tn);
     il.lds0 = lds_address(smem);
+    stagger_poison_lds<2 * kBuf, kInterThreads>(il.lds0);
     const int wave = il.wave;
 
     f32x4 acc[2][2][4][4];
@@ -164,7 +165,7 @@ gemm_interleaved_kernel(GemmParams pin) {
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<24>();                   // A0(0) and B0(0) landed (this wave's part)
-    rendezvous();                       // ... and every wave's part
+    rendezvous(il.sg);                  // ... and every wave's part
     {
         const auto bs = il.bases(0, kBuf);
         for (int j = 0; j < 8; ++j) {
@@ -185,10 +186,10 @@ gemm_interleaved_kernel(GemmParams pin) {
         constexpr bool kMask = decltype(mask)::value;
         const uint32_t cur = (s & 1) ? kBuf : 0u, nxt = kBuf - cur;
         const auto bs = il.bases(cur, nxt);
-        wait_and_rendezvous();
+        wait_and_rendezvous(il.sg);
         il.template cluster<true, false, kMask, true>(acc[0][0], a0, b0, b1, bs, 0, 1, s + 2, cur, 0);
         il.template cluster<false, true, kMask, true>(acc[0][1], a0, b1, a1, bs, 0, 1, s + 2, cur, 0);
-        wait_and_rendezvous();
+        wait_and_rendezvous(il.sg);
         il.template cluster<false, true, kMask, false>(acc[1][0], a1, b0, a0, bs, 1, 0, s + 2, cur, 1);
         il.template cluster<true, false, kMask, false>(acc[1][1], a1, b1, b0, bs, 1, 0, s + 2, cur, 1);
     };

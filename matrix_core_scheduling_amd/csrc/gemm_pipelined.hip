@@ -140,12 +140,12 @@ __device__ __forceinline__ void mem_stage_begin() { __builtin_amdgcn_s_setprio(1
 // End of a memory stage: this wave's copies for the reads two stages later
 // have landed, and so have its own LDS reads (their registers feed the next
 // stage and their half may be refilled two stages on).
-__device__ __forceinline__ void mem_stage_end() {
+__device__ __forceinline__ void mem_stage_end(Stagger &sg) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<kCopyWait>();
     wait_lgkmcnt<0>();
     __builtin_amdgcn_s_setprio(0);
-    rendezvous();
+    rendezvous(sg);
 }
 
 template <int kElem, bool kTransB, bool kOutF32, bool kOffset>
@@ -159,6 +159,7 @@ gemm_pipelined_kernel(GemmParams pin) {
     tile_coords(p, blockIdx.x, tm, tn);
     Pipeline<kElem, kTransB, kOutF32, kOffset> pl(p, tm, tn);
     pl.lds0 = lds_address(smem);
+    stagger_poison_lds<2 * kBuf, kPipeThreads>(pl.lds0);
     const int wave = pl.wave;
 
     f32x4 acc[2][2][2][4];
@@ -181,17 +182,17 @@ gemm_pipelined_kernel(GemmParams pin) {
     pl.copy_b(1, kBuf, 1);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<10>();                   // a0(0) a1(0) b0(0) landed (this wave's part)
-    rendezvous();                       // ... and every wave's part
+    rendezvous(pl.sg);                  // ... and every wave's part
     pl.read_a(a0, 0, 0);
     pl.read_a(a1, 0, 1);
     pl.read_b(b0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt<0>();
     wait_vmcnt<kCopyWait>();            // b1(0) landed: the state at the end of S3 of step -1
-    rendezvous();
+    rendezvous(pl.sg);
 
     if constexpr (kOffset) {
-        if (wave >= 4) __builtin_amdgcn_s_barrier();   // group B waits: entry offset
+        if (wave >= 4) group_barrier(pl.sg);           // group B waits: entry offset
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -204,31 +205,31 @@ gemm_pipelined_kernel(GemmParams pin) {
             // S0: quadrants Q00 and Q10
             quadrant<kElem>(acc[0][0], a0, b0);
             quadrant<kElem>(acc[1][0], a1, b0);
-            rendezvous();
+            rendezvous(pl.sg);
             // S1
             mem_stage_begin();
             pl.read_b(b1, cur, 1);
             pl.copy_a(s + 2, cur, 0);
             pl.copy_a(s + 2, cur, 1);
             pl.copy_b(s + 2, cur, 0);
-            mem_stage_end();
+            mem_stage_end(pl.sg);
             // S2: quadrants Q01 and Q11
             quadrant<kElem>(acc[0][1], a0, b1);
             quadrant<kElem>(acc[1][1], a1, b1);
-            rendezvous();
+            rendezvous(pl.sg);
             // S3
             mem_stage_begin();
             pl.read_a(a0, nxt, 0);
             pl.read_a(a1, nxt, 1);
             pl.read_b(b0, nxt, 0);
             pl.copy_b(s + 2, cur, 1);
-            mem_stage_end();
+            mem_stage_end(pl.sg);
         }
     }
 
     if constexpr (kOffset) {
         __builtin_amdgcn_sched_barrier(0);
-        if (wave < 4) __builtin_amdgcn_s_barrier();    // group A waits: exit offset
+        if (wave < 4) group_barrier(pl.sg);            // group A waits: exit offset
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();   // the zero-window copies of steps past the end, before LDS is released

@@ -69,7 +69,7 @@ struct Tile128 : Loader<kElem, kTransB, kWaves128, kT, kHalf>, Block64Reader<kTr
                                           const i32x4 (&b)[4][2], i32x4 (&an)[4][2],
                                           i32x4 (&bn)[4][2], int s) const {
         wait_vmcnt<2 * Base::P>();
-        rendezvous();
+        rendezvous(this->sg);
         const Bases bs = this->bases_at(lds0, slot(s + 1), slot(s + 1));
         const uint32_t cbuf = slot(s + kAhead);
         static_for<0, 8>([&](auto g) {
@@ -96,7 +96,7 @@ struct Tile128 : Loader<kElem, kTransB, kWaves128, kT, kHalf>, Block64Reader<kTr
     __device__ __forceinline__ void kstep16(f32x4 (&acc)[4][4], i32x4 (&a)[4][2], i32x4 (&b)[4][2],
                                             int s) const {
         wait_vmcnt<2 * Base::P>();
-        rendezvous();
+        rendezvous(this->sg);
         const Bases bs = this->bases_at(lds0, slot(s), slot(s + 1));
         const uint32_t cbuf = slot(s + kAhead);
         static_for<0, 8>([&](auto g) {
@@ -130,6 +130,7 @@ gemm_tile128_kernel(GemmParams pin) {
     tile_coords(p, blockIdx.x, tm, tn);
     Tile128<kElem, kTransB> t(p, tm, tn);
     t.lds0 = lds_address(smem);
+    stagger_poison_lds<kRing * kSlot, kWaves128 * 64>(t.lds0);
 
     f32x4 acc[4][4];
     for (int mt = 0; mt < 4; ++mt)
@@ -143,7 +144,7 @@ gemm_tile128_kernel(GemmParams pin) {
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<2 * (kAhead - 1) * Tile128<kElem, kTransB>::P>();   // step 0 landed (this wave)
-    rendezvous();                                                  // ... and every wave's part
+    rendezvous(t.sg);                                              // ... and every wave's part
     t.read_all(0, a0, b0);
 
     // A given M x K (and B given N x K) needs the per-lane k mask on the

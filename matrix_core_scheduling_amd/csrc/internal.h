@@ -25,6 +25,8 @@ struct GemmParams {
     int kslice;
     float *ws;
     int64_t ldws;
+    // Seed of the race-stress pauses (read only by the race-stress build).
+    uint32_t stagger_seed;
 };
 
 // The view of the product one workgroup computes: the whole of it, or with
@@ -60,6 +62,11 @@ constexpr int kTile128 = 128, kTile128Threads = 256;
 // Generic kernel: 64x64 tiles of 256 threads.
 constexpr int kGenTile = 64, kGenThreads = 256;
 
+// The host-side accessors below stay inside the library (hidden), so two
+// builds of it loaded into one process (the product and the race-stress
+// build) each launch their own kernels.
+#pragma GCC visibility push(hidden)
+
 // Return the device function for (elem, trans_b, out_f32[, offset]) so the host
 // can launch it or query its attributes; nullptr for a combination that is not
 // compiled (the 256x256 kernels take FP8 operands only with B given N x K).
@@ -71,5 +78,18 @@ const void *generic_kernel(int elem, bool trans_b, bool out_f32);
 const void *zero_fill_kernel(bool out_f32);
 // Split-K reduction into C: out_kind 0 FP16, 1 BF16, 2 FP32.
 const void *splitk_reduce_kernel(int out_kind);
+
+#pragma GCC visibility pop
+
+// Seed for the next launch's race-stress pauses: a fresh value per launch in
+// the race-stress build (MCS_STAGGER), 0 in the product build.
+inline uint32_t next_stagger_seed() {
+#ifdef MCS_STAGGER
+    static uint32_t counter = 0;
+    return __atomic_add_fetch(&counter, 1u, __ATOMIC_RELAXED) * 0x9E3779B9u;
+#else
+    return 0;
+#endif
+}
 
 }  // namespace mcs

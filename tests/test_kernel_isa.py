@@ -13,6 +13,11 @@ kernel one (1 barrier; FP8: two); a 128-byte K-step is 64 FP16/BF16 MFMAs
 that in the 4-wave kernel and half of it in the 128x128-tile kernel.  The
 attention kernel's trips run 64 MFMAs (QK and PV of one 64-key block) and 4
 barriers.  No kernel of these files uses scratch memory at all.
+
+The race-stress build of the same files (MCS_STAGGER) must keep every loop
+as it is -- the same MFMAs, barriers and no copies or scratch -- and add one
+sleep loop on each side of every barrier, while the product build has no
+sleep at all.
 """
 import os
 import re
@@ -58,9 +63,48 @@ def asm(tmp_path_factory):
     return {k: open(build.device_asm(src, str(d / (src + ".s")))).read() for k, src in SOURCES.items()}
 
 
+@pytest.fixture(scope="module")
+def stagger_asm(tmp_path_factory):
+    d = tmp_path_factory.mktemp("isa_stagger")
+    return {k: open(build.device_asm(src, str(d / (src + ".s")), ["-DMCS_STAGGER=1"])).read()
+            for k, src in SOURCES.items()}
+
+
+SLEEP_LOOP = ["s_cmp_eq_u32", "s_cbranch_scc1", "0:", "s_sleep", "s_sub_u32", "s_cmp_lg_u32", "s_cbranch_scc1",
+              "1:"]
+
+
+def _strip_sleeps(ops):
+    """The loop's mnemonics without the race-stress sleep loops (one inline asm
+    statement each, local labels 0 and 1 included)."""
+    out, i = [], 0
+    while i < len(ops):
+        if ops[i:i + len(SLEEP_LOOP)] == SLEEP_LOOP:
+            i += len(SLEEP_LOOP)
+            continue
+        out.append(ops[i])
+        i += 1
+    return out
+
+
 @pytest.mark.parametrize("kernel", sorted(EXPECT))
 def test_main_loops(asm, kernel):
-    found = loops(asm[kernel])
+    check_loops(asm[kernel], kernel)
+
+
+@pytest.mark.parametrize("kernel", sorted(EXPECT))
+def test_race_stress_build_keeps_the_loops(asm, stagger_asm, kernel):
+    assert "s_sleep" not in asm[kernel]
+    n = check_loops(stagger_asm[kernel], kernel, strip=True)
+    assert n > 0
+    sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", stagger_asm[kernel])
+    assert sizes and all(int(x) == 0 for x in sizes), sizes
+
+
+def check_loops(text, kernel, strip=False):
+    """Check every main loop of `kernel` in `text`; return the number of sleeps seen."""
+    found = loops(text)
+    sleeps = 0
     per_fn = {}
     for (fn, hdr), ops in found.items():
         if kernel not in fn:
@@ -74,11 +118,17 @@ def test_main_loops(asm, kernel):
         fp8 = "ILi2E" in fn
         for hdr, ops in ls:
             where = f"{fn} loop {hdr}"
+            if strip:
+                bars = ops.count("s_barrier")
+                sleeps += ops.count("s_sleep")
+                assert ops.count("s_sleep") == 2 * bars, f"{where}: {ops.count('s_sleep')} sleeps, {bars} barriers"
+                ops = _strip_sleeps(ops)
             copies = [o for o in ops if o.startswith("v_accvgpr_")]
             assert not copies, f"{where}: {len(copies)} accumulator copies"
             assert not [o for o in ops if o.startswith("scratch_") or o.startswith("buffer_store")], where
             assert sum(o.startswith("v_mfma") for o in ops) == (f8_mfma if fp8 else f16_mfma), where
             assert ops.count("s_barrier") == (f8_bars if fp8 else f16_bars), where
+    return sleeps
 
 
 @pytest.mark.parametrize("kernel", sorted(EXPECT))
