@@ -252,8 +252,11 @@ def bench_attention(a, w) -> int:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=100)
+    # 1,000 untimed and 1,000 timed launches, as the pages' FlyDSL/HIP comparison does
+    # ("Porting High-Performance HIP Kernels to FlyDSL", section "Results"); a fresh
+    # process needs tens of milliseconds of work before the clock settles.
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default=si.HEADLINE, choices=sorted(si.WORKLOADS) + sorted(si.ATTN_WORKLOADS))
     ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "interleaved", "tile128", "generic"])
     ap.add_argument("--splits", default="auto",
