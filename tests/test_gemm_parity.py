@@ -10,7 +10,7 @@ import pytest
 import matrix_core_scheduling_amd as mcs
 import oracle
 import seeded_inputs as si
-from tests.gpu_util import assert_bit_exact, assert_within_tolerance, run
+from tests.gpu_util import assert_bit_exact, assert_within_tolerance, run, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -326,3 +326,54 @@ def test_kernels_have_no_spills():
                     assert info["local_bytes"] == 0, info
                     assert info["shared_bytes"] == 128 * 1024, info
                     assert info["block_threads"] == threads
+
+
+@pytest.mark.parametrize("elem", ["f16", "fp8"])
+def test_longest_rows_the_tiled_kernels_take(elem):
+    """Rows of 2^24 - 16 bytes, the most the tiled kernels accept (their 128-row
+    copy windows then span ~2 GiB of 32-bit buffer offsets): M = 130, N = 24,
+    K = 8,388,600 FP16 or 16,777,200 FP8 (a partial last K-step either way),
+    B given N x K.  Sparse integer operands put their nonzeros in the first,
+    middle and last K-steps, so every product is a short exact sum: each
+    output must equal it bit for bit (and the oracle at sampled points)."""
+    torch = pytest.importorskip("torch")
+    M, N = 130, 24
+    eb = 1 if elem == "fp8" else 2
+    K = (2 ** 24 - 16) // eb
+    if elem == "fp8":
+        enc, dt, oe = {-2: 0xC0, -1: 0xB8, 0: 0, 1: 0x38, 2: 0x40}, np.uint8, "bf16"
+    else:
+        enc, dt, oe = {-2: 0xC000, -1: 0xBC00, 0: 0, 1: 0x3C00, 2: 0x4000}, np.uint16, "f16"
+    a = np.zeros((M, K), dt)
+    b = np.zeros((N, K), dt)
+    r = np.arange(M)
+    a[r, K - 1 - r] = enc[1]
+    a[r, 8 * r + 3] = enc[2]
+    a[r, K // 2 + r] = enc[-1]
+    for j in range(N):
+        b[j, K - 1 - r] = [enc[(j + x) % 5 - 2] for x in r]
+        b[j, 8 * r + 3] = [enc[(j * x) % 3 - 1] for x in r]
+        b[j, K // 2 + r] = [enc[(j + x) % 2] for x in r]
+    cols = np.unique(np.concatenate([K - 1 - r, 8 * r + 3, K // 2 + r]))
+    exact = oracle.decode(a[:, cols], elem) @ oracle.decode(b[:, cols], elem).T
+    ii = np.array([0, 1, 64, 127, 128, 129, 129])
+    jj = np.array([0, 23, 5, 17, 0, 23, 11])
+    cpts, _ = oracle.gemm_points(a, b, elem, 1, ii, jj)
+    assert np.array_equal(cpts, exact[ii, jj])
+    A, _ = upload(a, elem)
+    B, _ = upload(b, elem)
+    del a, b
+    stream = torch.cuda.current_stream().cuda_stream
+    dtype = mcs.GEMM_DTYPE_FP8_E4M3 if elem == "fp8" else mcs.GEMM_DTYPE_F16
+    out_type = mcs.GEMM_OUT_BF16 if elem == "fp8" else mcs.GEMM_OUT_SAME
+    cdt = torch.bfloat16 if elem == "fp8" else torch.float16
+    for sched in (mcs.GEMM_SCHED_PIPELINED, mcs.GEMM_SCHED_INTERLEAVED, mcs.GEMM_SCHED_TILE128):
+        print(f"[gpu] longest rows {elem} M={M} N={N} K={K} sched={sched}", flush=True)
+        C = torch.full((M, N), 7.0, dtype=cdt, device="cuda")
+        st = mcs.gemm_ex(dtype, M, N, K, A.data_ptr(), K, B.data_ptr(), K, 1, C.data_ptr(), N, out_type, sched,
+                         stream)
+        assert st == mcs.GEMM_OK, mcs.gemm_status_string(st)
+        torch.cuda.synchronize()
+        got = oracle.decode(C.cpu().view(torch.int16).numpy().view(np.uint16), oe)
+        bad = np.argwhere(got != exact)
+        assert bad.size == 0, f"sched {sched}: {len(bad)} wrong, first {bad[0].tolist()}"
