@@ -400,7 +400,7 @@ struct FragOffsets {
             row[ks] = (row0 + l16) * 128 + (((4 * ks) | lg) ^ swz) * 16;
     }
 
-    // col0 a multiple of 64
+    // col0 a multiple of 32
     __device__ __forceinline__ void cols_tr(int col0, int lane) {
         // lane (lg, l16) of a transposed read for (nt, ks, h) loads 8 bytes of
         // k-row 32ks + 4h + 8lg + (l16 >> 2), columns col0 + 16nt + 4(l16 & 3):
@@ -498,19 +498,20 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int wg, int &tm
 
 // ---- fused epilogue ------------------------------------------------------
 //
-// Store one lane's part of four neighbouring 16x16 accumulator tiles (columns
-// col0 .. col0+63 of row `row`).  With the B fragment as the first MFMA
+// Store one lane's part of kN (2 or 4) neighbouring 16x16 accumulator tiles
+// (columns col0 .. col0+16kN-1 of row `row`).  With the B fragment as the first MFMA
 // operand, lane l of tile nt holds columns 16nt + 4(l >> 4) .. +3 of row
 // l & 15.  FP32 output stores those four values (16 bytes).  For a 16-bit
 // output (FP16, or BF16 with kBF16; round to nearest even), lanes l and l^16
 // trade halves of tiles nt and nt+1 so every lane stores eight consecutive
 // columns (16 bytes).  Columns at or past N are not written.
-template <bool kBF16, bool kOutF32>
-__device__ __forceinline__ void store_strip(const GemmParams &p, const f32x4 (&v4)[4], int row,
+template <bool kBF16, bool kOutF32, int kN>
+__device__ __forceinline__ void store_strip(const GemmParams &p, const f32x4 (&v4)[kN], int row,
                                             int col0, int lane) {
+    static_assert(kN == 2 || kN == 4, "pairs of 16-column tiles");
     const int g = lane >> 4;
     if constexpr (kOutF32) {
-        for (int nt = 0; nt < 4; ++nt) {
+        for (int nt = 0; nt < kN; ++nt) {
             const int col = col0 + 16 * nt + 4 * g;
             f32x4 v = v4[nt];
             asm volatile("" : "+v"(v));   // stage through VGPRs: keeps the accumulators' allocation free
@@ -523,7 +524,7 @@ __device__ __forceinline__ void store_strip(const GemmParams &p, const f32x4 (&v
             }
         }
     } else {
-        for (int nt = 0; nt < 4; nt += 2) {
+        for (int nt = 0; nt < kN; nt += 2) {
             i32x2 h0, h1;
             if constexpr (kBF16) {
                 h0 = __builtin_bit_cast(i32x2, __builtin_convertvector(v4[nt], bf16x4));

@@ -48,7 +48,8 @@
 // R was copied with eight copies of this wave issued after it by the end of
 // stage R-2 (S1 copies six, S3 two), so both memory stages end with
 // vmcnt(8) lgkmcnt(0); every copy has a full K-step to land.  At most 64
-// fragment VGPRs are live (a0 a1 b0 b1 is 16+16+32+32, never all four).
+// fragment VGPRs are live with B given N x K (a0 a1 b0 b1 is 16+16+32+32,
+// never all four), 80 with B given K x N (32+32+16+16).
 // The LDS reads open each memory stage so that their latency overlaps the
 // address and descriptor work of the copies.  Copies of K-steps past the end
 // use an empty buffer window, so they write zeros (buffer loads outside the
@@ -64,7 +65,8 @@
 // rows) with chunk ^ 2*((k & 3) + 4*((k >> 3) & 1)), read with the gfx950
 // transposing ds_read_b64_tr_b16 into the K-major MFMA operand.
 // Wave (wm, wn) = (wave & 3, wave >> 2) owns rows 32wm..32wm+31 of every A half
-// and columns 64wn..64wn+63 of every B half: a 32x64 block of each quadrant.
+// and columns 64wn..64wn+63 of every B half: a 32x64 block of each quadrant
+// (B given K x N: (wave & 1, wave >> 1), a 64x32 block; see WaveLayout).
 // MFMA: v_mfma_f32_16x16x32_{f16,bf16} with the B fragment as the first
 // operand, so each lane ends with four consecutive columns of one row; for a
 // 16-bit output, lanes l and l^16 trade halves of two neighbouring tiles so
@@ -76,39 +78,56 @@ namespace {
 
 constexpr int kCopyWait = 8;               // vmcnt at the end of each memory stage
 
+// Wave layout.  B given N x K: 4 (M) x 2 (N) waves, wave (wm, wn) owning rows
+// 32wm.. of every A half and columns 64wn.. of every B half.  B given K x N:
+// 2 x 4, rows 64wm.. and columns 32wn..: a B fragment of 16 columns then
+// takes two transposing 8-byte reads against one 16-byte read for A, and this
+// layout issues 16 + 16 LDS reads per wave per K-step where 4 x 2 issues
+// 8 + 32 (measured on 16384x2048x8192: the 4 x 2 layout spent 30 % more
+// wave-cycles waiting to issue LDS instructions per FLOP than B given N x K).
+template <bool kTransB>
+struct WaveLayout {
+    static constexpr int kWM = kTransB ? 4 : 2;     // waves along M
+    static constexpr int kRows = 128 / kWM;         // rows of each A half per wave
+    static constexpr int kCols = 128 * kWM / 8;     // columns of each B half per wave
+    static constexpr int kMT = kRows / 16, kNT = kCols / 16;
+    static constexpr int kShift = kWM == 4 ? 2 : 1;  // wave >> kShift = wn
+};
+
 // Per-wave state of the 8-wave kernel: the shared copy loader plus this
 // wave's fragment read offsets.
 template <int kElem, bool kTransB, bool kOutF32, bool kOffset>
 struct Pipeline : Loader<kElem, kTransB, 8> {
     using Loader<kElem, kTransB, 8>::lds0;
+    using L = WaveLayout<kTransB>;
     FragOffsets fa, fb;
 
     __device__ __forceinline__ Pipeline(const GemmParams &prm, int tm, int tn)
         : Loader<kElem, kTransB, 8>(prm, tm, tn) {
         const int lane = threadIdx.x & 63;
-        const int wm = this->wave & 3, wn = this->wave >> 2;
-        fa.rows(32 * wm, lane);
+        const int wm = this->wave & (L::kWM - 1), wn = this->wave >> L::kShift;
+        fa.rows(L::kRows * wm, lane);
         if constexpr (kTransB)
-            fb.rows(64 * wn, lane);
+            fb.rows(L::kCols * wn, lane);
         else
-            fb.cols_tr(64 * wn, lane);
+            fb.cols_tr(L::kCols * wn, lane);
     }
 
-    __device__ __forceinline__ void read_a(i32x4 (&a)[2][2], uint32_t buf, int h) const {
+    __device__ __forceinline__ void read_a(i32x4 (&a)[L::kMT][2], uint32_t buf, int h) const {
         const uint32_t base = lds0 + buf + kOffA + h * kHalf;
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < L::kMT; ++mt)
             for (int ks = 0; ks < 2; ++ks)
                 a[mt][ks] = lds_read128(base + fa.row[ks] + mt * 2048);
     }
 
-    __device__ __forceinline__ void read_b(i32x4 (&b)[4][2], uint32_t buf, int h) const {
+    __device__ __forceinline__ void read_b(i32x4 (&b)[L::kNT][2], uint32_t buf, int h) const {
         const uint32_t base = lds0 + buf + kOffB + h * kHalf;
         if constexpr (kTransB) {
-            for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < L::kNT; ++nt)
                 for (int ks = 0; ks < 2; ++ks)
                     b[nt][ks] = lds_read128(base + fb.row[ks] + nt * 2048);
         } else {
-            for (int nt = 0; nt < 4; ++nt)
+            for (int nt = 0; nt < L::kNT; ++nt)
                 for (int ks = 0; ks < 2; ++ks) {
                     const i32x2 lo = lds_read64_tr(base + fb.tr[nt] + (32 * ks + 0) * 256);
                     const i32x2 hi = lds_read64_tr(base + fb.tr[nt] + (32 * ks + 4) * 256);
@@ -120,17 +139,17 @@ struct Pipeline : Loader<kElem, kTransB, 8> {
 
 // One quadrant's MFMAs over the K-step: two 16x16x32 k-slices for 16-bit
 // operands, or one 16x16x128 FP8 MFMA over both chunks.
-template <int kElem>
-__device__ __forceinline__ void quadrant(f32x4 (&acc)[2][4], const i32x4 (&a)[2][2],
-                                         const i32x4 (&b)[4][2]) {
+template <int kElem, int kMT, int kNT>
+__device__ __forceinline__ void quadrant(f32x4 (&acc)[kMT][kNT], const i32x4 (&a)[kMT][2],
+                                         const i32x4 (&b)[kNT][2]) {
     if constexpr (kElem == kElemFP8) {
-        for (int mt = 0; mt < 2; ++mt)
-            for (int nt = 0; nt < 4; ++nt)
+        for (int mt = 0; mt < kMT; ++mt)
+            for (int nt = 0; nt < kNT; ++nt)
                 acc[mt][nt] = mfma_fp8(b[nt][0], b[nt][1], a[mt][0], a[mt][1], acc[mt][nt]);
     } else {
         for (int ks = 0; ks < 2; ++ks)
-            for (int mt = 0; mt < 2; ++mt)
-                for (int nt = 0; nt < 4; ++nt)
+            for (int mt = 0; mt < kMT; ++mt)
+                for (int nt = 0; nt < kNT; ++nt)
                     acc[mt][nt] = mfma<kElem>(b[nt][ks], a[mt][ks], acc[mt][nt]);
     }
 }
@@ -162,13 +181,14 @@ gemm_pipelined_kernel(GemmParams pin) {
     stagger_poison_lds<2 * kBuf, kPipeThreads>(pl.lds0);
     const int wave = pl.wave;
 
-    f32x4 acc[2][2][2][4];
+    using L = WaveLayout<kTransB>;
+    f32x4 acc[2][2][L::kMT][L::kNT];
     for (int qa = 0; qa < 2; ++qa)
         for (int qb = 0; qb < 2; ++qb)
-            for (int mt = 0; mt < 2; ++mt)
-                for (int nt = 0; nt < 4; ++nt)
+            for (int mt = 0; mt < L::kMT; ++mt)
+                for (int nt = 0; nt < L::kNT; ++nt)
                     acc[qa][qb][mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    i32x4 a0[2][2], a1[2][2], b0[4][2], b1[4][2];
+    i32x4 a0[L::kMT][2], a1[L::kMT][2], b0[L::kNT][2], b1[L::kNT][2];
 
     // ---- prologue: the copy stream of steps 0 and 1 in steady-state order
     // (a0 a1 b0, then b1, per step), then the fragments S0 of step 0 needs.
@@ -237,13 +257,14 @@ gemm_pipelined_kernel(GemmParams pin) {
     // ---- epilogue.  The lane id is recomputed here so no lane-derived value
     // stays live across the loop.
     const int lane = __lane_id();
-    const int wm = wave & 3, wn = wave >> 2;
+    const int wm = wave & (L::kWM - 1), wn = wave >> L::kShift;
     for (int qa = 0; qa < 2; ++qa)
-        for (int mt = 0; mt < 2; ++mt) {
-            const int row = pl.win.m0 + 128 * qa + 32 * wm + 16 * mt + (lane & 15);
+        for (int mt = 0; mt < L::kMT; ++mt) {
+            const int row = pl.win.m0 + 128 * qa + L::kRows * wm + 16 * mt + (lane & 15);
             if (row >= p.M) continue;
             for (int qb = 0; qb < 2; ++qb)
-                store_strip<kElem != kElemF16, kOutF32>(p, acc[qa][qb][mt], row, pl.win.n0 + 128 * qb + 64 * wn, lane);
+                store_strip<kElem != kElemF16, kOutF32>(p, acc[qa][qb][mt], row,
+                                                        pl.win.n0 + 128 * qb + L::kCols * wn, lane);
         }
 }
 
