@@ -504,7 +504,13 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int wg, int &tm
 // l & 15.  FP32 output stores those four values (16 bytes).  For a 16-bit
 // output (FP16, or BF16 with kBF16; round to nearest even), lanes l and l^16
 // trade halves of tiles nt and nt+1 so every lane stores eight consecutive
-// columns (16 bytes).  Columns at or past N are not written.
+// columns (16 bytes).  The trade is two v_permlane16_swap (gfx950), which swap
+// the odd 16-lane rows of their first operand with the even rows of their
+// second: with tile nt's packed values as the first operand and tile nt+1's
+// as the second, an even lane group ends up holding its own four columns of
+// tile nt followed by its partner's, and an odd group its partner's four
+// columns of tile nt+1 followed by its own, with no LDS round trip.  Columns
+// at or past N are not written.
 template <bool kBF16, bool kOutF32, int kN>
 __device__ __forceinline__ void store_strip(const GemmParams &p, const f32x4 (&v4)[kN], int row,
                                             int col0, int lane) {
@@ -534,12 +540,10 @@ __device__ __forceinline__ void store_strip(const GemmParams &p, const f32x4 (&v
                 h1 = __builtin_bit_cast(i32x2, __builtin_convertvector(v4[nt + 1], f16x4));
             }
             const bool odd = g & 1;
-            const i32x2 send = odd ? h0 : h1;
-            i32x2 recv;
-            recv.x = __shfl_xor(send.x, 16);
-            recv.y = __shfl_xor(send.y, 16);
-            const i32x4 out = odd ? i32x4{recv.x, recv.y, h1.x, h1.y}
-                                  : i32x4{h0.x, h0.y, recv.x, recv.y};
+            const auto sx = __builtin_amdgcn_permlane16_swap(h0.x, h1.x, false, false);
+            const auto sy = __builtin_amdgcn_permlane16_swap(h0.y, h1.y, false, false);
+            const i32x4 out = {static_cast<int>(sx[0]), static_cast<int>(sy[0]), static_cast<int>(sx[1]),
+                               static_cast<int>(sy[1])};
             const int col = col0 + 16 * nt + (odd ? 16 + 4 * (g - 1) : 4 * g);
             uint16_t *c = reinterpret_cast<uint16_t *>(p.C) + (int64_t)row * p.ldc + col;
             if (col + 8 <= p.N) {
