@@ -155,6 +155,9 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t num_record
 // reads 0).  Issued from inline assembly so the compiler neither reorders it
 // nor adds waits of its own: the schedule's explicit vmcnt waits cover it.
 // M0 (the LDS destination) needs one wait state before the load reads it.
+// The compiler treats M0 as reserved and may not honour the clobber; these
+// kernels leave M0 to this asm alone (no compiler-generated instruction
+// touches it, checked in the ISA).
 template <uint32_t kOff>
 __device__ __forceinline__ void copy16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
     // Both values are wave-uniform by construction; readfirstlane states it so

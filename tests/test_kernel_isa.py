@@ -136,3 +136,22 @@ def test_no_scratch_anywhere(asm, kernel):
     sizes = re.findall(r"\.private_segment_fixed_size:\s+(\d+)", asm[kernel])
     assert sizes and all(int(x) == 0 for x in sizes), sizes
     assert not re.findall(r"\.vgpr_spill_count:\s+[1-9]", asm[kernel])
+
+
+@pytest.mark.parametrize("kernel", sorted(EXPECT))
+def test_m0_only_in_the_copy_asm(asm, kernel):
+    """The copies set M0 (the LDS destination of buffer_load ... lds) inside
+    their inline assembly.  The compiler treats M0 as reserved and may ignore
+    the clobber, so no compiler-generated instruction may read or write M0:
+    every mention of m0 must sit between ASMSTART and ASMEND."""
+    inside, stray = False, []
+    for line in asm[kernel].splitlines():
+        t = line.strip()
+        if t.startswith(";;#ASMSTART"):
+            inside = True
+        elif t.startswith(";;#ASMEND"):
+            inside = False
+        elif not inside and not t.startswith(";") and re.search(r"\bm0\b", t):
+            stray.append(t)
+    assert not stray, stray[:5]
+
