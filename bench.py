@@ -52,7 +52,8 @@ MALL_BYTES = 256 * 2 ** 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def counter_record(workload: str, schedule: str):
     """The committed counter record (profiles/traffic.json) of this kernel on
-    this workload, if it was taken on the kernel's current source; else None."""
+    this workload, if it was taken on the kernel's current code (the
+    comment-free text of its sources); else None."""
     from matrix_core_scheduling_amd import profiling
 
     kernel = schedule
@@ -63,7 +64,7 @@ def counter_record(workload: str, schedule: str):
             t = json.load(f).get(profiling.traffic_key(workload, kernel))
     except (OSError, ValueError):
         return None
-    if not t or t.get("kernel_source_sha256") != profiling.kernel_source_hash(kernel):
+    if not t or t.get("kernel_code_sha256") != profiling.kernel_code_hash(kernel):
         return None
     return t
 

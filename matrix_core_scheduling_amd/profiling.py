@@ -106,11 +106,37 @@ def derived(c: dict, n_xcc: int, simds: int) -> dict:
     return out
 
 
-def kernel_source_hash(schedule: str = "pipelined") -> str:
+def code_text(src: str) -> str:
+    """C++ source with comments removed and every run of whitespace made one
+    space: what the compiler sees, so editing a comment keeps the hash."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_code_hash(schedule: str = "pipelined") -> str:
+    """SHA-256 of the comment-free code of the sources a timed kernel is built from."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[schedule]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 
@@ -137,7 +163,7 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, sche
     r = {"fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
          "hbm_bytes_per_launch": round(fetch + write), "fetch_scale": round(f_scale, 5),
          "write_scale": round(w_scale, 5), "copy_calibration_mib": copy_mib,
-         "kernel_source_sha256": kernel_source_hash(schedule)}
+         "kernel_code_sha256": kernel_code_hash(schedule)}
     if busy_dir:
         ag = agent(busy_dir)
         cs = next(iter(counters([busy_dir], kernel).values()))
