@@ -155,3 +155,21 @@ def test_m0_only_in_the_copy_asm(asm, kernel):
             stray.append(t)
     assert not stray, stray[:5]
 
+
+
+def test_pipelined_lds_reads_per_layout(asm):
+    """LDS reads per two K-steps of the 8-wave kernel: with B given N x K (4 x 2
+    waves) 48 ds_read_b128; with B given K x N (2 x 4 waves) 32 ds_read_b128
+    for A and 32 transposing ds_read_b64_tr_b16 for B -- 64 reads where the
+    4 x 2 layout would issue 16 + 64."""
+    seen = set()
+    for (fn, hdr), ops in loops(asm["gemm_pipelined_kernel"]).items():
+        if "gemm_pipelined_kernel" not in fn:
+            continue
+        m = re.search(r"kernelILi(\d)ELb(\d)E", fn)
+        elem, trans_b = int(m.group(1)), int(m.group(2))
+        b128, tr = ops.count("ds_read_b128"), ops.count("ds_read_b64_tr_b16")
+        want = (48, 0) if trans_b else (32, 32)
+        assert (b128, tr) == want, f"{fn}: {b128} b128 + {tr} tr reads, want {want}"
+        seen.add(trans_b)
+    assert seen == {0, 1}
