@@ -166,7 +166,8 @@ int gemm_auto_schedule(int64_t M, int64_t N);
  *              (no workspace needed)
  * Returns GEMM_EINVAL for a missing, misaligned or too small workspace, for
  * schedule GENERIC, or for an explicit schedule the operands do not allow
- * (with AUTO, such operands run gemm_ex's generic kernel unsplit).
+ * (with AUTO, such operands run gemm_ex's generic kernel unsplit), and
+ * GEMM_EUNSUPPORTED when the workspace size does not fit in int64_t.
  */
 int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K,
                    const void *A, int64_t lda,
@@ -176,7 +177,9 @@ int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K,
                    hipStream_t stream);
 
 /* Workspace bytes gemm_ex_splitk needs for these sizes and splits (0 when it
- * would not split).  Returns a gemm_status. */
+ * would not split).  Returns a gemm_status: GEMM_EINVAL for a null `bytes`,
+ * negative sizes or splits outside 1 .. 256, GEMM_EUNSUPPORTED for a size
+ * that does not fit in int64_t. */
 int gemm_splitk_workspace_bytes(int dtype, int64_t M, int64_t N, int64_t K, int splits,
                                 int64_t *bytes);
 

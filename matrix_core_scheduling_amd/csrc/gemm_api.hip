@@ -117,6 +117,14 @@ void split_plan(int elem, int64_t K, int splits, int64_t &kslice, int &slices) {
 
 int64_t ws_row(int64_t N) { return (N + 3) / 4 * 4; }
 
+// Bytes of `slices` FP32 partial products of M rows of ws_row(N) floats, or
+// -1 where that count does not fit in int64_t (M and N up to 2^31 - 1).
+int64_t ws_bytes(int64_t slices, int64_t M, int64_t N) {
+    const int64_t row = ws_row(N) * 4;
+    if (M > INT64_MAX / row / slices) return -1;
+    return slices * M * row;
+}
+
 // The tiled kernel AUTO runs for aligned operands: the 256x256 warp-pipelined
 // kernel, or the 128x128-tile kernel when the product has fewer 256x256 tiles
 // than half of MI355X's 256 compute units (measured: 1024^3 22.1 -> 10.6 us,
@@ -181,7 +189,9 @@ extern "C" int gemm_splitk_workspace_bytes(int dtype, int64_t M, int64_t N, int6
     int64_t kslice = 0;
     int slices = 1;
     if (K > 0) split_plan(elem_of(dtype), K, splits, kslice, slices);
-    *bytes = slices > 1 ? static_cast<int64_t>(slices) * M * ws_row(N) * 4 : 0;
+    const int64_t need = slices > 1 && M > 0 && N > 0 ? ws_bytes(slices, M, N) : 0;
+    if (need < 0) return GEMM_EUNSUPPORTED;
+    *bytes = need;
     return GEMM_OK;
 }
 
@@ -219,7 +229,8 @@ extern "C" int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K, const 
     if (!fast) return schedule == GEMM_SCHED_AUTO
         ? gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream)
         : GEMM_EINVAL;
-    const int64_t need = static_cast<int64_t>(slices) * M * ws_row(N) * 4;
+    const int64_t need = ws_bytes(slices, M, N);
+    if (need < 0) return GEMM_EUNSUPPORTED;
     if (!workspace || !aligned16(workspace) || workspace_bytes < need) return GEMM_EINVAL;
     if (schedule == GEMM_SCHED_AUTO) schedule = auto_tiled_schedule(M, N);
 

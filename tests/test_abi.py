@@ -132,6 +132,12 @@ def test_splitk_workspace_size(lib):
     assert mcs.gemm_splitk_workspace_bytes(fp8, 256, 256, 1024, 4) == 4 * 256 * 256 * 4
     with pytest.raises(mcs.GemmError):
         mcs.gemm_splitk_workspace_bytes(f16, 64, 64, 64, 0)
+    # 4 x (2^31 - 1) x (2^31 - 8) x 4 bytes does not fit in int64_t
+    big = 2 ** 31 - 8
+    with pytest.raises(mcs.GemmError) as e:
+        mcs.gemm_splitk_workspace_bytes(f16, big + 7, big, 2 ** 20, 4)
+    assert e.value.status == mcs.GEMM_EUNSUPPORTED
+    assert mcs.gemm_splitk_workspace_bytes(f16, 2 ** 20, 2 ** 20, 2 ** 20, 4) == 2 ** 44
 
 
 def test_splitk_validation_before_launch(lib):
@@ -147,6 +153,10 @@ def test_splitk_validation_before_launch(lib):
     bad = (1024, 1024, 1024, P + 2, 1024, P, 1024, 1, P, 1024, 0)                      # unaligned A
     assert sk(0, *bad, mcs.GEMM_SCHED_PIPELINED, 4, P, need, 0) == mcs.GEMM_EINVAL
     assert sk(0, 0, 8, 8, 0, 8, 0, 8, 1, 0, 8, 0, mcs.GEMM_SCHED_AUTO, 4, 0, 0, 0) == mcs.GEMM_OK  # empty
+    # a workspace size that overflows int64_t is refused, whatever workspace_bytes claims
+    big = 2 ** 31 - 8
+    huge = (big + 7, big, 2 ** 20, P, 2 ** 20, P, 2 ** 20, 1, P, big, 0)
+    assert sk(0, *huge, mcs.GEMM_SCHED_PIPELINED, 4, P, 2 ** 62, 0) == mcs.GEMM_EUNSUPPORTED
 
 
 def test_auto_schedule(lib):
