@@ -433,6 +433,7 @@ int attention_launch(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return GEMM_EINVAL;
     // row indices and per-head element offsets stay below 2^31
     if (seq_q >= (int64_t(1) << 23) || seq_k >= (int64_t(1) << 23)) return GEMM_EUNSUPPORTED;
+    if (batch > 0x7FFFFFFF || heads > 0x7FFFFFFF) return GEMM_EUNSUPPORTED;   // batch * heads fits int64_t
     const int64_t groups = batch * heads;
     const int64_t nq = (seq_q + kQRows - 1) / kQRows;
     if (groups > 0x7FFFFFFF || nq * groups > 0x7FFFFFFF) return GEMM_EUNSUPPORTED;

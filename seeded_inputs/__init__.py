@@ -233,7 +233,8 @@ class Workload:
 # MI355X figures are quoted on, an 8192^3 BF16 case, a tall-skinny
 # 16384x2048x8192 case with FP32 output, the 8192^3 FP8 E4M3 shape (B given
 # N x K, normally distributed values) an MI355X FP8 figure is quoted on, and
-# one GPU's row block (512x4096x8192) of an 8-way row split of the FP16 shape.
+# one GPU's row block (512x4096x8192) of an 8-way row split of the FP16 shape,
+# and the FP16 shape at twice the K (4096x4096x16384), the second MI355X point.
 WORKLOADS = {
     "f16_256": Workload("f16_256", "f16", 256, 256, 256, 0, "uniform", "same", 1001),
     "f16_1024_bt": Workload("f16_1024_bt", "f16", 1024, 1024, 1024, 1, "normal_scaled", "same", 1002),
@@ -243,6 +244,7 @@ WORKLOADS = {
                                            "uniform", "f32", 1005),
     "fp8_8192": Workload("fp8_8192", "fp8", 8192, 8192, 8192, 1, "normal", "bf16", 1006),
     "f16_512x4096x8192": Workload("f16_512x4096x8192", "f16", 512, 4096, 8192, 1, "uniform", "same", 1007),
+    "f16_4096x4096x16384": Workload("f16_4096x4096x16384", "f16", 4096, 4096, 16384, 1, "uniform", "same", 1008),
 }
 HEADLINE = "f16_4096x4096x8192"
 

@@ -210,6 +210,8 @@ def test_attention_argument_errors(lib):
     assert call(V=0) == mcs.GEMM_EINVAL
     assert call(lse=P + 2) == mcs.GEMM_EINVAL
     assert call(seq_q=1 << 23) == mcs.GEMM_EUNSUPPORTED
+    assert call(batch=1 << 40, heads=1 << 40) == mcs.GEMM_EUNSUPPORTED      # batch * heads would overflow
+    assert call(batch=1 << 20, heads=1 << 12) == mcs.GEMM_EUNSUPPORTED      # 2^32 workgroup rows
     # empty problems enqueue nothing
     assert call(batch=0, Q=0, K=0, V=0, O=0) == mcs.GEMM_OK
     assert call(seq_q=0, Q=0, K=0, V=0, O=0) == mcs.GEMM_OK
