@@ -138,19 +138,25 @@ struct Pipeline : Loader<kElem, kTransB, 8> {
 };
 
 // One quadrant's MFMAs over the K-step: two 16x16x32 k-slices for 16-bit
-// operands, or one 16x16x128 FP8 MFMA over both chunks.
+// operands, or one 16x16x128 FP8 MFMA over both chunks.  The tiles go in a
+// snake (columns forward on even rows of tiles, backward on odd ones), so
+// within a k-slice consecutive MFMAs differ in one operand only.
 template <int kElem, int kMT, int kNT>
 __device__ __forceinline__ void quadrant(f32x4 (&acc)[kMT][kNT], const i32x4 (&a)[kMT][2],
                                          const i32x4 (&b)[kNT][2]) {
     if constexpr (kElem == kElemFP8) {
         for (int mt = 0; mt < kMT; ++mt)
-            for (int nt = 0; nt < kNT; ++nt)
+            for (int j = 0; j < kNT; ++j) {
+                const int nt = mt & 1 ? kNT - 1 - j : j;
                 acc[mt][nt] = mfma_fp8(b[nt][0], b[nt][1], a[mt][0], a[mt][1], acc[mt][nt]);
+            }
     } else {
         for (int ks = 0; ks < 2; ++ks)
             for (int mt = 0; mt < kMT; ++mt)
-                for (int nt = 0; nt < kNT; ++nt)
+                for (int j = 0; j < kNT; ++j) {
+                    const int nt = mt & 1 ? kNT - 1 - j : j;
                     acc[mt][nt] = mfma<kElem>(b[nt][ks], a[mt][ks], acc[mt][nt]);
+                }
     }
 }
 
