@@ -179,6 +179,15 @@ def _stream_handle(stream):
     return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
 
 
+def _same_gpu(*tensors):
+    """The kernels dereference every pointer on the GPU: host tensors, or
+    tensors on different devices, are refused before any library call."""
+    dev = tensors[0].device
+    for t in tensors:
+        if not t.is_cuda or t.device != dev:
+            raise ValueError(f"all tensors must be on one GPU device (got {t.device} and {dev})")
+
+
 def gemm(A, B, trans_b: bool = False, out=None, out_dtype=None,
          schedule: int = GEMM_SCHED_AUTO, stream=None):
     """C = A @ B (trans_b=False, B is K x N) or A @ B.T (trans_b=True, B is N x K).
@@ -197,6 +206,7 @@ def gemm(A, B, trans_b: bool = False, out=None, out_dtype=None,
         raise TypeError("A and B must both be float16, bfloat16 or float8_e4m3fn")
     if A.dim() != 2 or B.dim() != 2:
         raise ValueError("A and B must be 2-D")
+    _same_gpu(A, B)
     if A.stride(1) != 1 or B.stride(1) != 1:
         raise ValueError("A and B need unit column stride")
     M, K = A.shape
@@ -211,6 +221,7 @@ def gemm(A, B, trans_b: bool = False, out=None, out_dtype=None,
         out = torch.empty((M, N), dtype=out_dtype or (torch.bfloat16 if fp8 else A.dtype), device=A.device)
     if out.shape != (M, N) or (out.stride(1) != 1 and N > 1):
         raise ValueError("out must be M x N with unit column stride")
+    _same_gpu(A, out)
     if out.dtype == torch.float32:
         out_type = GEMM_OUT_F32
     elif out.dtype == torch.bfloat16 and A.dtype != torch.float16:
@@ -254,14 +265,20 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
         raise ValueError("q (B,H,Sq,D), k and v (B,H,Sk,D) expected")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k and v must be contiguous")
+    _same_gpu(q, k, v)
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     out = torch.empty_like(q) if out is None else out
     if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
+    _same_gpu(q, out)
     if with_lse and lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.numel() != B * H * Sq or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 tensor of B*H*Sq elements")
+        _same_gpu(q, lse)
     st = attention_fwd(dtypes[q.dtype], B, H, Sq, Sk, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                        out.data_ptr(), lse.data_ptr() if lse is not None else None, scale, int(bool(causal)),
                        _stream_handle(stream))

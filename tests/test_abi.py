@@ -112,6 +112,18 @@ def test_pipelined_schedule_refuses_unaligned_operands(lib):
     assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_TILE128, 0) == mcs.GEMM_EINVAL
 
 
+def test_torch_wrappers_refuse_host_tensors(lib):
+    """A host tensor's pointer would be dereferenced by the GPU: refused before
+    any library call."""
+    torch = pytest.importorskip("torch")
+    a = torch.zeros((64, 64), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        mcs.gemm(a, a, trans_b=True)
+    q = torch.zeros((1, 1, 16, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        mcs.attention(q, q, q)
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(mcs, "_lib", None)
     with pytest.raises(RuntimeError, match="no non-HIP fallback"):
