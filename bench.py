@@ -10,9 +10,13 @@ launch; the other workloads include 8192^3 BF16, 8192^3 FP8 E4M3 and the
 launches per step), on inputs already resident in HBM.  Inputs are seeded synthetic matrices (A and
 B uniform in [-1, 1), B given N x K); enough rotating input sets are kept on
 the device that one pass over them exceeds the 256 MB last-level cache, and
-consecutive steps use consecutive sets.  Warm-up launches are untimed; the K
-timed launches are bracketed by device synchronisation and timed with HIP
-events on the stream they are enqueued on.  Throughput = 2MNK / time.
+consecutive steps use consecutive sets.  Before the W warm-up launches the
+GPU runs untimed launches until its clock has settled (at least --settle-ms of
+GPU time, then until the per-launch time stops falling; reported as settle_ms
+and settle_launches), so the K timed launches measure the sustained rate
+however small K and W are.  The K timed launches are bracketed by device
+synchronisation and timed with HIP events on the stream they are enqueued on.
+Throughput = 2MNK / time.
 
 The CPU baseline runs the oracle (a plain binary64 triple loop) on a bounded
 block of output rows of the same workload, on the host's cores, and the GPU
@@ -117,6 +121,46 @@ def copy_calibration(mib: int) -> int:
     return 0
 
 
+def settle(launch, stream, min_ms: float, max_ms: float):
+    """Untimed launches until the GPU clock has settled, whatever --warmup asks.
+
+    A GPU that sat idle (while the host generated the inputs) starts at
+    another clock than the one it holds under sustained load: the first tens
+    of milliseconds of launches run up to ~25 % slow.  Launches go in chunks
+    of about 20 ms of GPU time, each timed with HIP events on the launch
+    stream; settling ends once at least ``min_ms`` of GPU time has run and
+    the latest chunk's per-launch time is no more than 0.5 % below the best
+    earlier chunk (the time has stopped falling), or after ``max_ms``.
+    Returns (GPU milliseconds, launches, per-launch ms of the last chunk)."""
+    import torch
+
+    if max_ms <= 0:
+        return 0.0, 0, None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(4):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total, n = e0.elapsed_time(e1), 4
+    per = max(1, int(math.ceil(20.0 / max(total / 4, 1e-3))))
+    best = last = None
+    while total < max_ms:
+        e0.record(stream)
+        for i in range(per):
+            launch(n + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        total += ms
+        n += per
+        last = ms / per
+        if best is not None and total >= min_ms and last >= 0.995 * best:
+            break
+        best = last if best is None else min(best, last)
+    return total, n, last
+
+
 def bench_attention(a, w) -> int:
     """One attention_fwd launch per step over the whole (B, H) batch."""
     import numpy as np
@@ -157,7 +201,9 @@ def bench_attention(a, w) -> int:
         if st != mcs.GEMM_OK:
             raise mcs.GemmError(st, "attention_fwd")
 
-    print(f"[bench] warm-up {a.warmup}", file=sys.stderr, flush=True)
+    settle_ms, settle_n, settle_last = settle(launch, stream, a.settle_ms, a.settle_max_ms)
+    print(f"[bench] settled: {settle_n} launches, {settle_ms:.1f} ms of GPU time; warm-up {a.warmup}",
+          file=sys.stderr, flush=True)
     for i in range(a.warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -240,6 +286,9 @@ def bench_attention(a, w) -> int:
                    "schedule": "in_phase" if sched == mcs.GEMM_SCHED_IN_PHASE else "pipelined"},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "wall_s_timed": round(wall, 4),
+        "settle_ms": round(settle_ms, 2),
+        "settle_launches": settle_n,
+        "settled_ms_per_launch": None if settle_last is None else round(settle_last, 6),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic,
                      "mfma_busy": mfma_busy_for(w.name, "attention")},
@@ -262,6 +311,10 @@ def main(argv=None) -> int:
     ap.add_argument("--schedule", default="auto", choices=["auto", "pipelined", "in_phase", "interleaved", "tile128", "generic"])
     ap.add_argument("--splits", default="auto",
                     help="K-slices (gemm_ex_splitk) or 'auto' (gemm_splitk_suggest; 1 for the default shape)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed GPU time run before the warm-up, whatever --warmup says (clock settling)")
+    ap.add_argument("--settle-max-ms", type=float, default=3000.0,
+                    help="upper bound of the settling period (0 disables it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -348,7 +401,9 @@ def main(argv=None) -> int:
         if st != mcs.GEMM_OK:
             raise mcs.GemmError(st, "launch")
 
-    print(f"[bench] warm-up {a.warmup}", file=sys.stderr, flush=True)
+    settle_ms, settle_n, settle_last = settle(launch, stream, a.settle_ms, a.settle_max_ms)
+    print(f"[bench] settled: {settle_n} launches, {settle_ms:.1f} ms of GPU time; warm-up {a.warmup}",
+          file=sys.stderr, flush=True)
     for i in range(a.warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -451,6 +506,9 @@ def main(argv=None) -> int:
         "pct_of_unit_peak": round(100.0 * tflops / PEAK_TFLOPS_UNITS[w.dtype], 2),
         "batch_median_ms": round(batch_med, 6),
         "wall_s_timed": round(wall, 4),
+        "settle_ms": round(settle_ms, 2),
+        "settle_launches": settle_n,
+        "settled_ms_per_launch": None if settle_last is None else round(settle_last, 6),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
                      "mfma_busy": mfma_busy_for(w.name, eff)},

@@ -50,7 +50,8 @@ extern "C" {
  *   scale      the score scale, finite and > 0 (usually 1/sqrt(head_dim))
  *   causal     0 or 1
  * Returns GEMM_OK; GEMM_EINVAL for a bad type, flag, scale, negative size,
- * a null or misaligned pointer where data is needed; GEMM_EUNSUPPORTED for
+ * a null pointer where data is needed; GEMM_EALIGN for Q, K, V or O not
+ * 16-byte aligned or lse not 4-byte aligned; GEMM_EUNSUPPORTED for
  * another head_dim or sizes whose element counts reach 2^31 per head (or
  * more than 2^31-1 workgroups); GEMM_EHIP if the launch fails.  Empty
  * problems (batch, heads or seq_q zero) enqueue nothing; seq_k == 0 writes

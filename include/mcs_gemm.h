@@ -6,9 +6,9 @@
  *                      operands) or FP32 output.
  *
  * The operation is the tiled dense product of "Two Waves, One Stage Apart:
- * Warp-Pipelining Triton GEMMs on AMD Instinct" (opening section: a tiled
- * GEMM computes on one pair of operand tiles while it prepares the next;
- * throughput is counted as 2MNK / elapsed time, Table 1).  The kernel holds
+ * Warp-Pipelining Triton GEMMs on AMD Instinct" (opening section: the loop
+ * overlaps the matrix work on the current K-step with fetching the operands
+ * of later ones; throughput is 2MNK / elapsed time, Table 1).  The kernel holds
  * two wave groups one stage apart (sections "Two Waves, One Stage Apart",
  * "Creating and Closing the Offset", "MI350 Series (gfx950, CDNA 4): Three
  * Overlapping Flows"); its buffer-resource loads with out-of-range reads
@@ -34,12 +34,20 @@
  * Errors are reported before anything is enqueued (nothing runs on error):
  *   GEMM_EINVAL       null pointer where data is needed, negative size,
  *                     leading dimension below its minimum, bad flag value;
- *   GEMM_EUNSUPPORTED a size the kernels cannot index (any dimension or
- *                     leading dimension >= 2^31, or more than 2^31-1 tiles);
+ *   GEMM_EALIGN       A, B or C not 16-byte aligned, lda or ldb times the
+ *                     element size not a multiple of 16 bytes, or ldc not a
+ *                     multiple of 8 elements (the MFMA kernels move 16 bytes
+ *                     per lane);
+ *   GEMM_EUNSUPPORTED a shape the MFMA kernels do not cover: K times the
+ *                     element size not a multiple of 16 bytes, an odd N with
+ *                     B given K x N, FP8 with B given K x N, rows of A or B
+ *                     of 2^24 bytes or more; or a size they cannot index
+ *                     (any dimension or leading dimension >= 2^31, or more
+ *                     than 2^31-1 tiles);
  *   GEMM_EHIP         the launch itself failed (hipGetLastError() holds it).
- * Alignment is never an error: operands that are not 16-byte aligned (or
- * leading dimensions / K that are not multiples of 8) take a slower generic
- * GPU kernel instead of the pipelined one.
+ * gemm_f16, gemm_bf16 and gemm_fp8 only ever run the MFMA kernels.  A plain
+ * FMA kernel that takes any alignment and shape is available, on request
+ * only, as gemm_ex(..., GEMM_SCHED_GENERIC, ...).
  */
 #ifndef MCS_GEMM_H
 #define MCS_GEMM_H
@@ -54,6 +62,7 @@ extern "C" {
 enum gemm_status {
     GEMM_OK = 0,
     GEMM_EINVAL = -1,
+    GEMM_EALIGN = -2,
     GEMM_EUNSUPPORTED = -3,
     GEMM_EHIP = -4
 };
@@ -73,14 +82,14 @@ enum gemm_dtype {
 /* Kernel schedule selector for gemm_ex. */
 enum gemm_schedule {
     GEMM_SCHED_AUTO = 0,       /* what gemm_f16 / gemm_bf16 / gemm_fp8 use:
-                                  when the operands allow it PIPELINED, or
-                                  TILE128 for products with fewer than 128
-                                  output tiles of 256x256
-                                  (gemm_auto_schedule); else GENERIC */
+                                  PIPELINED, or TILE128 for products with
+                                  fewer than 128 output tiles of 256x256
+                                  (gemm_auto_schedule) */
     GEMM_SCHED_PIPELINED = 1,  /* 8 waves, two groups held one stage apart */
     GEMM_SCHED_IN_PHASE = 2,   /* same kernel and stages, groups kept in phase
                                   (no entry/exit offset): the ablation baseline */
-    GEMM_SCHED_GENERIC = 3,    /* plain LDS-tiled FMA kernel, any alignment */
+    GEMM_SCHED_GENERIC = 3,    /* plain LDS-tiled FMA kernel, no MFMA: any
+                                  alignment and shape, on request only */
     GEMM_SCHED_INTERLEAVED = 4, /* 4 waves, one per SIMD, each interleaving its
                                   own MFMA, LDS reads and copies ("Porting
                                   High-Performance HIP Kernels to FlyDSL",
@@ -102,7 +111,8 @@ enum gemm_schedule {
  *   C          device pointer, M x N result, row stride ldc >= max(N, 1);
  *              element type set by out_type (gemm_out_type)
  *   stream     HIP stream the kernel is enqueued on
- * Returns a gemm_status.
+ * Returns a gemm_status (GEMM_EALIGN / GEMM_EUNSUPPORTED for operands the
+ * MFMA kernels cannot take, see above).
  */
 int gemm_f16(int64_t M, int64_t N, int64_t K,
              const void *A, int64_t lda,
@@ -120,8 +130,9 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
  * gemm_fp8 -- C = A . B with FP8 E4M3 operands (one byte per element, leading
  * dimensions in elements), FP32 accumulation; out_type GEMM_OUT_BF16 or
  * GEMM_OUT_F32 (GEMM_OUT_SAME is GEMM_EINVAL).  Other arguments as gemm_f16.
- * The fast kernels take B given N x K (trans_b = 1); B given K x N runs the
- * generic kernel.  NaN operands (0x7F, 0xFF) propagate.
+ * The MFMA kernels take B given N x K (trans_b = 1) only; B given K x N is
+ * GEMM_EUNSUPPORTED here (gemm_ex with GEMM_SCHED_GENERIC takes it).  NaN
+ * operands (0x7F, 0xFF) propagate.
  */
 int gemm_fp8(int64_t M, int64_t N, int64_t K,
              const void *A, int64_t lda,
@@ -131,12 +142,10 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K,
 
 /*
  * gemm_ex -- the same product with the operand type (gemm_dtype) and the
- * kernel schedule (gemm_schedule) chosen by the caller.  PIPELINED,
- * IN_PHASE, INTERLEAVED and TILE128 need 16-byte aligned A, B, C, rows of A and B
- * (lda, ldb times the element size) and of K elements that are whole 16-byte
- * chunks, ldc a multiple of 8, and an even N when B is K x N (FP8: B given
- * N x K); asking for them otherwise returns GEMM_EINVAL (nothing is
- * launched).
+ * kernel schedule (gemm_schedule) chosen by the caller.  AUTO, PIPELINED,
+ * IN_PHASE, INTERLEAVED and TILE128 run MFMA kernels and return GEMM_EALIGN
+ * or GEMM_EUNSUPPORTED (nothing launched) for operands they cannot take, as
+ * gemm_f16 does; GENERIC runs the plain FMA kernel on any operands.
  */
 int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K,
             const void *A, int64_t lda,
@@ -144,10 +153,10 @@ int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K,
             void *C, int64_t ldc, int out_type, int schedule,
             hipStream_t stream);
 
-/* The tiled schedule AUTO runs for an M x N product whose operands the tiled
- * kernels can take: GEMM_SCHED_PIPELINED, or GEMM_SCHED_TILE128 when there
- * are fewer than 128 output tiles of 256x256 (half of MI355X's compute
- * units).  GEMM_EINVAL for negative sizes.  No device call. */
+/* The tiled schedule AUTO runs for an M x N product: GEMM_SCHED_PIPELINED,
+ * or GEMM_SCHED_TILE128 when there are fewer than 128 output tiles of
+ * 256x256 (half of MI355X's compute units).  GEMM_EINVAL for negative sizes.
+ * No device call. */
 int gemm_auto_schedule(int64_t M, int64_t N);
 
 /*
@@ -164,10 +173,10 @@ int gemm_auto_schedule(int64_t M, int64_t N);
  * library allocates nothing.  Calls that share a workspace must not overlap.
  *   splits     1 .. 256; 1, or a K too short for two slices, runs gemm_ex
  *              (no workspace needed)
- * Returns GEMM_EINVAL for a missing, misaligned or too small workspace, for
- * schedule GENERIC, or for an explicit schedule the operands do not allow
- * (with AUTO, such operands run gemm_ex's generic kernel unsplit), and
- * GEMM_EUNSUPPORTED when the workspace size does not fit in int64_t.
+ * Returns GEMM_EINVAL for a missing, misaligned or too small workspace or
+ * for schedule GENERIC; GEMM_EALIGN / GEMM_EUNSUPPORTED for operands the
+ * MFMA kernels cannot take (as gemm_ex), and GEMM_EUNSUPPORTED when the
+ * workspace size does not fit in int64_t.
  */
 int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K,
                    const void *A, int64_t lda,

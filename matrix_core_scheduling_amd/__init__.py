@@ -26,7 +26,7 @@ LIBRARY = os.path.join(_PKG, "libmcs_gemm.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "mcs_gemm.h")
 ATTN_HEADER = os.path.join(os.path.dirname(_PKG), "include", "mcs_attention.h")
 
-GEMM_OK, GEMM_EINVAL, GEMM_EUNSUPPORTED, GEMM_EHIP = 0, -1, -3, -4
+GEMM_OK, GEMM_EINVAL, GEMM_EALIGN, GEMM_EUNSUPPORTED, GEMM_EHIP = 0, -1, -2, -3, -4
 GEMM_OUT_SAME, GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1, 2
 GEMM_DTYPE_F16, GEMM_DTYPE_BF16, GEMM_DTYPE_FP8_E4M3 = 0, 1, 2
 GEMM_SCHED_AUTO, GEMM_SCHED_PIPELINED, GEMM_SCHED_IN_PHASE, GEMM_SCHED_GENERIC, GEMM_SCHED_INTERLEAVED = 0, 1, 2, 3, 4
@@ -197,6 +197,10 @@ def gemm(A, B, trans_b: bool = False, out=None, out_dtype=None,
     leading dimension).  ``out`` (M x N, unit column stride) is written in
     place if given; otherwise a tensor of ``out_dtype`` is allocated by torch
     (default: the operand dtype, bfloat16 for FP8 operands; float32 allowed).
+    Operands the MFMA kernels cannot take (misaligned views, K not a whole
+    number of 16-byte chunks, ...) raise GemmError with GEMM_EALIGN or
+    GEMM_EUNSUPPORTED; ``schedule=GEMM_SCHED_GENERIC`` asks for the plain FMA
+    kernel, which takes anything.
     Runs on the current stream (or ``stream``) and does not synchronise."""
     import torch
 

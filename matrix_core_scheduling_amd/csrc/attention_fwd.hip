@@ -428,9 +428,10 @@ int attention_launch(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int
     if (!(scale > 0.f) || !std::isfinite(scale)) return GEMM_EINVAL;
     if (head_dim != kHeadDim) return GEMM_EUNSUPPORTED;
     if (batch == 0 || heads == 0 || seq_q == 0) return GEMM_OK;
-    if (!Q || !O || !aligned16(Q) || !aligned16(O)) return GEMM_EINVAL;
-    if (seq_k > 0 && (!K || !V || !aligned16(K) || !aligned16(V))) return GEMM_EINVAL;
-    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return GEMM_EINVAL;
+    if (!Q || !O || (seq_k > 0 && (!K || !V))) return GEMM_EINVAL;
+    if (!aligned16(Q) || !aligned16(O)) return GEMM_EALIGN;
+    if (seq_k > 0 && (!aligned16(K) || !aligned16(V))) return GEMM_EALIGN;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return GEMM_EALIGN;
     // row indices and per-head element offsets stay below 2^31
     if (seq_q >= (int64_t(1) << 23) || seq_k >= (int64_t(1) << 23)) return GEMM_EUNSUPPORTED;
     if (batch > 0x7FFFFFFF || heads > 0x7FFFFFFF) return GEMM_EUNSUPPORTED;   // batch * heads fits int64_t

@@ -24,19 +24,23 @@ int elem_of(int dtype) {
          : dtype == GEMM_DTYPE_BF16 ? mcs::kElemBF16 : mcs::kElemF16;
 }
 
-// Can the 256x256 kernels take these operands?
-bool pipelined_ok(int elem, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
-                  int64_t ldb, int trans_b, const void *C, int64_t ldc) {
+// Can the tiled MFMA kernels take these operands?  GEMM_EALIGN: a pointer or
+// a leading dimension that 16-byte loads and stores cannot use (A, B and C
+// 16-byte aligned; lda and ldb whole 16-byte multiples; ldc a multiple of 8
+// elements).  GEMM_EUNSUPPORTED: a shape they do not cover -- a K extent that
+// is not a whole number of 16-byte chunks (copies move whole chunks), an odd
+// N with B given K x N (a K x N row is copied in whole dwords up to its last
+// valid column), FP8 with B given K x N, or rows of 2^24 bytes or more (128
+// rows of one copy window must stay below 2^31 bytes of buffer offset).
+int tiled_status(int elem, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                 int64_t ldb, int trans_b, const void *C, int64_t ldc) {
     const int64_t eb = mcs::elem_bytes(elem);
-    if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return false;
-    if ((lda * eb) % 16 || (ldb * eb) % 16 || (K * eb) % 16 || ldc % 8) return false;
-    if (lda * eb >= kMaxRowBytes || ldb * eb >= kMaxRowBytes) return false;
-    if (!trans_b) {
-        if (elem == mcs::kElemFP8) return false;
-        // A K x N operand is copied in whole dwords up to the last valid column.
-        if (N % 2) return false;
-    }
-    return true;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return GEMM_EALIGN;
+    if ((lda * eb) % 16 || (ldb * eb) % 16 || ldc % 8) return GEMM_EALIGN;
+    if ((K * eb) % 16) return GEMM_EUNSUPPORTED;
+    if (lda * eb >= kMaxRowBytes || ldb * eb >= kMaxRowBytes) return GEMM_EUNSUPPORTED;
+    if (!trans_b && (elem == mcs::kElemFP8 || N % 2)) return GEMM_EUNSUPPORTED;
+    return GEMM_OK;
 }
 
 bool out_ok(int dtype, int out_type) {
@@ -165,10 +169,6 @@ extern "C" int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A
                       prm, stream);
     }
 
-    const bool fast = pipelined_ok(elem, N, K, A, lda, B, ldb, trans_b, C, ldc);
-    if (schedule == GEMM_SCHED_AUTO) schedule = fast ? auto_tiled_schedule(M, N) : GEMM_SCHED_GENERIC;
-    if (schedule != GEMM_SCHED_GENERIC && !fast) return GEMM_EINVAL;
-
     if (schedule == GEMM_SCHED_GENERIC) {
         const int64_t gx = (N + mcs::kGenTile - 1) / mcs::kGenTile;
         const int64_t gy = (M + mcs::kGenTile - 1) / mcs::kGenTile;
@@ -178,6 +178,9 @@ extern "C" int gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A
                       dim3(mcs::kGenThreads), prm, stream);
     }
 
+    const int st = tiled_status(elem, N, K, A, lda, B, ldb, trans_b, C, ldc);
+    if (st != GEMM_OK) return st;
+    if (schedule == GEMM_SCHED_AUTO) schedule = auto_tiled_schedule(M, N);
     return launch_tiles(elem, trans_b, out_f32, schedule, prm, K, 1, stream);
 }
 
@@ -225,10 +228,8 @@ extern "C" int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K, const 
     if (K > 0) split_plan(elem, K, splits, kslice, slices);
     if (slices == 1)
         return gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream);
-    const bool fast = pipelined_ok(elem, N, K, A, lda, B, ldb, trans_b, C, ldc);
-    if (!fast) return schedule == GEMM_SCHED_AUTO
-        ? gemm_ex(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, stream)
-        : GEMM_EINVAL;
+    const int tst = tiled_status(elem, N, K, A, lda, B, ldb, trans_b, C, ldc);
+    if (tst != GEMM_OK) return tst;
     const int64_t need = ws_bytes(slices, M, N);
     if (need < 0) return GEMM_EUNSUPPORTED;
     if (!workspace || !aligned16(workspace) || workspace_bytes < need) return GEMM_EINVAL;
@@ -326,7 +327,8 @@ extern "C" const char *gemm_status_string(int status) {
     switch (status) {
         case GEMM_OK: return "GEMM_OK: success";
         case GEMM_EINVAL: return "GEMM_EINVAL: invalid argument";
-        case GEMM_EUNSUPPORTED: return "GEMM_EUNSUPPORTED: size outside what the kernels can index";
+        case GEMM_EALIGN: return "GEMM_EALIGN: pointer or leading dimension not 16-byte aligned";
+        case GEMM_EUNSUPPORTED: return "GEMM_EUNSUPPORTED: shape or size the kernel does not cover";
         case GEMM_EHIP: return "GEMM_EHIP: HIP launch failure (see hipGetLastError)";
         default: return "unknown gemm_status";
     }

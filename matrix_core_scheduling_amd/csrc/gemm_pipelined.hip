@@ -16,10 +16,11 @@
 // per 64-deep K-step); here two quadrants share a stage, four stages per
 // K-step, because each rendezvous costs the MFMA pipe ~75 cycles (measured
 // with the memory work removed) and 16 MFMAs (256 cycles) were too little
-// work to cover it ("Stage Size and Register Pressure": stages must hold
-// enough matrix work to cover preparation without excessive barrier
-// overhead).  The loop is unrolled twice so each LDS buffer is addressed
-// statically.  Copies of future tiles go straight from global memory into
+// work to amortise it (section "Stage Size and Register Pressure" weighs
+// the same trade: bigger stages hide more of the other group's memory work
+// per rendezvous, at the price of registers).  The loop is unrolled twice so
+// each LDS buffer is addressed statically.  Copies of future tiles go
+// straight from global memory into
 // LDS (buffer_load ... lds), the operand halves are double buffered, and
 // three flows overlap: copies of a future K-step, LDS reads for the next
 // stage, and MFMA on the current one.

@@ -21,6 +21,8 @@ row stride in elements; padding elements get values too):
     normal(0,1)    : Box-Muller on the two uniforms drawn at 2i and 2i+1:
                      v = sqrt(-2 ln(1 - u(2i))) * cos(2 pi u(2i+1))
     integers [-2,2]: v = (x mod 5) - 2
+    integers {1,2} : v = (x mod 2) + 1      ("int12": same-sign sums that grow
+                     like 2.25 K, past FP16's exact-integer range)
 
 The double v is rounded once to the operand type: FP16 by numpy's
 float64->float16 cast (round to nearest even), BF16 by float64->float32
@@ -124,6 +126,11 @@ def _values_into(dist: str, seed: int, stream: int, start: int, out: np.ndarray,
             np.sqrt(r, out=r)
             np.multiply(r, g, out=g)
             f = g
+        elif dist == "int12":
+            z = _mix_chunk(key, start + c0, m, sc)
+            np.bitwise_and(z, np.uint64(1), out=z)
+            np.add(z, np.uint64(1), out=z)
+            np.copyto(f, z, casting="unsafe")
         elif dist == "int5":
             z = _mix_chunk(key, start + c0, m, sc)
             np.remainder(z, np.uint64(5), out=z)

@@ -43,8 +43,9 @@ def run(elem: str, M: int, N: int, K: int, a_bits, b_bits, trans_b: int, out: st
     """C = A.B on the GPU through the C ABI; returns (C float64 M x N, raw C bits).
     out: "same" (the operand type; not for fp8), "f32" or "bf16".
 
-    With allow_refusal, a GEMM_EINVAL answer (the requested schedule cannot
-    take these operands; nothing was launched) returns None instead."""
+    With allow_refusal, a GEMM_EALIGN or GEMM_EUNSUPPORTED answer (the MFMA
+    kernels cannot take these operands; nothing was launched) returns None
+    instead."""
     torch = _torch()
     print(f"[gpu] {entry} elem={elem} M={M} N={N} K={K} trans_b={trans_b} out={out} "
           f"sched={schedule} ldc={ldc} a_off={a_offset}", flush=True)
@@ -67,7 +68,7 @@ def run(elem: str, M: int, N: int, K: int, a_bits, b_bits, trans_b: int, out: st
     else:
         fn = {"f16": mcs.gemm_f16, "bf16": mcs.gemm_bf16, "fp8": mcs.gemm_fp8}[elem]
         st = fn(M, N, K, a_ptr, lda, B.data_ptr(), ldb, trans_b, C.data_ptr(), ldc, out_type, stream)
-    if allow_refusal and st == mcs.GEMM_EINVAL:
+    if allow_refusal and st in (mcs.GEMM_EALIGN, mcs.GEMM_EUNSUPPORTED):
         return None
     assert st == mcs.GEMM_OK, mcs.gemm_status_string(st)
     torch.cuda.synchronize()

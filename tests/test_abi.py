@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in (mcs.GEMM_OK, mcs.GEMM_EINVAL, mcs.GEMM_EUNSUPPORTED, mcs.GEMM_EHIP):
+    for st in (mcs.GEMM_OK, mcs.GEMM_EINVAL, mcs.GEMM_EALIGN, mcs.GEMM_EUNSUPPORTED, mcs.GEMM_EHIP):
         assert mcs.gemm_status_string(st).startswith(("GEMM_OK", "GEMM_E"))
     assert "unknown" in mcs.gemm_status_string(12345)
 
@@ -90,26 +90,51 @@ def test_ex_rejects_bad_dtype_and_schedule(lib):
     assert mcs.gemm_ex(0, *good, -1, 0) == mcs.GEMM_EINVAL
 
 
-def test_pipelined_schedule_refuses_unaligned_operands(lib):
-    # P + 2 is not 16-byte aligned: the pipelined schedule cannot take it and
-    # says so instead of launching.
-    args = (256, 256, 64, P + 2, 64, P, 64, 1, P, 256, 0)
-    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
-    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_IN_PHASE, 0) == mcs.GEMM_EINVAL
-    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
-    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_TILE128, 0) == mcs.GEMM_EINVAL
-    args = (256, 256, 60, P, 64, P, 64, 1, P, 256, 0)             # K % 8 != 0
-    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
-    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
-    assert mcs.gemm_ex(0, *args, mcs.GEMM_SCHED_TILE128, 0) == mcs.GEMM_EINVAL
-    fp8 = mcs.GEMM_DTYPE_FP8_E4M3
-    args = (256, 256, 136, P, 256, P, 256, 1, P, 256, mcs.GEMM_OUT_BF16)  # FP8: K % 16 != 0
-    assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
-    args = (256, 256, 128, P, 136, P, 256, 1, P, 256, mcs.GEMM_OUT_BF16)  # FP8: lda % 16 != 0
-    assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
-    args = (256, 256, 128, P, 128, P, 256, 0, P, 256, mcs.GEMM_OUT_BF16)  # FP8, B given K x N
-    assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_PIPELINED, 0) == mcs.GEMM_EINVAL
-    assert mcs.gemm_ex(fp8, *args, mcs.GEMM_SCHED_TILE128, 0) == mcs.GEMM_EINVAL
+MFMA_SCHEDS = ("AUTO", "PIPELINED", "IN_PHASE", "INTERLEAVED", "TILE128")
+
+
+@pytest.mark.parametrize("sched", MFMA_SCHEDS)
+def test_mfma_schedules_refuse_what_they_cannot_take(lib, sched):
+    """Operands the MFMA kernels cannot take are refused before anything is
+    launched, with the reason: GEMM_EALIGN for pointers and leading
+    dimensions, GEMM_EUNSUPPORTED for shapes.  AUTO (what gemm_f16 runs)
+    refuses them too: it never falls back to the plain FMA kernel."""
+    s = getattr(mcs, "GEMM_SCHED_" + sched)
+    ex = mcs.gemm_ex
+    f16, fp8 = mcs.GEMM_DTYPE_F16, mcs.GEMM_DTYPE_FP8_E4M3
+    BF = mcs.GEMM_OUT_BF16
+    assert ex(f16, 256, 256, 64, P + 2, 64, P, 64, 1, P, 256, 0, s, 0) == mcs.GEMM_EALIGN     # A
+    assert ex(f16, 256, 256, 64, P, 64, P + 8, 64, 1, P, 256, 0, s, 0) == mcs.GEMM_EALIGN     # B
+    assert ex(f16, 256, 256, 64, P, 64, P, 64, 1, P + 4, 256, 0, s, 0) == mcs.GEMM_EALIGN     # C
+    assert ex(f16, 256, 256, 64, P, 68, P, 64, 1, P, 256, 0, s, 0) == mcs.GEMM_EALIGN         # lda
+    assert ex(f16, 256, 256, 64, P, 64, P, 260, 0, P, 256, 0, s, 0) == mcs.GEMM_EALIGN        # ldb
+    assert ex(f16, 256, 250, 64, P, 64, P, 64, 1, P, 252, 0, s, 0) == mcs.GEMM_EALIGN         # ldc
+    assert ex(f16, 256, 256, 60, P, 64, P, 64, 1, P, 256, 0, s, 0) == mcs.GEMM_EUNSUPPORTED   # K % 8
+    assert ex(f16, 256, 255, 64, P, 64, P, 256, 0, P, 256, 0, s, 0) == mcs.GEMM_EUNSUPPORTED  # odd N, K x N
+    big = (1 << 23)                                                  # a 2^24-byte FP16 row
+    assert ex(f16, 4, 4, 64, P, big, P, 64, 1, P, 8, 0, s, 0) == mcs.GEMM_EUNSUPPORTED
+    assert ex(fp8, 256, 256, 136, P, 256, P, 256, 1, P, 256, BF, s, 0) == mcs.GEMM_EUNSUPPORTED  # K % 16
+    assert ex(fp8, 256, 256, 128, P, 136, P, 256, 1, P, 256, BF, s, 0) == mcs.GEMM_EALIGN        # lda % 16
+    assert ex(fp8, 256, 256, 128, P, 128, P, 256, 0, P, 256, BF, s, 0) == mcs.GEMM_EUNSUPPORTED  # B K x N
+
+
+@pytest.mark.parametrize("fn", ["gemm_f16", "gemm_bf16", "gemm_fp8"])
+def test_entry_points_report_alignment(lib, fn):
+    """The spec entry points run only the MFMA kernels: a misaligned
+    operand is GEMM_EALIGN, never a silent switch to a slower kernel."""
+    out = VALID_OUT[fn]
+    f = getattr(mcs, fn)
+    assert f(256, 256, 128, P + 2, 128, P, 128, 1, P, 256, out, 0) == mcs.GEMM_EALIGN
+    assert f(256, 256, 128, P, 136 if fn == "gemm_fp8" else 132, P, 128, 1, P, 256, out, 0) == mcs.GEMM_EALIGN
+    assert f(256, 256, 124, P, 128, P, 128, 1, P, 256, out, 0) == mcs.GEMM_EUNSUPPORTED     # K tail
+
+
+def test_splitk_refuses_what_the_mfma_kernels_cannot_take(lib):
+    sk = mcs.gemm_ex_splitk
+    args = (512, 512, 8192, P + 2, 8192, P, 8192, 1, P, 512, 0)
+    assert sk(0, *args, mcs.GEMM_SCHED_AUTO, 4, P, 1 << 30, 0) == mcs.GEMM_EALIGN
+    args = (512, 512, 8188, P, 8192, P, 8192, 1, P, 512, 0)
+    assert sk(0, *args, mcs.GEMM_SCHED_AUTO, 4, P, 1 << 30, 0) == mcs.GEMM_EUNSUPPORTED
 
 
 def test_torch_wrappers_refuse_host_tensors(lib):
@@ -163,7 +188,7 @@ def test_splitk_validation_before_launch(lib):
     assert sk(0, *args, mcs.GEMM_SCHED_AUTO, 0, P, need, 0) == mcs.GEMM_EINVAL          # splits < 1
     assert sk(0, *args, mcs.GEMM_SCHED_AUTO, 257, P, need, 0) == mcs.GEMM_EINVAL
     bad = (1024, 1024, 1024, P + 2, 1024, P, 1024, 1, P, 1024, 0)                      # unaligned A
-    assert sk(0, *bad, mcs.GEMM_SCHED_PIPELINED, 4, P, need, 0) == mcs.GEMM_EINVAL
+    assert sk(0, *bad, mcs.GEMM_SCHED_PIPELINED, 4, P, need, 0) == mcs.GEMM_EALIGN
     assert sk(0, 0, 8, 8, 0, 8, 0, 8, 1, 0, 8, 0, mcs.GEMM_SCHED_AUTO, 4, 0, 0, 0) == mcs.GEMM_OK  # empty
     # a workspace size that overflows int64_t is refused, whatever workspace_bytes claims
     big = 2 ** 31 - 8
@@ -217,10 +242,10 @@ def test_attention_argument_errors(lib):
     assert call(scale=float("inf")) == mcs.GEMM_EINVAL
     assert call(head_dim=64) == mcs.GEMM_EUNSUPPORTED
     assert call(Q=0) == mcs.GEMM_EINVAL
-    assert call(O=P + 8) == mcs.GEMM_EINVAL                          # misaligned
-    assert call(K=P + 2) == mcs.GEMM_EINVAL
+    assert call(O=P + 8) == mcs.GEMM_EALIGN                          # misaligned
+    assert call(K=P + 2) == mcs.GEMM_EALIGN
     assert call(V=0) == mcs.GEMM_EINVAL
-    assert call(lse=P + 2) == mcs.GEMM_EINVAL
+    assert call(lse=P + 2) == mcs.GEMM_EALIGN
     assert call(seq_q=1 << 23) == mcs.GEMM_EUNSUPPORTED
     assert call(batch=1 << 40, heads=1 << 40) == mcs.GEMM_EUNSUPPORTED      # batch * heads would overflow
     assert call(batch=1 << 20, heads=1 << 12) == mcs.GEMM_EUNSUPPORTED      # 2^32 workgroup rows

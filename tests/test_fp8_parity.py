@@ -59,7 +59,9 @@ def test_shapes_every_element(shape, trans_b, out, sched):
               return_raw=True, allow_refusal=True)
     if got is None:
         assert not fast_eligible(K, trans_b)
-        got = run("fp8", M, N, K, a, b, trans_b, out=out, ldc=ldc, c_fill=-3.0, return_raw=True)
+        assert run("fp8", M, N, K, a, b, trans_b, out=out, ldc=ldc, allow_refusal=True) is None
+        got = run("fp8", M, N, K, a, b, trans_b, out=out, schedule=mcs.GEMM_SCHED_GENERIC, ldc=ldc,
+                  c_fill=-3.0, return_raw=True)
     else:
         assert fast_eligible(K, trans_b)
     c, _, full = got
@@ -85,7 +87,8 @@ def test_integer_regime_bit_exact(shape, out, sched):
 def test_b_given_k_by_n_runs_generic_and_matches_n_by_k():
     M, N, K = 384, 320, 528
     a, b = operands("normal", M, N, K, 0, seed=61)
-    c0 = run("fp8", M, N, K, a, b, 0, out="f32")[0]
+    assert run("fp8", M, N, K, a, b, 0, out="f32", entry="abi", allow_refusal=True) is None
+    c0 = run("fp8", M, N, K, a, b, 0, out="f32", schedule=mcs.GEMM_SCHED_GENERIC)[0]
     cref, sabs = oracle.gemm(a, b, "fp8", 0)
     assert_within_tolerance(c0, cref, sabs, "fp8 B K x N", out="f32")
     c1 = run("fp8", M, N, K, a, np.ascontiguousarray(b.T), 1, out="f32")[0]
@@ -128,11 +131,13 @@ def test_nan_operand_propagates():
     assert np.isfinite(c).all()
 
 
-def test_misaligned_operand_takes_generic_path_and_is_correct():
+def test_misaligned_operand_is_refused_and_runs_on_request_in_the_plain_kernel():
     M, N, K = 100, 70, 64
     a, b = operands("normal", M, N, K, 1, seed=17)
     cref, sabs = oracle.gemm(a, b, "fp8", 1, K=K, N=N)
-    c, _ = run("fp8", M, N, K, a, b, 1, out="bf16", a_offset=1)      # A starts 1 byte into its buffer
+    # A starts 1 byte into its buffer: gemm_fp8 says GEMM_EALIGN and launches nothing
+    assert run("fp8", M, N, K, a, b, 1, out="bf16", a_offset=1, entry="abi", allow_refusal=True) is None
+    c, _ = run("fp8", M, N, K, a, b, 1, out="bf16", a_offset=1, schedule=mcs.GEMM_SCHED_GENERIC)
     assert_within_tolerance(c, cref, sabs, "misaligned A", out="bf16")
 
 

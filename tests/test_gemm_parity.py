@@ -71,9 +71,12 @@ def test_shapes_every_element(shape, elem, trans_b, out, sched):
     got = run(elem, M, N, K, a, b, trans_b, out=out, schedule=SCHEDS[sched], ldc=ldc, c_fill=-3.0,
               return_raw=True, allow_refusal=True)
     if got is None:
-        # refused before launch, as documented; the default schedule must still be right
+        # refused before launch, as documented (and so is AUTO, the entry points'
+        # schedule); the plain kernel, asked for explicitly, must still be right
         assert not pipelined_eligible(N, K, trans_b)
-        got = run(elem, M, N, K, a, b, trans_b, out=out, ldc=ldc, c_fill=-3.0, return_raw=True)
+        assert run(elem, M, N, K, a, b, trans_b, out=out, ldc=ldc, allow_refusal=True) is None
+        got = run(elem, M, N, K, a, b, trans_b, out=out, schedule=mcs.GEMM_SCHED_GENERIC, ldc=ldc,
+                  c_fill=-3.0, return_raw=True)
     else:
         assert pipelined_eligible(N, K, trans_b)
     c, _, full = got
@@ -88,7 +91,9 @@ def test_generic_kernel_every_element(elem, trans_b):
     M, N, K = 130, 77, 45                  # K % 8 != 0 and odd sizes: only the generic kernel
     a, b = operands(elem, "normal", M, N, K, trans_b, seed=3)
     cref, sabs = ref(a, b, elem, trans_b, K, N)
-    c, _ = run(elem, M, N, K, a, b, trans_b, schedule=mcs.GEMM_SCHED_AUTO)
+    # the entry points' AUTO schedule refuses the shape instead of switching kernels
+    assert run(elem, M, N, K, a, b, trans_b, entry="abi", allow_refusal=True) is None
+    c, _ = run(elem, M, N, K, a, b, trans_b, schedule=mcs.GEMM_SCHED_GENERIC)
     assert_within_tolerance(c, cref, sabs, "generic", out=elem)
     c, _ = run(elem, M, N, K, a, b, trans_b, schedule=mcs.GEMM_SCHED_GENERIC, out="f32")
     assert_within_tolerance(c, cref, sabs, "generic f32")
@@ -110,6 +115,51 @@ def test_integer_regime_bit_exact(shape, elem, trans_b, out, sched):
     cref = oracle.gemm(a, b, elem, trans_b, with_sabs=False)
     _, bits = run(elem, M, N, K, a, b, trans_b, out=out, schedule=SCHEDS[sched])
     assert_bit_exact(bits, cref, elem, out, f"int {shape} {elem} tb={trans_b} {out} {sched}")
+
+
+# ---- output rounding beyond FP16's exact-integer range: round to nearest even ---
+
+def same_sign_integer_operands(elem, M, N, K, trans_b, seed):
+    """Integers in {1, 2}, with every odd row of A negated: the sums grow like
+    +-2.25 K, so for K >= 1024 most of them lie past 2048, where FP16 has no
+    integer spacing left and the output must round -- ties included (an odd
+    sum in [2048, 4096) sits exactly between two FP16 values).  Every partial
+    sum stays below 4 K <= 2^14 in magnitude, so FP32 accumulation is exact in
+    any order and the only rounding is the conversion to the output type."""
+    a, b = operands(elem, "int12", M, N, K, trans_b, seed=seed)
+    a[1::2] |= np.uint16(0x8000)                # sign bit: odd rows of A negative
+    return a, b
+
+
+def rounding_cases(cref, elem):
+    """Counts of results that are not representable in the output type and of
+    exact ties between two neighbours (so the test can tell RNE from
+    round-toward-zero and round-half-away)."""
+    lo = oracle.decode(oracle.round_to(cref, elem), elem)
+    inexact = lo != cref
+    # a tie: the value is the midpoint of the rounded result and its neighbour
+    # one spacing away (the spacing of FP16 at |x| in [2^e, 2^(e+1)) is 2^(e-10))
+    mant = 10 if elem == "f16" else 7
+    e = np.floor(np.log2(np.maximum(np.abs(cref), 1.0)))
+    ulp = np.ldexp(1.0, (e - mant).astype(np.int64))
+    tie = np.abs(cref / ulp - np.round(cref / ulp)) == 0.5
+    return int(inexact.sum()), int(tie.sum())
+
+
+@pytest.mark.parametrize("sched", ["pipelined", "in_phase", "interleaved", "tile128"])
+@pytest.mark.parametrize("trans_b", [0, 1])
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+@pytest.mark.parametrize("K", [1024, 2048, 4096])
+def test_output_rounds_to_nearest_even(K, elem, trans_b, sched):
+    """The FP32 -> FP16/BF16 epilogue is round-to-nearest-even, bit for bit:
+    the exact sums here need rounding (and hit ties) in the output type."""
+    M, N = 512, 520
+    a, b = same_sign_integer_operands(elem, M, N, K, trans_b, seed=60 + K)
+    cref = oracle.gemm(a, b, elem, trans_b, with_sabs=False)
+    inexact, ties = rounding_cases(cref, elem)
+    assert inexact > M * N // 4 and ties > 1000, (inexact, ties)
+    _, bits = run(elem, M, N, K, a, b, trans_b, schedule=SCHEDS[sched])
+    assert_bit_exact(bits, cref, elem, "same", f"RNE K={K} {elem} tb={trans_b} {sched}")
 
 
 # ---- closed forms ---------------------------------------------------------------
@@ -152,7 +202,7 @@ def test_all_ones_gives_k(elem):
 
 def test_rank_one_integer():
     rng = np.random.default_rng(8)
-    M, N, K = 300, 260, 96
+    M, N, K = 300, 264, 96
     u = rng.integers(-3, 4, M).astype(np.float16)
     v = rng.integers(-3, 4, N).astype(np.float16)
     a = np.repeat(u[:, None], K, axis=1).view(np.uint16)
@@ -161,7 +211,23 @@ def test_rank_one_integer():
     assert np.array_equal(c, K * np.outer(u.astype(np.float64), v.astype(np.float64)))
 
 
-# ---- the five workloads, in the configuration the benchmark launches -----------
+# ---- the workloads, in the configuration the benchmark launches: every element ----
+
+_ORACLE = {}
+
+
+def workload_reference(name):
+    """(A bits, B bits, Cref, Sabs) of a workload's first input set: the full
+    oracle over every output element (threaded over the host's cores; about
+    20 s for the 8192^3 products on 16 threads), computed once per session."""
+    if name not in _ORACLE:
+        w = si.WORKLOADS[name]
+        print(f"[gpu] oracle for workload {name} ({w.M}x{w.N}x{w.K})", flush=True)
+        a, b = w.operands(0)
+        cref, sabs = oracle.gemm(a, b, w.dtype, w.trans_b)
+        _ORACLE[name] = (a, b, cref, sabs)
+    return _ORACLE[name]
+
 
 def sample_points(M, N, count, seed):
     rng = np.random.default_rng(seed)
@@ -175,21 +241,26 @@ def sample_points(M, N, count, seed):
     return np.array(ii), np.array(jj)
 
 
+def check_workload(name, c, what):
+    """Sampled points first (a quick, independent recomputation at single
+    elements), then every element against the full oracle."""
+    w = si.WORKLOADS[name]
+    a, b, cref, sabs = workload_reference(name)
+    ii, jj = sample_points(w.M, w.N, 500, seed=w.seed)
+    cp, sp = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
+    assert np.array_equal(cp, cref[ii, jj]) and np.array_equal(sp, sabs[ii, jj])
+    assert_within_tolerance(c[ii, jj][None, :], cp[None, :], sp[None, :], f"{what} (points)", out=w.out_type)
+    assert_within_tolerance(c, cref, sabs, what, out=w.out_type)
+
+
 @pytest.mark.parametrize("name", list(si.WORKLOADS))
 def test_workload(name):
+    """Every workload through the entry point (gemm_f16 / gemm_bf16 /
+    gemm_fp8, AUTO), every element against the oracle."""
     w = si.WORKLOADS[name]
-    a, b = w.operands(0)
+    a, b, _, _ = workload_reference(name)
     c, _ = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, entry="abi")
-    if w.M * w.N * w.K <= 2 ** 31:
-        cref, sabs = oracle.gemm(a, b, w.dtype, w.trans_b)
-        assert_within_tolerance(c, cref, sabs, name, out=w.out_type)
-    else:
-        ii, jj = sample_points(w.M, w.N, 3000, seed=w.seed)
-        cref, sabs = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
-        assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name,
-                                out=w.out_type)
-        # properties at every element: finite, and bounded by the operands
-        assert np.isfinite(c).all()
+    check_workload(name, c, name)
 
 
 # ---- invariants --------------------------------------------------------------
@@ -235,31 +306,21 @@ def test_tile128_matches_pipelined_bitwise(elem, trans_b, out):
                                   or w.M <= 512])
 def test_workload_tile128(name):
     """Workloads with few 256x256 tiles through the 128x128-tile kernel:
-    every element (sampled points for the 512x4096x8192 share)."""
+    every element."""
     w = si.WORKLOADS[name]
-    a, b = w.operands(0)
+    a, b, _, _ = workload_reference(name)
     c, _ = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, schedule=mcs.GEMM_SCHED_TILE128)
-    if w.M * w.N * w.K <= 2 ** 31:
-        cref, sabs = oracle.gemm(a, b, w.dtype, w.trans_b)
-        assert_within_tolerance(c, cref, sabs, name, out=w.out_type)
-    else:
-        ii, jj = sample_points(w.M, w.N, 3000, seed=w.seed + 2)
-        cref, sabs = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
-        assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name,
-                                out=w.out_type)
+    check_workload(name, c, f"{name} tile128")
 
 
 @pytest.mark.parametrize("name", [n for n, w in si.WORKLOADS.items() if w.M * w.N >= 4096 * 4096])
 def test_workload_interleaved(name):
-    """Full-size workloads through the 4-wave kernel: sampled oracle parity and
-    bitwise agreement with the 8-wave kernel at every element."""
+    """Full-size workloads through the 4-wave and the 8-wave kernel: every
+    element against the oracle, and the two bitwise equal."""
     w = si.WORKLOADS[name]
-    a, b = w.operands(0)
+    a, b, _, _ = workload_reference(name)
     c, bits = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, schedule=mcs.GEMM_SCHED_INTERLEAVED)
-    ii, jj = sample_points(w.M, w.N, 3000, seed=w.seed + 1)
-    cref, sabs = oracle.gemm_points(a, b, w.dtype, w.trans_b, ii, jj)
-    assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], name,
-                            out=w.out_type)
+    check_workload(name, c, f"{name} interleaved")
     _, bits_p = run(w.dtype, w.M, w.N, w.K, a, b, w.trans_b, out=w.out, schedule=mcs.GEMM_SCHED_PIPELINED)
     assert np.array_equal(bits, bits_p)
 
@@ -308,11 +369,13 @@ def test_output_padding_untouched(elem):
     assert_within_tolerance(c, cref, sabs, "ldc > N", out=elem)
 
 
-def test_misaligned_operand_takes_generic_path_and_is_correct():
+def test_misaligned_operand_is_refused_and_runs_on_request_in_the_plain_kernel():
     M, N, K = 100, 70, 64
     a, b = operands("f16", "uniform", M, N, K, 1, seed=17)
     cref, sabs = ref(a, b, "f16", 1, K, N)
-    c, _ = run("f16", M, N, K, a, b, 1, a_offset=1)          # A starts 2 bytes into its buffer
+    # A starts 2 bytes into its buffer: gemm_f16 says GEMM_EALIGN and launches nothing
+    assert run("f16", M, N, K, a, b, 1, a_offset=1, entry="abi", allow_refusal=True) is None
+    c, _ = run("f16", M, N, K, a, b, 1, a_offset=1, schedule=mcs.GEMM_SCHED_GENERIC)
     assert_within_tolerance(c, cref, sabs, "misaligned A")
 
 

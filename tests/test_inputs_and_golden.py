@@ -37,6 +37,10 @@ def test_distributions():
     assert abs(n.mean()) < 0.01 and abs(n.std() - 1) < 0.01
     i = si.values("int5", 7, 0, 100000)
     assert set(np.unique(i)) == {-2.0, -1.0, 0.0, 1.0, 2.0}
+    j = si.values("int12", 7, 0, 100000)
+    assert set(np.unique(j)) == {1.0, 2.0} and abs(j.mean() - 1.5) < 0.01
+    # each draw is the low bit of the counter's SplitMix64 output, plus one
+    assert np.array_equal(j[:64], (si.raw_u64(7, 0, 0, 64) & np.uint64(1)).astype(np.float64) + 1)
 
 
 def test_operand_bits_round_once():

@@ -105,14 +105,28 @@ def test_splitk_schedules_agree_bitwise():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-def test_splitk_shard_workload_sampled():
+def test_splitk_shard_workload_every_element():
     """One GPU's row block of the 8-way split of the 4096x4096x8192 product
-    (512x4096x8192), split four ways: sampled oracle points."""
+    (512x4096x8192), split two and four ways: every element."""
     M, N, K = 512, 4096, 8192
     a, b = operands("f16", "uniform", M, N, K, 1, seed=1003)
-    c, _, _ = run_splitk("f16", M, N, K, a, b, 1, "same", mcs.GEMM_SCHED_AUTO, 4)
-    rng = np.random.default_rng(7)
-    ii = np.concatenate([rng.integers(0, M, 2000), [0, M - 1, 255, 256]])
-    jj = np.concatenate([rng.integers(0, N, 2000), [0, N - 1, 4095, 256]])
-    cref, sabs = oracle.gemm_points(a, b, "f16", 1, ii, jj)
-    assert_within_tolerance(c[ii, jj][None, :], cref[None, :], sabs[None, :], "shard splitk")
+    cref, sabs = oracle.gemm(a, b, "f16", 1)
+    for splits in (2, 4):
+        c, _, _ = run_splitk("f16", M, N, K, a, b, 1, "same", mcs.GEMM_SCHED_AUTO, splits)
+        assert_within_tolerance(c, cref, sabs, f"shard splitk {splits}")
+
+
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+@pytest.mark.parametrize("K", [1024, 2048, 4096])
+def test_splitk_output_rounds_to_nearest_even(K, elem):
+    """The reduction kernel rounds the summed FP32 partials to nearest even:
+    same-sign integer sums past FP16's exact-integer range (ties included),
+    exact in FP32 in any order, must equal RNE of the exact value bit for bit."""
+    M, N = 512, 520
+    a, b = operands(elem, "int12", M, N, K, 1, seed=80 + K)
+    a[1::2] |= np.uint16(0x8000)                # odd rows of A negative
+    cref = oracle.gemm(a, b, elem, 1, with_sabs=False)
+    assert int((oracle.decode(oracle.round_to(cref, elem), elem) != cref).sum()) > M * N // 4
+    for splits in (2, 3, 4):
+        _, bits, _ = run_splitk(elem, M, N, K, a, b, 1, "same", mcs.GEMM_SCHED_AUTO, splits)
+        assert_bit_exact(bits, cref, elem, "same", f"splitk RNE K={K} {elem} splits={splits}")

@@ -31,7 +31,7 @@ def _padded_view(bits, elem, pad):
 ])
 def test_gemm_wrapper_matches_the_c_abi(elem, trans_b, out):
     torch = _torch()
-    M, N, K = 300, 264, 520
+    M, N, K = 300, 264, 528
     print(f"[gpu] torch wrapper {elem} trans_b={trans_b} out={out} {M}x{N}x{K}", flush=True)
     a = si.matrix_bits(elem, "uniform", M, K, seed=9100, stream=0)
     b = (si.matrix_bits(elem, "uniform", N, K, seed=9100, stream=1) if trans_b
@@ -70,3 +70,23 @@ def test_gemm_wrapper_allocates_the_operand_type():
         oe = "bf16" if elem == "fp8" else elem
         assert_within_tolerance(oracle.decode(C.cpu().view(torch.int16).numpy().view(np.uint16), oe),
                                 cref, sabs, f"allocated output {elem}", out=oe)
+
+
+def test_gemm_wrapper_reports_operands_the_mfma_kernels_cannot_take():
+    """A view whose rows are not whole 16-byte multiples raises GEMM_EALIGN
+    (nothing is launched); the plain kernel takes it when asked for."""
+    torch = _torch()
+    M, N, K = 64, 96, 120
+    print(f"[gpu] torch wrapper refusal {M}x{N}x{K}", flush=True)
+    a = si.matrix_bits("f16", "uniform", M, K, seed=9300, stream=0)
+    b = si.matrix_bits("f16", "uniform", N, K, seed=9300, stream=1)
+    A = _padded_view(a, "f16", 4)                # lda = 124: 248-byte rows
+    B = _padded_view(b, "f16", 8)
+    with pytest.raises(mcs.GemmError) as e:
+        mcs.gemm(A, B, trans_b=True)
+    assert e.value.status == mcs.GEMM_EALIGN
+    C = mcs.gemm(A, B, trans_b=True, schedule=mcs.GEMM_SCHED_GENERIC)
+    torch.cuda.synchronize()
+    cref, sabs = oracle.gemm(a, b, "f16", 1, K=K, N=N)
+    assert_within_tolerance(oracle.decode(C.cpu().view(torch.int16).numpy().view(np.uint16), "f16"),
+                            cref, sabs, "plain kernel on request", out="f16")
