@@ -64,7 +64,8 @@ enum gemm_status {
     GEMM_EINVAL = -1,
     GEMM_EALIGN = -2,
     GEMM_EUNSUPPORTED = -3,
-    GEMM_EHIP = -4
+    GEMM_EHIP = -4,
+    GEMM_ENOSCRATCH = -5   /* gemm_ex_splitk_noalloc: partials exceed its scratch */
 };
 
 enum gemm_out_type {
@@ -184,6 +185,33 @@ int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K,
                    void *C, int64_t ldc, int out_type, int schedule,
                    int splits, void *workspace, int64_t workspace_bytes,
                    hipStream_t stream);
+
+/*
+ * gemm_ex_splitk_noalloc -- gemm_ex_splitk for callers that cannot allocate
+ * (code under HIP graph capture, serving loops that forbid hipMalloc,
+ * harnesses without an allocator): the same product, kernels and results,
+ * bit for bit, with the FP32 partials kept in a device array of the library
+ * instead of a caller workspace.  The call allocates nothing and calls no
+ * allocating routine.
+ *   The array holds GEMM_SPLITK_SCRATCH_BYTES (32 MiB); every GPU the
+ *   library runs on keeps its own copy until the process ends.  Products
+ *   whose partials need more (gemm_splitk_workspace_bytes for the same
+ *   sizes and splits) return GEMM_ENOSCRATCH before anything is enqueued.
+ *   Products that would not split (splits 1, or K too short) run gemm_ex.
+ *   All calls on one GPU share its array: calls that overlap in time on one
+ *   GPU (several streams or host threads) race on the partials and give
+ *   wrong results; serialise them.  The device is the one `stream` belongs
+ *   to.  On its first call on a device the library looks up that device's
+ *   copy (hipGetSymbolAddress, which may load the code object there).
+ * Other arguments and errors as gemm_ex_splitk, minus the workspace.
+ */
+#define GEMM_SPLITK_SCRATCH_BYTES ((int64_t)32 << 20)
+
+int gemm_ex_splitk_noalloc(int dtype, int64_t M, int64_t N, int64_t K,
+                           const void *A, int64_t lda,
+                           const void *B, int64_t ldb, int trans_b,
+                           void *C, int64_t ldc, int out_type, int schedule,
+                           int splits, hipStream_t stream);
 
 /* Workspace bytes gemm_ex_splitk needs for these sizes and splits (0 when it
  * would not split).  Returns a gemm_status: GEMM_EINVAL for a null `bytes`,

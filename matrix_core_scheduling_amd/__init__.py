@@ -3,7 +3,7 @@ and the attention forward pass built in the same stage abstraction.
 
 The functions ``gemm_f16``, ``gemm_bf16``, ``gemm_fp8``, ``gemm_ex``,
 ``gemm_ex_splitk``, ``gemm_splitk_workspace_bytes``, ``gemm_auto_schedule``,
-``gemm_splitk_suggest``,
+``gemm_splitk_suggest``, ``gemm_ex_splitk_noalloc``,
 ``gemm_kernel_info``, ``gemm_status_string``, ``attention_fwd`` and
 ``attention_fwd_ex`` mirror the
 C ABI in ``include/mcs_gemm.h`` and ``include/mcs_attention.h`` one to one
@@ -26,7 +26,8 @@ LIBRARY = os.path.join(_PKG, "libmcs_gemm.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "mcs_gemm.h")
 ATTN_HEADER = os.path.join(os.path.dirname(_PKG), "include", "mcs_attention.h")
 
-GEMM_OK, GEMM_EINVAL, GEMM_EALIGN, GEMM_EUNSUPPORTED, GEMM_EHIP = 0, -1, -2, -3, -4
+GEMM_OK, GEMM_EINVAL, GEMM_EALIGN, GEMM_EUNSUPPORTED, GEMM_EHIP, GEMM_ENOSCRATCH = 0, -1, -2, -3, -4, -5
+GEMM_SPLITK_SCRATCH_BYTES = 32 << 20   # the static scratch of gemm_ex_splitk_noalloc
 GEMM_OUT_SAME, GEMM_OUT_F32, GEMM_OUT_BF16 = 0, 1, 2
 GEMM_DTYPE_F16, GEMM_DTYPE_BF16, GEMM_DTYPE_FP8_E4M3 = 0, 1, 2
 GEMM_SCHED_AUTO, GEMM_SCHED_PIPELINED, GEMM_SCHED_IN_PHASE, GEMM_SCHED_GENERIC, GEMM_SCHED_INTERLEAVED = 0, 1, 2, 3, 4
@@ -69,6 +70,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.gemm_ex.restype = ci
     lib.gemm_ex_splitk.argtypes = [ci] + sig + [ci, ci, vp, i64, vp]
     lib.gemm_ex_splitk.restype = ci
+    lib.gemm_ex_splitk_noalloc.argtypes = [ci] + sig + [ci, ci, vp]
+    lib.gemm_ex_splitk_noalloc.restype = ci
     lib.gemm_splitk_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ctypes.POINTER(i64)]
     lib.gemm_splitk_workspace_bytes.restype = ci
     lib.gemm_auto_schedule.argtypes = [i64, i64]
@@ -135,6 +138,12 @@ def gemm_ex_splitk(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, sc
                    workspace, workspace_bytes, stream) -> int:
     return load().gemm_ex_splitk(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule,
                                  splits, workspace, workspace_bytes, stream)
+
+
+def gemm_ex_splitk_noalloc(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, splits,
+                           stream) -> int:
+    return load().gemm_ex_splitk_noalloc(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule,
+                                         splits, stream)
 
 
 def gemm_splitk_workspace_bytes(dtype: int, M: int, N: int, K: int, splits: int) -> int:

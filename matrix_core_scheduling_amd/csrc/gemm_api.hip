@@ -8,6 +8,9 @@
 // kernel compiled ahead of time) with the sizes passed at run time.
 #include "mcs_gemm.h"
 
+#include <atomic>
+#include <mutex>
+
 #include "internal.h"
 
 namespace {
@@ -214,10 +217,17 @@ extern "C" int gemm_splitk_suggest(int dtype, int64_t M, int64_t N, int64_t K, i
     return static_cast<int>(s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s));
 }
 
-extern "C" int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
-                              const void *B, int64_t ldb, int trans_b, void *C, int64_t ldc,
-                              int out_type, int schedule, int splits, void *workspace,
-                              int64_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// The split-K product: validation, then the slices' FP32 partials into the
+// workspace the caller gives (ws_kind kCallerWorkspace) or into the static
+// scratch array below (kStaticScratch, which the caller cannot see).
+enum WsKind { kCallerWorkspace, kStaticScratch };
+int scratch_address(hipStream_t stream, void **out);
+
+int splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+           int64_t ldb, int trans_b, void *C, int64_t ldc, int out_type, int schedule, int splits,
+           WsKind ws_kind, void *workspace, int64_t workspace_bytes, hipStream_t stream) {
     const int v = validate(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule);
     if (v != GEMM_OK) return v;
     if (splits < 1 || splits > kMaxSplits || schedule == GEMM_SCHED_GENERIC) return GEMM_EINVAL;
@@ -232,7 +242,13 @@ extern "C" int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K, const 
     if (tst != GEMM_OK) return tst;
     const int64_t need = ws_bytes(slices, M, N);
     if (need < 0) return GEMM_EUNSUPPORTED;
-    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return GEMM_EINVAL;
+    if (ws_kind == kStaticScratch) {
+        if (need > GEMM_SPLITK_SCRATCH_BYTES) return GEMM_ENOSCRATCH;
+        const int st = scratch_address(stream, &workspace);
+        if (st != GEMM_OK) return st;
+    } else if (!workspace || !aligned16(workspace) || workspace_bytes < need) {
+        return GEMM_EINVAL;
+    }
     if (schedule == GEMM_SCHED_AUTO) schedule = auto_tiled_schedule(M, N);
 
     GemmParams prm{};
@@ -258,6 +274,64 @@ extern "C" int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K, const 
     void *args[] = {&prm, &slices};
     return to_status(hipLaunchKernel(mcs::splitk_reduce_kernel(out_kind),
                                      dim3(static_cast<unsigned>(blocks)), dim3(256), args, 0, stream));
+}
+
+// ---- the allocation-free split K ------------------------------------------
+//
+// The FP32 partials of gemm_ex_splitk_noalloc live in this file-scope device
+// array.  Every GPU the library runs on holds its own copy from the moment
+// the code object is loaded until the process ends.  Host code never uses
+// the array's name as an address: on the host it is only a stand-in that the
+// runtime maps to each device's copy.  scratch_address asks the runtime for
+// that device address once per device, with the device current, and keeps
+// it; kernels only ever receive the kept address.  The slice kernels write
+// every partial element the reduction reads for its output (it also reads,
+// and discards, up to three pad columns per row), so nothing has to be
+// cleared between calls.
+static __device__ __align__(256) float scratch[GEMM_SPLITK_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+int scratch_address(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return GEMM_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return GEMM_EUNSUPPORTED;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            int cur = -1;
+            if (hipGetDevice(&cur) != hipSuccess) return GEMM_EHIP;
+            if (cur != dev && hipSetDevice(dev) != hipSuccess) return GEMM_EHIP;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (cur != dev && hipSetDevice(cur) != hipSuccess) return GEMM_EHIP;
+            if (e != hipSuccess || !p) return GEMM_EHIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" int gemm_ex_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                              const void *B, int64_t ldb, int trans_b, void *C, int64_t ldc,
+                              int out_type, int schedule, int splits, void *workspace,
+                              int64_t workspace_bytes, hipStream_t stream) {
+    return splitk(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, splits,
+                  kCallerWorkspace, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gemm_ex_splitk_noalloc(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
+                                      int64_t lda, const void *B, int64_t ldb, int trans_b, void *C,
+                                      int64_t ldc, int out_type, int schedule, int splits,
+                                      hipStream_t stream) {
+    return splitk(dtype, M, N, K, A, lda, B, ldb, trans_b, C, ldc, out_type, schedule, splits,
+                  kStaticScratch, nullptr, 0, stream);
 }
 
 extern "C" int gemm_f16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
@@ -330,6 +404,9 @@ extern "C" const char *gemm_status_string(int status) {
         case GEMM_EALIGN: return "GEMM_EALIGN: pointer or leading dimension not 16-byte aligned";
         case GEMM_EUNSUPPORTED: return "GEMM_EUNSUPPORTED: shape or size the kernel does not cover";
         case GEMM_EHIP: return "GEMM_EHIP: HIP launch failure (see hipGetLastError)";
+        case GEMM_ENOSCRATCH:
+            return "GEMM_ENOSCRATCH: split-K partials larger than the library's static scratch "
+                   "(GEMM_SPLITK_SCRATCH_BYTES)";
         default: return "unknown gemm_status";
     }
 }

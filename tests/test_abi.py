@@ -19,6 +19,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = mcs.header_functions()
     assert set(names) == {"gemm_f16", "gemm_bf16", "gemm_fp8", "gemm_ex", "gemm_ex_splitk",
+                          "gemm_ex_splitk_noalloc",
                           "gemm_splitk_workspace_bytes", "gemm_auto_schedule", "gemm_splitk_suggest",
                           "gemm_kernel_info", "attention_fwd", "attention_fwd_ex",
                           "gemm_status_string"}
@@ -34,7 +35,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in (mcs.GEMM_OK, mcs.GEMM_EINVAL, mcs.GEMM_EALIGN, mcs.GEMM_EUNSUPPORTED, mcs.GEMM_EHIP):
+    for st in (mcs.GEMM_OK, mcs.GEMM_EINVAL, mcs.GEMM_EALIGN, mcs.GEMM_EUNSUPPORTED, mcs.GEMM_EHIP,
+               mcs.GEMM_ENOSCRATCH):
         assert mcs.gemm_status_string(st).startswith(("GEMM_OK", "GEMM_E"))
     assert "unknown" in mcs.gemm_status_string(12345)
 
@@ -258,3 +260,23 @@ def test_attention_argument_errors(lib):
     assert mcs.attention_fwd_ex(*ex, mcs.GEMM_SCHED_GENERIC, 0) == mcs.GEMM_EINVAL
     assert mcs.attention_fwd_ex(*ex, 9, 0) == mcs.GEMM_EINVAL
     assert mcs.attention_fwd_ex(f16, 0, 2, 64, 64, 128, 0, 0, 0, 0, 0, 0.125, 0, mcs.GEMM_SCHED_IN_PHASE, 0) == mcs.GEMM_OK
+
+
+def test_noalloc_splitk_validation_before_launch(lib):
+    """The allocation-free split K checks everything before touching a
+    device: its scratch limit (32 MiB of FP32 partials) included."""
+    nk = mcs.gemm_ex_splitk_noalloc
+    text = open(mcs.HEADER).read()
+    assert "#define GEMM_SPLITK_SCRATCH_BYTES ((int64_t)32 << 20)" in text
+    # 4 slices x 1024 x 2048 floats = 32 MiB: the largest that fits; 4 x 1024 x 2052 does not
+    assert mcs.gemm_splitk_workspace_bytes(0, 1024, 2048, 8192, 4) == mcs.GEMM_SPLITK_SCRATCH_BYTES
+    big = (1024, 2056, 8192, P, 8192, P, 8192, 1, P, 2056, 0)
+    assert nk(0, *big, mcs.GEMM_SCHED_AUTO, 4, 0) == mcs.GEMM_ENOSCRATCH
+    assert "scratch" in mcs.gemm_status_string(mcs.GEMM_ENOSCRATCH)
+    args = (1024, 1024, 1024, P, 1024, P, 1024, 1, P, 1024, 0)
+    assert nk(0, *args, mcs.GEMM_SCHED_GENERIC, 4, 0) == mcs.GEMM_EINVAL
+    assert nk(0, *args, mcs.GEMM_SCHED_AUTO, 0, 0) == mcs.GEMM_EINVAL
+    assert nk(0, *args, mcs.GEMM_SCHED_AUTO, 257, 0) == mcs.GEMM_EINVAL
+    bad = (1024, 1024, 1024, P + 2, 1024, P, 1024, 1, P, 1024, 0)
+    assert nk(0, *bad, mcs.GEMM_SCHED_AUTO, 4, 0) == mcs.GEMM_EALIGN
+    assert nk(0, 0, 8, 8, 0, 8, 0, 8, 1, 0, 8, 0, mcs.GEMM_SCHED_AUTO, 4, 0) == mcs.GEMM_OK   # empty
