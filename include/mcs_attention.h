@@ -62,11 +62,14 @@ int attention_fwd(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int64_
                   float *lse, float scale, int causal, hipStream_t stream);
 
 /*
- * attention_fwd_ex -- the same with the stage schedule chosen: AUTO or
- * GEMM_SCHED_PIPELINED (the two wave groups one stage apart, what
- * attention_fwd runs) or GEMM_SCHED_IN_PHASE (the same stages with the
- * groups in step: the ablation of the offset).  Other schedules:
- * GEMM_EINVAL.  Results are bitwise identical across the two.
+ * attention_fwd_ex -- the same with the schedule chosen: AUTO (what
+ * attention_fwd runs), GEMM_SCHED_PIPELINED (8 waves, two wave groups one
+ * stage apart: one group's matrix products overlap the other's softmax),
+ * GEMM_SCHED_IN_PHASE (the same stages with the groups in step: the ablation
+ * of the offset) or GEMM_SCHED_INTERLEAVED (4 waves, one per SIMD, 64 query
+ * rows each, every wave interleaving its own matrix products with its own
+ * softmax: half the LDS reads per query row).  Other schedules: GEMM_EINVAL.
+ * Results are bitwise identical across all of them.
  */
 int attention_fwd_ex(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int64_t seq_k,
                      int64_t head_dim, const void *Q, const void *K, const void *V, void *O,

@@ -36,6 +36,14 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
 
 
+# Per-source options.  The attention kernel's scores are finite or -inf (a
+# masked key) for finite inputs, so its maxima need no NaN quieting: without
+# it each fmaxf is one v_max instead of a max plus canonicalising copies.
+# The compiler's own MFMAs in it keep their accumulators in VGPRs (the 4-wave
+# form writes its O products itself, with AGPR accumulators).
+EXTRA = {"attention_fwd.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature; that warning is noise
@@ -48,7 +56,8 @@ def _run(cmd):
 def device_asm(src: str, out: str, defines=()) -> str:
     """Write the gfx950 assembly of one source file of csrc/ to ``out``
     (``defines``: extra -D options, e.g. ["-DMCS_STAGGER=1"] for the race-stress build)."""
-    _run([HIPCC, *COMMON, *defines, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out])
+    _run([HIPCC, *COMMON, *EXTRA.get(src, []), *defines, "--cuda-device-only", "-S", os.path.join(CSRC, src),
+          "-o", out])
     return out
 
 
@@ -61,7 +70,7 @@ def build(asm_dir: str | None = None, jobs: int = 4) -> str:
     def compile_one(job):
         src, objdir, defs = job
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        _run([HIPCC, *COMMON, *defs, "-c", os.path.join(CSRC, src), "-o", obj])
+        _run([HIPCC, *COMMON, *EXTRA.get(src, []), *defs, "-c", os.path.join(CSRC, src), "-o", obj])
         if asm_dir and not defs:
             os.makedirs(asm_dir, exist_ok=True)
             device_asm(src, os.path.join(asm_dir, src.replace(".hip", f"-{ARCH}.s")))

@@ -19,9 +19,10 @@
 // softmax stage of the other:
 //   0  MFMA   S(i+1) = Q K(i+1)^T; the V(i) fragments are read into the
 //             registers of the K fragments as those are used (half after
-//             the first two d-chunks, half after the last); wait for block i+2
+//             the first two d-chunks, half after the last); the copies of
+//             block i+3 go out with the first half; wait for block i+2
 //   1  VALU   O *= alpha(i); row max of S(i+1): m(i+1),
-//             alpha(i+1) = 2^(m(i) - m(i+1)); copies of block i+3
+//             alpha(i+1) = 2^(m(i) - m(i+1))
 //   2  MFMA   O += P(i) V(i); the K(i+2) fragments read the same way
 //   3  VALU   P(i+1) = 2^(c S(i+1) - m(i+1)) rounded to the operand type,
 //             l = alpha(i+1) l + row sums
@@ -38,13 +39,15 @@
 // at one chunk is conflict-free); V rows at c ^ 2(row & 7) (each half-wave
 // of a transposing ds_read_b64_tr_b16 touches 8 rows x 32 bytes, distinct
 // banks).  Waits:
-//   * copy -> read: block i+2 is copied during trip i-1 (stage 1) and each
-//     wave waits vmcnt(0) (block i+3 is not issued yet) at the end of stage 0
-//     of trip i; its K is read in stage 2 of trip i (the other group's wait
-//     is then two stages back), its V in trip i+2.
+//   * copy -> read: block i+2 is copied during trip i-1 (stage 0) and each
+//     wave waits vmcnt(4) (only block i+3's four copies, issued later in the
+//     same stage, may still fly) at the end of stage 0 of trip i; its K is
+//     read in stage 2 of trip i (the other group's wait is then two stages
+//     back), its V in trip i+2.
 //   * read -> refill: block i+3 goes into the slot of block i-1, whose V was
 //     last read in stage 0 of trip i-1 (lgkmcnt(0) before stage 1's
-//     barrier), five stages before the copies.
+//     barrier; the trailing group's one stage later), four stages before
+//     the copies.
 //
 // The probabilities are packed straight from the S accumulators: a lane
 // holds 4 consecutive keys of one row per 16-key tile, so the PV MFMA takes
@@ -172,9 +175,14 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                 cpV[i] = static_cast<uint32_t>(row * kRowBytes + (pch ^ (2 * (row & 7))) * 16);
             }
         }
+        // Window of block j: whole for the blocks of 64 existing keys, the
+        // tail's rows for a partial last block, empty past the last block the
+        // workgroup needs.  Compares and selects of uniform values only, so
+        // the descriptor stays on the scalar unit.
+        const int nfull = p.Sk / kKeys;
+        const uint32_t tail_rec = static_cast<uint32_t>(p.Sk - nfull * kKeys) * kRowBytes;
         auto copy_block = [&](int j) {
-            const int rows = j < nblk ? min(kKeys, p.Sk - j * kKeys) : 0;
-            const uint32_t nrec = rows > 0 ? static_cast<uint32_t>(rows * kRowBytes) : 0u;
+            const uint32_t nrec = j < nfull ? (j < nblk ? kKVTile : 0u) : (j < nblk ? tail_rec : 0u);
             const int64_t at = kbase + static_cast<int64_t>(j) * kKVTile;
             const i32x4 rk = make_rsrc(p.K + at, nrec);
             const i32x4 rv = make_rsrc(p.V + at, nrec);
@@ -274,9 +282,16 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         // first half: row maxima of S and the running shift m.  m moves only
         // when a row's maximum exceeds it by more than kLazy (log2 units): the
         // exponentials then stay below 2^kLazy, and O and l are rescaled by
-        // alpha = 2^(m_old - m_new) only in those rows (lazy rescaling).
+        // alpha = 2^(m_old - m_new) only in those rows (lazy rescaling).  Each
+        // lane first compares the maximum of its own 16 scores of the row (times
+        // c) with m + kLazy; only when some lane of the wave exceeds it does the
+        // wave combine the four lanes of each row (c > 0 and rounding is
+        // monotonic, so the largest lane product is the row maximum times c:
+        // the decision is the same as from the row maximum itself).
         auto softmax_max = [&]() {
             pin_s();
+            float lm[2];
+            bool up = false;
             for (int mt = 0; mt < 2; ++mt) {
                 // a tree of three-input maxima (depth 3, not a chain of 15)
                 const f32x4 *x = s[mt];
@@ -285,16 +300,20 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                 const float t2 = fmaxf(fmaxf(x[1][2], x[1][3]), x[2][0]);
                 const float t3 = fmaxf(fmaxf(x[2][1], x[2][2]), x[2][3]);
                 const float t4 = fmaxf(fmaxf(x[3][0], x[3][1]), x[3][2]);
-                float mx = fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), x[3][3]));
-                mx = row_reduce(mx, [](float a, float b) { return fmaxf(a, b); }) * p.c;
-                if (mx > m[mt] + kLazy) {
-                    alpha[mt] = __builtin_amdgcn_exp2f(m[mt] - mx);
-                    m[mt] = mx;
-                } else {
-                    alpha[mt] = 1.f;
-                }
-                asm volatile("" : "+v"(m[mt]), "+v"(alpha[mt]));
+                lm[mt] = fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), x[3][3])) * p.c;
+                up = up || lm[mt] > m[mt] + kLazy;
             }
+            alpha[0] = alpha[1] = 1.f;
+            if (__builtin_amdgcn_ballot_w64(up) != 0) {
+                for (int mt = 0; mt < 2; ++mt) {
+                    const float mx = row_reduce(lm[mt], [](float a, float b) { return fmaxf(a, b); });
+                    if (mx > m[mt] + kLazy) {
+                        alpha[mt] = __builtin_amdgcn_exp2f(m[mt] - mx);
+                        m[mt] = mx;
+                    }
+                }
+            }
+            asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(alpha[0]), "+v"(alpha[1]));
         };
         // second half: P = 2^(c S - m) in the operand type, running row sums
         auto softmax_exp = [&]() {
@@ -344,13 +363,14 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
 
         // one trip; kMasked: block i+1 may hold keys some row must not see
         auto trip = [&](int i, auto masked) {
-            // stage 0: S(i+1); first half of the V(i) fragments; wait for block i+2
-            qk([&] { read_v(i, 0, 1); }, [&] { read_v(i, 1, 2); });
+            // stage 0: S(i+1); the V(i) fragments; copies of block i+3 (issued
+            // among the MFMAs, off the softmax stages' critical path); wait for
+            // block i+2
+            qk([&] { read_v(i, 0, 1); copy_block(i + 3); }, [&] { read_v(i, 1, 2); });
             __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<0>();                // block i+2 (block i+3 is not issued yet)
+            wait_vmcnt<4>();                // block i+2 (only block i+3's four copies may fly)
             rendezvous(sg);
-            // stage 1: rescale O, rest of V(i), row max of S(i+1), copies of block i+3
-            copy_block(i + 3);
+            // stage 1: rescale O, row max of S(i+1)
             rescale();                      // by alpha(i), before softmax_max sets alpha(i+1)
             if constexpr (decltype(masked)::value) mask(i + 1);
             softmax_max();
@@ -408,6 +428,422 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
     }
 }
 
+// ---- the 4-wave form: one wave per SIMD, each interleaving its own matrix
+// work with its own softmax ------------------------------------------------
+//
+// Every wave of the 8-wave form reads the whole 64-key K and V block for its
+// 32 query rows: 256 KiB of LDS reads per CU per block, against 2,048 MFMA
+// cycles per SIMD.  Here a workgroup of 4 waves (one per SIMD, 512 registers
+// each: the O accumulators go to AGPRs) takes the same 256 query rows, 64 per
+// wave, so each byte read from LDS feeds twice the MFMAs (128 KiB per block).
+// With one wave per SIMD nothing runs beside a wave's softmax, so each wave
+// software-pipelines its own loop over key blocks j (the scheme "Two Waves,
+// One Stage Apart" compares against, within-wave interleaving):
+//   phase A   S(j+1) = Q K(j+1)^T (64 MFMAs, the K fragments streamed from
+//             LDS), each group of 4 MFMAs carrying a quarter row-tile of the
+//             exponentials of block j: P(j) = 2^(S'(j)) in the operand type,
+//             row sums l = alpha(j) l + sums
+//   phase B   O *= alpha(j) (only when a row's shift moved); O += P(j) V(j)
+//             (64 MFMAs, V fragments streamed), the first half carrying the
+//             row maxima of S(j+1) -> m(j+1), alpha(j+1), the second half the
+//             scaling S'(j+1) = c S(j+1) - m(j+1)
+// and one barrier per block (after the wave's LDS reads and its part of the
+// copies of block j+2 completed).  The copies of block j+3 go out during
+// phase A into the slot of block j-1, whose last reads (V(j-1), phase B of
+// block j-1) every wave finished before that barrier.  Same LDS layout,
+// fragment formats, MFMA order per output element and softmax arithmetic as
+// the 8-wave form, so the two give the same bits.
+constexpr int kW4Waves = 4;
+
+// O += x . y with the accumulator in AGPRs, where the 4-wave form keeps O
+// (128 registers per lane) so that its VGPRs hold the scores, P and the
+// operands (the compiler's own MFMAs, the score products, are built with
+// their accumulators in VGPRs).  The instruction is written out; the
+// compiler does not see it as an MFMA, so the form keeps every hazard of it
+// out of the compiler's reach by construction: x (V fragments, from LDS)
+// and y (P, from VALU work at least one phase earlier) are written long
+// before, O is read by a VALU only after mfma_drain, and an accumulator's
+// two products of a block are 32 MFMAs apart.
+template <int kElem>
+__device__ __forceinline__ void mfma_agpr(f32x4 &acc, i32x4 x, i32x4 y) {
+    if constexpr (kElem == kElemBF16)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
+    else
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(x), "v"(y));
+}
+
+// S = x . y (+ S) with the scores in VGPRs (the softmax reads them) and the
+// row operand y (the Q fragments) in AGPRs, so that the 4-wave form's Q
+// (64 registers per lane) and O both live in AGPRs and its VGPRs hold the
+// scores, P and the streamed operands.  Written out like mfma_agpr, with
+// the same care for what the compiler cannot see: the K fragments come from
+// LDS (the compiler waits for them), Q is written once before the loop, an
+// accumulator's products are 4 MFMAs apart, and the softmax reads S only
+// after at least 11 more instructions or an explicit mfma_drain.  kFirst
+// starts from zero (its result early-clobber: it is a new value).
+template <int kElem, bool kFirst>
+__device__ __forceinline__ void mfma_qk(f32x4 &acc, i32x4 x, i32x4 y) {
+    if constexpr (kFirst) {
+        if constexpr (kElem == kElemBF16)
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(x), "a"(y));
+        else
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(x), "a"(y));
+    } else {
+        if constexpr (kElem == kElemBF16)
+            asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(x), "a"(y));
+        else
+            asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(x), "a"(y));
+    }
+}
+
+// Wait states between an MFMA of mfma_agpr / mfma_qk writing its result and
+// a VALU (or v_accvgpr_read) reading it: more than the 18 a 16x16x32 MFMA
+// (8 passes) may need.  The scheduling
+// walls keep the compiler, which sees no dependence on the nops, from
+// moving the reads above them.
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int kElem, bool kCausal>
+__global__ void __launch_bounds__(kW4Waves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attention_fwd4_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[kKVSlots * kKVSlot];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, r16 = lane & 15;
+
+    int bh, qb;
+    attn_coords<kCausal>(p, blockIdx.x, bh, qb);
+    const int q0 = qb * kQRows;
+    const int wrow = q0 + 64 * wave;                           // this wave's first query row
+    const int64_t qbase = static_cast<int64_t>(bh) * p.Sq * kRowBytes;
+    const int64_t kbase = static_cast<int64_t>(bh) * p.Sk * kRowBytes;
+
+    int kend = p.Sk;
+    if constexpr (kCausal) kend = max(0, min(p.Sk, min(p.Sq, q0 + kQRows) + p.off));
+    const int nblk = (kend + kKeys - 1) / kKeys;
+
+    // Q fragments (MFMA row operand): rows wrow + 16rt + r16, d 32dc + 8g ..
+    i32x4 qf[4][4];
+    for (int rt = 0; rt < 4; ++rt) {
+        const int row = wrow + 16 * rt + r16;
+        const char *src = p.Q + qbase + static_cast<int64_t>(min(row, p.Sq - 1)) * kRowBytes + 16 * g;
+        for (int dc = 0; dc < 4; ++dc) {
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(src + 64 * dc);
+            qf[rt][dc] = row < p.Sq ? v : i32x4{0, 0, 0, 0};
+        }
+    }
+    // Q moves to its AGPRs here, well before the first score MFMA: the
+    // compiler does not pad a VALU write followed by an asm MFMA reading it
+    for (int rt = 0; rt < 4; ++rt)
+        for (int dc = 0; dc < 4; ++dc) asm volatile("" : "+a"(qf[rt][dc]));
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 2");
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x4 o[4][8];                                             // [rt][16-column tile of d]
+    for (int rt = 0; rt < 4; ++rt)
+        for (int dt = 0; dt < 8; ++dt) o[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m[4], l[4], alpha[4];
+    for (int rt = 0; rt < 4; ++rt) { m[rt] = -INFINITY; l[rt] = 0.f; alpha[rt] = 1.f; }
+
+    if (nblk > 0) {
+        const uint32_t lds0 = lds_address(smem);
+        stagger_poison_lds<kKVSlots * kKVSlot, kW4Waves * 64>(lds0);
+        Stagger sg(p.stagger_seed);
+        // copy lanes: wave w moves pieces 4w .. 4w+3 (4 rows x 256 bytes each)
+        // of the K and of the V block
+        uint32_t cpK[4], cpV[4];
+        {
+            const int x = lane >> 4, pch = lane & 15;
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * (4 * wave + i) + x;
+                cpK[i] = static_cast<uint32_t>(row * kRowBytes + (pch ^ (row & 15)) * 16);
+                cpV[i] = static_cast<uint32_t>(row * kRowBytes + (pch ^ (2 * (row & 7))) * 16);
+            }
+        }
+        const int nfull = p.Sk / kKeys;
+        const uint32_t tail_rec = static_cast<uint32_t>(p.Sk - nfull * kKeys) * kRowBytes;
+        struct CopySet { i32x4 rk, rv; uint32_t dst; };
+        auto copy_set = [&](int j) {
+            const uint32_t nrec = j < nfull ? (j < nblk ? kKVTile : 0u) : (j < nblk ? tail_rec : 0u);
+            const int64_t at = kbase + static_cast<int64_t>(j) * kKVTile;
+            return CopySet{make_rsrc(p.K + at, nrec), make_rsrc(p.V + at, nrec),
+                           lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + 4 * wave * 1024};
+        };
+        // piece q (0..7) of this wave's share: K pieces 0..3, then V pieces 0..3
+        auto copy_piece = [&](const CopySet &cs, auto q) {
+            constexpr int kq = decltype(q)::value;
+            if constexpr (kq < 4) copy16<kq * 1024>(cs.rk, cs.dst, cpK[kq]);
+            else copy16<kKVTile + (kq - 4) * 1024>(cs.rv, cs.dst, cpV[kq - 4]);
+        };
+        auto copy_block = [&](int j) {
+            const CopySet cs = copy_set(j);
+            static_for<0, 8>([&](auto q) { copy_piece(cs, q); });
+        };
+
+        uint32_t kofs[4], vofs[8];
+        for (int dc = 0; dc < 4; ++dc)
+            kofs[dc] = static_cast<uint32_t>(r16 * kRowBytes + (((4 * dc + g) ^ r16) * 16));
+        {
+            const int rr = 4 * (g & 1) + (r16 >> 2);
+            const int base = (4 * g + (r16 >> 2)) * kRowBytes + 16 * ((r16 & 3) >> 1) + 8 * (r16 & 1);
+            for (int dt = 0; dt < 8; ++dt) vofs[dt] = static_cast<uint32_t>(base + 32 * (dt ^ rr));
+        }
+        // read bases of one block (one address add per lane base, kept opaque
+        // to the compiler; the rest of every read's address is an immediate)
+        auto k_bases = [&](uint32_t slot, uint32_t (&kb)[4]) {
+            for (int dc = 0; dc < 4; ++dc) {
+                kb[dc] = slot + kofs[dc];
+                asm volatile("" : "+v"(kb[dc]));
+            }
+        };
+        auto v_bases = [&](uint32_t slot, uint32_t (&vb)[8]) {
+            for (int dt = 0; dt < 8; ++dt) {
+                vb[dt] = slot + kKVTile + vofs[dt];
+                asm volatile("" : "+v"(vb[dt]));
+            }
+        };
+        auto k_frag = [&](const uint32_t (&kb)[4], int kt, int dc) { return lds_read128(kb[dc] + kt * 16 * kRowBytes); };
+        auto v_frag = [&](const uint32_t (&vb)[8], int dt, int c) {
+            const i32x2 lo = lds_read64_tr(vb[dt] + (32 * c) * kRowBytes);
+            const i32x2 hi = lds_read64_tr(vb[dt] + (32 * c + 16) * kRowBytes);
+            return i32x4{lo.x, lo.y, hi.x, hi.y};
+        };
+        auto slot_of = [&](int j) { return lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot; };
+
+        i32x4 pf[4][2];                                        // P [rt][32-key chunk], operand type
+        f32x4 s[4][4];                                         // S of one block [rt][16-key tile]
+        // row sums of P per row-tile, in the order ((p0 + p1) + (p2 + p3)) of the
+        // four 16-key tiles' parts: p0, then p0 + p1, then p2, then the total
+        float psum[4], ppart[4];
+
+        // P and the row sum part of tile (rt, kt) from the scaled scores
+        auto exp_tile = [&](int rt, int kt) {
+            f32x4 pr;
+            for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(s[rt][kt][e]);
+            const float part = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            if (kt == 0) psum[rt] = part;
+            else if (kt == 1) psum[rt] += part;
+            else if (kt == 2) ppart[rt] = part;
+            else psum[rt] += ppart[rt] + part;
+            const i32x2 h = pack4<kElem>(pr);
+            if (kt & 1) {
+                pf[rt][kt >> 1].z = h.x;
+                pf[rt][kt >> 1].w = h.y;
+            } else {
+                pf[rt][kt >> 1].x = h.x;
+                pf[rt][kt >> 1].y = h.y;
+            }
+        };
+        auto row_sums = [&]() {
+            for (int rt = 0; rt < 4; ++rt) l[rt] = l[rt] * alpha[rt] + psum[rt];
+        };
+        // S(j) = Q K(j)^T into s, K-tile column major.  The first MFMA of
+        // column kt overwrites it, so with kExp the previous block's scaled
+        // scores are turned into P one column ahead: group (kt, dc) exponentiates
+        // tile (dc, kt + 1) (column 0 was done at the end of the previous P V)
+        auto phase_a = [&](int j, auto exp_on, auto copy_on, const CopySet &cs) {
+            constexpr bool kExp = decltype(exp_on)::value, kCopy = decltype(copy_on)::value;
+            uint32_t kb[4];
+            k_bases(slot_of(j), kb);
+            i32x4 kf[4];
+            for (int dc = 0; dc < 4; ++dc) kf[dc] = k_frag(kb, 0, dc);
+            static_for<0, 4>([&](auto kt_) {
+                constexpr int kt = decltype(kt_)::value;
+                static_for<0, 4>([&](auto dc_) {
+                    constexpr int dc = decltype(dc_)::value;
+                    for (int rt = 0; rt < 4; ++rt) {
+                        if constexpr (dc == 0) mfma_qk<kElem, true>(s[rt][kt], kf[dc], qf[rt][dc]);
+                        else mfma_qk<kElem, false>(s[rt][kt], kf[dc], qf[rt][dc]);
+                    }
+                    if constexpr (kt < 3) kf[dc] = k_frag(kb, kt + 1, dc);
+                    if constexpr (kCopy && kt * 4 + dc < 8) copy_piece(cs, std::integral_constant<int, kt * 4 + dc>{});
+                    if constexpr (kExp && kt < 3) exp_tile(dc, kt + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            });
+            if constexpr (kExp) row_sums();
+        };
+        // keys past the end, and (causal) keys above the diagonal, score -inf
+        auto mask = [&](int j) {
+            const int k0 = j * kKeys;
+            bool need = k0 + kKeys > p.Sk;
+            if constexpr (kCausal) need = need || (k0 + kKeys - 1 > wrow + p.off);
+            if (need) {
+                mfma_drain();               // the last score MFMAs of the block
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int lim = kCausal ? min(p.Sk, wrow + 16 * rt + r16 + p.off + 1) : p.Sk;
+                    const int t = lim - k0 - 4 * g;
+                    for (int kt = 0; kt < 4; ++kt)
+                        for (int e = 0; e < 4; ++e)
+                            if (16 * kt + e >= t) s[rt][kt][e] = -INFINITY;
+                }
+            }
+        };
+        // lane-local row maxima of row-tile rt (times c) and the lazy test
+        auto local_max = [&](int rt) {
+            const f32x4 *x = s[rt];
+            const float t0 = fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]);
+            const float t1 = fmaxf(fmaxf(x[0][3], x[1][0]), x[1][1]);
+            const float t2 = fmaxf(fmaxf(x[1][2], x[1][3]), x[2][0]);
+            const float t3 = fmaxf(fmaxf(x[2][1], x[2][2]), x[2][3]);
+            const float t4 = fmaxf(fmaxf(x[3][0], x[3][1]), x[3][2]);
+            return fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), x[3][3])) * p.c;
+        };
+        // new shifts from the lane-local maxima (see the 8-wave form)
+        auto new_shift = [&](const float (&lm)[4]) {
+            bool up = false;
+            for (int rt = 0; rt < 4; ++rt) up = up || lm[rt] > m[rt] + kLazy;
+            for (int rt = 0; rt < 4; ++rt) alpha[rt] = 1.f;
+            if (__builtin_amdgcn_ballot_w64(up) != 0) {
+                for (int rt = 0; rt < 4; ++rt) {
+                    const float mx = row_reduce(lm[rt], [](float a, float b) { return fmaxf(a, b); });
+                    if (mx > m[rt] + kLazy) {
+                        alpha[rt] = __builtin_amdgcn_exp2f(m[rt] - mx);
+                        m[rt] = mx;
+                    }
+                }
+            }
+            for (int rt = 0; rt < 4; ++rt) asm volatile("" : "+v"(m[rt]), "+v"(alpha[rt]));
+        };
+        auto scale_tile = [&](int rt, int kt) {
+            const float ref = m[rt] == -INFINITY ? 0.f : m[rt];
+            for (int e = 0; e < 4; ++e) s[rt][kt][e] = __builtin_fmaf(s[rt][kt][e], p.c, -ref);
+        };
+        // O *= alpha, skipped when no row of the wave changed its shift
+        auto rescale = [&]() {
+            bool any = false;
+            for (int rt = 0; rt < 4; ++rt) any = any || alpha[rt] != 1.f;
+            // O is pinned to its AGPRs on both sides of the branch and goes
+            // through VGPRs only inside it (a VALU cannot multiply an AGPR):
+            // left to itself, the compiler moves all of O out of its AGPRs on
+            // every block, whether the branch is taken or not
+            for (int rt = 0; rt < 4; ++rt)
+                for (int dt = 0; dt < 8; ++dt) asm volatile("" : "+a"(o[rt][dt]));
+            if (__builtin_amdgcn_ballot_w64(any) == 0) return;
+            mfma_drain();
+            for (int rt = 0; rt < 4; ++rt)
+                for (int dt = 0; dt < 8; ++dt) {
+                    o[rt][dt] *= alpha[rt];
+                    asm volatile("" : "+a"(o[rt][dt]));
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_nop 1");        // the last AGPR writes, before an MFMA reads O
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // O += P(j) V(j).  With kMax the groups also carry the softmax of the
+        // next block's scores: lane-local maxima (groups 1, 3, 5, 7), the new
+        // shifts (after group 7), the scaling of all 16 tiles (groups 8-15,
+        // column 0 first) and column 0's P (groups 12-15, after the first
+        // half of P(j) -- chunk 0 -- has been consumed)
+        auto phase_b = [&](int j, auto max_on) {
+            constexpr bool kMax = decltype(max_on)::value;
+            uint32_t vb[8];
+            v_bases(slot_of(j), vb);
+            i32x4 vf[2];
+            vf[0] = v_frag(vb, 0, 0);
+            float lm[4];
+            static_for<0, 16>([&](auto u_) {
+                constexpr int u = decltype(u_)::value, c = u >> 3, dt = u & 7;
+                if constexpr (u + 1 < 16) vf[(u + 1) & 1] = v_frag(vb, (u + 1) & 7, (u + 1) >> 3);
+                const i32x4 cur = vf[u & 1];
+                for (int rt = 0; rt < 4; ++rt) mfma_agpr<kElem>(o[rt][dt], cur, pf[rt][c]);
+                if constexpr (kMax) {
+                    if constexpr (u < 8 && (u & 1)) lm[u >> 1] = local_max(u >> 1);
+                    if constexpr (u == 7) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        new_shift(lm);
+                    }
+                    if constexpr (u == 8 || u == 9) {
+                        scale_tile(2 * (u - 8), 0);
+                        scale_tile(2 * (u - 8) + 1, 0);
+                    }
+                    if constexpr (u >= 10) {
+                        // tiles (rt, kt) with kt >= 1, two per group: index 2(u-10), 2(u-10)+1 of 12
+                        constexpr int i0 = 2 * (u - 10), i1 = i0 + 1;
+                        scale_tile(i0 / 3, 1 + i0 % 3);
+                        scale_tile(i1 / 3, 1 + i1 % 3);
+                    }
+                    if constexpr (u >= 12) exp_tile(u - 12, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+
+        // ---- prologue: blocks 0-2 in flight; S(0) scaled, its column 0 of P
+        for (int j = 0; j < 3; ++j) copy_block(j);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<16>();                   // block 0 (this wave's pieces)
+        rendezvous(sg);                     // ... and everyone's
+        phase_a(0, std::false_type{}, std::false_type{}, copy_set(0));
+        mfma_drain();
+        mask(0);
+        {
+            float lm[4];
+            for (int rt = 0; rt < 4; ++rt) lm[rt] = local_max(rt);
+            new_shift(lm);
+            for (int rt = 0; rt < 4; ++rt)
+                for (int kt = 0; kt < 4; ++kt) scale_tile(rt, kt);
+            for (int rt = 0; rt < 4; ++rt) exp_tile(rt, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<8>();                    // block 1
+        wait_lgkmcnt<0>();
+        rendezvous(sg);
+
+        // one block: S(j+1) with the rest of P(j), then P(j) V(j) with the
+        // softmax of S(j+1)
+#pragma unroll 1
+        for (int j = 0; j + 1 < nblk; ++j) {
+            const CopySet cs = copy_set(j + 3);
+            phase_a(j + 1, std::true_type{}, std::true_type{}, cs);
+            mask(j + 1);
+            rescale();                      // by alpha(j), before phase_b sets alpha(j+1)
+            phase_b(j, std::true_type{});
+            __builtin_amdgcn_sched_barrier(0);
+            wait_lgkmcnt<0>();
+            wait_vmcnt<8>();                // block j+2 (only block j+3's eight copies may fly)
+            rendezvous(sg);
+        }
+        // ---- drain: the rest of the last block's P, its P V
+        for (int rt = 0; rt < 4; ++rt)
+            for (int kt = 1; kt < 4; ++kt) exp_tile(rt, kt);
+        row_sums();
+        rescale();
+        phase_b(nblk - 1, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<0>();                    // zero-window copies past the end
+        mfma_drain();                       // the last P V MFMAs, before O is read
+    }
+
+    // ---- O / l and lse
+    GemmParams out{};
+    out.C = p.O + qbase;
+    out.ldc = kHeadDim;
+    out.N = kHeadDim;
+    out.M = p.Sq;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const float lt = row_reduce(l[rt], [](float a, float b) { return a + b; });
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        for (int dt = 0; dt < 8; ++dt) o[rt][dt] *= inv;
+        const int row = wrow + 16 * rt + r16;
+        if (row >= p.Sq) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 v4[4] = {o[rt][4 * h], o[rt][4 * h + 1], o[rt][4 * h + 2], o[rt][4 * h + 3]};
+            store_strip<kElem == kElemBF16, false>(out, v4, row, 64 * h, lane);
+        }
+        if (p.lse && g == 0)
+            p.lse[static_cast<int64_t>(bh) * p.Sq + row] =
+                lt > 0.f ? (m[rt] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
 int attn_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_EHIP; }
 
 }  // namespace
@@ -422,7 +858,8 @@ int attention_launch(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int
     auto aligned16 = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; };
     if (dtype != GEMM_DTYPE_F16 && dtype != GEMM_DTYPE_BF16) return GEMM_EINVAL;
     if (causal != 0 && causal != 1) return GEMM_EINVAL;
-    if (schedule != GEMM_SCHED_AUTO && schedule != GEMM_SCHED_PIPELINED && schedule != GEMM_SCHED_IN_PHASE)
+    if (schedule != GEMM_SCHED_AUTO && schedule != GEMM_SCHED_PIPELINED && schedule != GEMM_SCHED_IN_PHASE &&
+        schedule != GEMM_SCHED_INTERLEAVED)
         return GEMM_EINVAL;
     if (batch < 0 || heads < 0 || seq_q < 0 || seq_k < 0 || head_dim < 0) return GEMM_EINVAL;
     if (!(scale > 0.f) || !std::isfinite(scale)) return GEMM_EINVAL;
@@ -454,6 +891,16 @@ int attention_launch(int dtype, int64_t batch, int64_t heads, int64_t seq_q, int
     prm.stagger_seed = next_stagger_seed();
     const bool offset = schedule != GEMM_SCHED_IN_PHASE;
     const void *fn = nullptr;
+    if (schedule == GEMM_SCHED_INTERLEAVED) {
+#define MCS_ATTN4(E, C) \
+    if ((dtype == GEMM_DTYPE_BF16) == (E == kElemBF16) && (causal != 0) == C) \
+        fn = reinterpret_cast<const void *>(&attention_fwd4_kernel<E, C>);
+        MCS_ATTN4(kElemF16, false) MCS_ATTN4(kElemF16, true) MCS_ATTN4(kElemBF16, false) MCS_ATTN4(kElemBF16, true)
+#undef MCS_ATTN4
+        void *args4[] = {&prm};
+        return attn_status(hipLaunchKernel(fn, dim3(static_cast<unsigned>(nq * groups)), dim3(kW4Waves * 64),
+                                           args4, 0, stream));
+    }
 #define MCS_ATTN(E, C, F) \
     if ((dtype == GEMM_DTYPE_BF16) == (E == kElemBF16) && (causal != 0) == C && offset == F) \
         fn = reinterpret_cast<const void *>(&attention_fwd_kernel<E, C, F>);

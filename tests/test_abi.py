@@ -256,7 +256,7 @@ def test_attention_argument_errors(lib):
     assert call(seq_q=0, Q=0, K=0, V=0, O=0) == mcs.GEMM_OK
     assert call(dtype=bf16, heads=0) == mcs.GEMM_OK
     ex = (f16, 1, 2, 64, 64, 128, P, P, P, P, P, 0.125, 0)
-    assert mcs.attention_fwd_ex(*ex, mcs.GEMM_SCHED_INTERLEAVED, 0) == mcs.GEMM_EINVAL
+    assert mcs.attention_fwd_ex(*ex, mcs.GEMM_SCHED_TILE128, 0) == mcs.GEMM_EINVAL
     assert mcs.attention_fwd_ex(*ex, mcs.GEMM_SCHED_GENERIC, 0) == mcs.GEMM_EINVAL
     assert mcs.attention_fwd_ex(*ex, 9, 0) == mcs.GEMM_EINVAL
     assert mcs.attention_fwd_ex(f16, 0, 2, 64, 64, 128, 0, 0, 0, 0, 0, 0.125, 0, mcs.GEMM_SCHED_IN_PHASE, 0) == mcs.GEMM_OK

@@ -29,27 +29,38 @@ def qkv(elem, B, H, Sq, Sk, D, seed, dist="normal"):
     return q, k[:, :, :Sk].copy(), v[:, :, :Sk].copy()
 
 
-def run_attention(elem, q, k, v, scale, causal, o_fill=-5.0):
-    """O (float64), lse (float64) and raw O bits from attention_fwd."""
+SCHED = {"auto": mcs.GEMM_SCHED_AUTO, "pipelined": mcs.GEMM_SCHED_PIPELINED, "in_phase": mcs.GEMM_SCHED_IN_PHASE,
+         "interleaved": mcs.GEMM_SCHED_INTERLEAVED}
+
+
+def run_attention(elem, q, k, v, scale, causal, o_fill=-5.0, sched="auto"):
+    """O (float64), lse (float64) and raw O bits from attention_fwd (sched "auto")
+    or attention_fwd_ex with the named schedule."""
     torch = _torch()
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
-    print(f"[gpu] attention elem={elem} B={B} H={H} Sq={Sq} Sk={Sk} D={D} causal={causal}", flush=True)
+    print(f"[gpu] attention elem={elem} B={B} H={H} Sq={Sq} Sk={Sk} D={D} causal={causal} sched={sched}",
+          flush=True)
     Q, _ = upload(q.reshape(-1, D), elem)
     K, _ = upload(k.reshape(-1, D) if Sk else np.zeros((1, D), np.uint16), elem)
     V, _ = upload(v.reshape(-1, D) if Sk else np.zeros((1, D), np.uint16), elem)
     O = torch.full((B * H * Sq * D,), o_fill, dtype=TORCH_DT[elem], device="cuda")
     L = torch.full((B * H * Sq,), 7.0, dtype=torch.float32, device="cuda")
-    st = mcs.attention_fwd(DT[elem], B, H, Sq, Sk, D, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
-                           L.data_ptr(), scale, int(causal), torch.cuda.current_stream().cuda_stream)
+    stream = torch.cuda.current_stream().cuda_stream
+    if sched == "auto":
+        st = mcs.attention_fwd(DT[elem], B, H, Sq, Sk, D, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                               L.data_ptr(), scale, int(causal), stream)
+    else:
+        st = mcs.attention_fwd_ex(DT[elem], B, H, Sq, Sk, D, Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                  O.data_ptr(), L.data_ptr(), scale, int(causal), SCHED[sched], stream)
     assert st == mcs.GEMM_OK, mcs.gemm_status_string(st)
     torch.cuda.synchronize()
     bits = O.cpu().view(torch.int16).numpy().view(np.uint16).reshape(B, H, Sq, D)
     return oracle.decode(bits, elem), L.cpu().double().numpy().reshape(B, H, Sq), bits
 
 
-def check(elem, q, k, v, scale, causal, rows=None, what=""):
-    o, lse, _ = run_attention(elem, q, k, v, scale, causal)
+def check(elem, q, k, v, scale, causal, rows=None, what="", sched="auto"):
+    o, lse, _ = run_attention(elem, q, k, v, scale, causal, sched=sched)
     B, H, Sq, D = q.shape
     Sk = k.shape[2]
     oref, lref, a, sabs = at.attention(q, k, v, elem, scale, causal, rows=rows)
@@ -71,21 +82,23 @@ SHAPES = [  # (B, H, Sq, Sk)
 ]
 
 
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("elem", ["f16", "bf16"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_shapes_every_element(shape, elem, causal):
+def test_shapes_every_element(shape, elem, causal, sched):
     B, H, Sq, Sk = shape
     q, k, v = qkv(elem, B, H, Sq, Sk, 128, seed=Sq * 7 + Sk)
-    check(elem, q, k, v, 1 / math.sqrt(128), causal, what=f"{shape} {elem} causal={causal}")
+    check(elem, q, k, v, 1 / math.sqrt(128), causal, what=f"{shape} {elem} causal={causal} {sched}", sched=sched)
 
 
-def test_uniform_values_and_other_scales():
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved"])
+def test_uniform_values_and_other_scales(sched):
     # scale 4: scores span hundreds in log2 units, so a running max that is not
     # the true row max overflows the exponentials
     for dist, scale in (("uniform", 0.3), ("normal", 0.02), ("normal", 0.25), ("normal", 4.0)):
         q, k, v = qkv("f16", 1, 2, 192, 320, 128, seed=3, dist=dist)
-        check("f16", q, k, v, scale, False, what=f"{dist} scale={scale}")
+        check("f16", q, k, v, scale, False, what=f"{dist} scale={scale}", sched=sched)
 
 
 def test_rows_without_keys_and_no_keys():
@@ -133,6 +146,21 @@ def test_in_phase_schedule_is_bitwise_identical(causal):
     torch.cuda.synchronize()
     assert np.array_equal(O.cpu().view(torch.int16).numpy().view(np.uint16).reshape(b0.shape), b0)
     assert np.array_equal(L.cpu().double().numpy().reshape(lse0.shape), lse0)
+
+
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_four_wave_form_is_bitwise_identical(elem, causal):
+    """The 4-wave form (one wave per SIMD, 64 query rows each) runs the same
+    MFMA sequence per output element and the same softmax arithmetic as the
+    8-wave form: the same bits of O and lse, on ragged sizes with masked
+    blocks, rows past the end and several key-block counts."""
+    for (B, H, Sq, Sk) in [(1, 3, 520, 777), (2, 2, 256, 64), (1, 1, 300, 129), (1, 2, 1000, 1100)]:
+        q, k, v = qkv(elem, B, H, Sq, Sk, 128, seed=Sq + Sk)
+        _, l8, b8 = run_attention(elem, q, k, v, 0.08, causal, sched="pipelined")
+        _, l4, b4 = run_attention(elem, q, k, v, 0.08, causal, sched="interleaved")
+        assert np.array_equal(b4, b8), (B, H, Sq, Sk, int((b4 != b8).sum()))
+        assert np.array_equal(l4, l8), (B, H, Sq, Sk)
 
 
 def test_torch_binding_matches_abi():

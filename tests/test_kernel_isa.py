@@ -173,3 +173,108 @@ def test_pipelined_lds_reads_per_layout(asm):
         assert (b128, tr) == want, f"{fn}: {b128} b128 + {tr} tr reads, want {want}"
         seen.add(trans_b)
     assert seen == {0, 1}
+
+
+def _function(asm_text, name_part):
+    """{symbol: [lines]} of every function whose symbol contains name_part."""
+    out, fn = {}, None
+    for line in asm_text.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            fn = m.group(1) if name_part in m.group(1) else None
+            if fn:
+                out[fn] = []
+            continue
+        if fn:
+            out[fn].append(line)
+            if "s_endpgm" in line:
+                fn = None
+    return out
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]$", tok) or re.match(r"([va])(\d+)$", tok)
+    if not m:
+        return set()
+    lo = int(m.group(2))
+    hi = int(m.group(3)) if m.lastindex == 3 else lo
+    return {(m.group(1), r) for r in range(lo, hi + 1)}
+
+
+def _mfma_hazards(lines):
+    """Wait-state violations around MFMAs, in program order (each instruction
+    one wait state, s_nop N counts N + 1): a VALU result read by an MFMA
+    fewer than 2 states later, and an MFMA result read by a VALU or store
+    fewer than 11 states later (8-pass 16x16x32 MFMA; the compiler pads
+    neither around inline-asm MFMAs)."""
+    bad, valu_w, mfma_w = [], [], []
+    for raw in lines:
+        t = raw.split(";")[0].strip()
+        if not t or t.startswith(".") or t.endswith(":"):
+            continue
+        op = t.split()[0]
+        ops = [x.strip().split()[0] for x in t[len(op):].split(",") if x.strip()]
+        cost = int(ops[0], 0) + 1 if op == "s_nop" else 1
+        dst = _regs(ops[0]) if ops else set()
+        srcs = set().union(*[_regs(x) for x in ops[1:]]) if len(ops) > 1 else set()
+        if op.startswith("v_mfma"):
+            if any(age < 2 and d & srcs for d, age in valu_w):
+                bad.append(("valu->mfma", t))
+            srcc = _regs(ops[3]) if len(ops) > 3 else set()
+            if any(age < 11 and d & srcs and d != srcc for d, age in mfma_w):
+                bad.append(("mfma->mfma", t))
+        elif op.startswith(("v_", "ds_write", "global_store", "buffer_store")):
+            reads = srcs | (dst if not op.startswith("v_") else set())
+            if any(age < 11 and d & reads for d, age in mfma_w):
+                bad.append(("mfma->valu", t))
+        valu_w = [(d, a + cost) for d, a in valu_w if a + cost < 2]
+        mfma_w = [(d, a + cost) for d, a in mfma_w if a + cost < 11]
+        if op.startswith("v_mfma"):
+            mfma_w.append((dst, 0))
+        elif op.startswith("v_") and dst:
+            valu_w.append((dst, 0))
+    return bad
+
+
+def test_attention_four_wave_kernel(asm):
+    """The 4-wave attention kernel writes its MFMAs as inline assembly (scores
+    in VGPRs, Q and O in AGPRs): no MFMA hazard anywhere in it, and per main
+    loop trip 128 MFMAs (QK and PV of one 64-key block), one barrier, and O
+    left in its AGPRs outside the rescale block: the moves there are the
+    few dozen the register allocator uses to park values, not the 128 O
+    reads that a rescale merged in VGPRs costs on every trip."""
+    fns = _function(asm["attention_fwd_kernel"], "attention_fwd4_kernel")
+    assert len(fns) == 4, sorted(fns)
+    for fn, lines in fns.items():
+        assert not _mfma_hazards(lines), (fn, _mfma_hazards(lines)[:3])
+        head = next(i for i, l in enumerate(lines) if "Loop Header" in l)
+        label = lines[head].split(":")[0]
+        end = next(i for i in range(head + 1, len(lines)) if lines[i].split()[:2] == ["s_branch", label])
+        body = lines[head:end + 1]
+        blocks, cur = [], []
+        for l in body:
+            if re.match(r"^(\.LBB\w+|; %bb\.\d+):", l):
+                blocks.append(cur)
+                cur = []
+            cur.append(l)
+        blocks.append(cur)
+        ops = [[l.strip().split()[0] for l in b if l.strip() and not l.strip().startswith((";", "."))]
+               for b in blocks]
+        flat = [o for b in ops for o in b]
+        assert sum(o.startswith("v_mfma") for o in flat) == 128, fn
+        assert flat.count("s_barrier") == 1, fn
+        assert not [o for o in flat if o.startswith(("scratch_", "buffer_store"))], fn
+        rescale = [b for b in ops if sum(o.startswith("v_accvgpr_write") for o in b) >= 128]
+        assert len(rescale) == 1, fn
+        rest = sum(o.startswith("v_accvgpr") for b in ops if b is not rescale[0] for o in b)
+        assert rest <= 96, f"{fn}: {rest} AGPR moves outside the rescale block"
+
+
+@pytest.mark.parametrize("kernel", sorted(EXPECT))
+def test_no_mfma_hazards(asm, kernel):
+    """No function of the file reads an MFMA operand or result too early (the
+    compiler pads its own MFMAs; this guards the inline-asm ones)."""
+    fns = _function(asm[kernel], "")
+    assert fns
+    for fn, lines in fns.items():
+        assert not _mfma_hazards(lines), (fn, _mfma_hazards(lines)[:3])

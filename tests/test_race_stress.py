@@ -124,7 +124,7 @@ def _attention_bits(lib, elem, q, k, v, scale, causal, sched):
     return O.cpu().view(torch.int16).numpy().view(np.uint16), L.cpu().numpy().view(np.uint32)
 
 
-@pytest.mark.parametrize("sched", ["pipelined", "in_phase"])
+@pytest.mark.parametrize("sched", ["pipelined", "in_phase", "interleaved"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("elem", ["f16", "bf16"])
 def test_attention_bitwise_under_stagger(elem, causal, sched):
