@@ -186,10 +186,17 @@ def bench_attention(a, w) -> int:
     outs = [torch.empty(w.B * w.H * w.Sq * w.D, dtype=tdt, device=dev) for _ in range(nrot)]
     lses = [torch.empty(w.B * w.H * w.Sq, dtype=torch.float32, device=dev) for _ in range(nrot)]
     dtype = {"f16": mcs.GEMM_DTYPE_F16, "bf16": mcs.GEMM_DTYPE_BF16}[w.dtype]
-    if a.schedule not in ("auto", "pipelined", "in_phase"):
-        print("attention runs the pipelined (groups one stage apart) or in_phase schedule", file=sys.stderr)
+    scheds = {"auto": mcs.GEMM_SCHED_PIPELINED, "pipelined": mcs.GEMM_SCHED_PIPELINED,
+              "in_phase": mcs.GEMM_SCHED_IN_PHASE, "interleaved": mcs.GEMM_SCHED_INTERLEAVED}
+    if a.schedule not in scheds:
+        print("attention runs the pipelined (8 waves, groups one stage apart), in_phase or interleaved "
+              "(4 waves) schedule", file=sys.stderr)
         return 2
-    sched = mcs.GEMM_SCHED_IN_PHASE if a.schedule == "in_phase" else mcs.GEMM_SCHED_PIPELINED
+    sched = scheds[a.schedule]
+    sched_name = {mcs.GEMM_SCHED_PIPELINED: "pipelined", mcs.GEMM_SCHED_IN_PHASE: "in_phase",
+                  mcs.GEMM_SCHED_INTERLEAVED: "interleaved"}[sched]
+    # counter records: the 8-wave kernel's (either offset) and the 4-wave kernel's
+    prof = "attention4" if sched == mcs.GEMM_SCHED_INTERLEAVED else "attention"
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
@@ -263,7 +270,7 @@ def bench_attention(a, w) -> int:
         n = heads * rows.size * (w.D + 1)
         check = {"rows": heads * rows.size, "elements": n, "outside_tolerance": bad, "pass": bad == 0}
 
-    traffic = traffic_for(w.name, "attention")
+    traffic = traffic_for(w.name, prof)
     peak = PEAK_TFLOPS[w.dtype]
     name = {"f16": "FP16", "bf16": "BF16"}[w.dtype]
     line = {
@@ -283,7 +290,7 @@ def bench_attention(a, w) -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Sq": w.Sq, "Sk": w.Sk, "D": w.D,
                    "causal": w.causal, "operands": w.dtype, "accumulate": "f32", "values": w.dist,
                    "seed": w.seed, "rotating_sets": nrot, "kernel": "attention",
-                   "schedule": "in_phase" if sched == mcs.GEMM_SCHED_IN_PHASE else "pipelined"},
+                   "schedule": sched_name},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "wall_s_timed": round(wall, 4),
         "settle_ms": round(settle_ms, 2),
@@ -291,7 +298,7 @@ def bench_attention(a, w) -> int:
         "settled_ms_per_launch": None if settle_last is None else round(settle_last, 6),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": traffic,
-                     "mfma_busy": mfma_busy_for(w.name, "attention")},
+                     "mfma_busy": mfma_busy_for(w.name, prof)},
         "cpu_baseline": cpu,
         "check": check,
     }

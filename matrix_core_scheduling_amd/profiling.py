@@ -34,7 +34,10 @@ KERNEL_SOURCES = {
     "interleaved": ("gemm_interleaved.hip", "device.h", "internal.h"),
     "tile128": ("gemm_tile128.hip", "device.h", "internal.h"),
     "attention": ("attention_fwd.hip", "device.h", "internal.h"),
+    "attention4": ("attention_fwd.hip", "device.h", "internal.h"),
 }
+# kernel-name filter of each schedule's counter rows
+KERNEL_NAMES = {"attention": "attention_fwd_kernel", "attention4": "attention_fwd4_kernel"}
 
 
 def _one(d: str, pattern: str) -> str:
@@ -146,7 +149,7 @@ def traffic_key(workload: str, schedule: str = "pipelined") -> str:
 
 def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib, schedule="pipelined",
             copy_kernel="copyBuffer", busy_dir=None) -> dict:
-    kernel = "attention_fwd" if schedule == "attention" else "gemm_" + schedule
+    kernel = KERNEL_NAMES.get(schedule, "gemm_" + schedule)
     copy_bytes = copy_mib * 2 ** 20
     cf = counters([copy_fetch_dir], copy_kernel)
     cw = counters([copy_write_dir], copy_kernel)
