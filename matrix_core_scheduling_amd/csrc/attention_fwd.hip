@@ -1,10 +1,10 @@
 // Attention forward pass for gfx950 in the stage abstraction of the GEMM
 // kernel: "Two Waves, One Stage Apart: Warp-Pipelining Triton GEMMs on AMD
-// Instinct", section "Beyond GEMM: FlashAttention" (Figure 11) describes the
-// loop -- per block of keys a QK product, the two halves of an online
-// softmax, a PV product and the movement of the next key/value blocks, the
-// QK of block i+1 issued before the PV of block i, one wave group's matrix
-// work overlapping the other group's softmax.  That page gives the schedule
+// Instinct", section "Beyond GEMM: FlashAttention" (Figure 11) lays out the
+// loop: for each block of keys, the score product, an online softmax in two
+// halves, the product with V, and the copies that bring in later K and V
+// blocks; the scores of block i+1 are computed before block i's product
+// with V, and while one wave group multiplies the other runs its softmax.  That page gives the schedule
 // for MI450 only, with no measurements; this is its MI355X form.
 //
 // Workgroup: 8 waves, 256 query rows of one (batch, head); wave w owns rows

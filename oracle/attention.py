@@ -4,8 +4,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this module.  It shares nothing with the GPU library.
 
 What it computes ("Two Waves, One Stage Apart: Warp-Pipelining Triton GEMMs
-on AMD Instinct", section "Beyond GEMM: FlashAttention", names the loop: QK
-and PV matrix products with an online softmax between them; the function is
+on AMD Instinct", section "Beyond GEMM: FlashAttention", names the loop: a
+score product, an online softmax, then the product with V; the function is
 the usual scaled dot-product attention, which an online softmax reaches up to
 rounding order).  For every batch b, head h and query row i:
 

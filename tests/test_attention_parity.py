@@ -188,3 +188,16 @@ def test_attention_workload(name):
     rows = np.unique(np.concatenate([rng.integers(0, w.Sq, 16), [0, 63, 64, 255, 256, w.Sq - 257, w.Sq - 1]]))
     o, lse = check(w.dtype, q, k, v, w.scale, w.causal, rows=rows, what=name)
     assert np.isfinite(o).all()
+
+
+@pytest.mark.parametrize("name", [n for n in si.ATTN_WORKLOADS if n != "attn_f16_b1h4s512d128"])
+def test_four_wave_form_full_size(name):
+    """The bench.py workloads at full size: the 4-wave form gives the 8-wave
+    form's bits for every element of O and lse (the 8-wave form is checked
+    against the oracle on sampled rows by test_attention_workload)."""
+    w = si.ATTN_WORKLOADS[name]
+    q, k, v = w.operands(0)
+    _, l8, b8 = run_attention(w.dtype, q, k, v, w.scale, w.causal, sched="pipelined")
+    _, l4, b4 = run_attention(w.dtype, q, k, v, w.scale, w.causal, sched="interleaved")
+    assert np.array_equal(b4, b8), (name, int((b4 != b8).sum()))
+    assert np.array_equal(l4, l8), name
