@@ -109,3 +109,31 @@ def assert_bit_exact(c_bits, cref, elem, out, what=""):
         bad = np.argwhere(~eq)
         i, j = bad[0]
         raise AssertionError(f"{what}: {len(bad)} elements differ; first at ({i},{j}) oracle {cref[i, j]}")
+
+
+# FP16 values whose sums land at the top of the FP16 range.  Each sum is an
+# integer below 2^24, so the FP32 accumulator holds it exactly.
+OVERFLOW_SUMS = [(32768, 32704, 31),          # 65503 -> 65504
+                 (32768, 32736),              # 65504, the largest finite FP16
+                 (32768, 32736, 15),          # 65519 -> 65504
+                 (32768, 32736, 16),          # 65520: the tie with 65536 goes to even, +inf
+                 (32768, 32768),              # 65536 -> +inf
+                 (32768,) * 32,               # 2^20 -> +inf
+                 (2048, 1, 0.5)]              # 2049.5 -> 2050 (a tie, to even)
+
+
+def overflow_operand(M: int, K: int, spread: bool = False) -> np.ndarray:
+    """A (M x K FP16 bits) whose row i holds the terms of OVERFLOW_SUMS[i % 7],
+    negated on every other block of 7 rows; with B all ones, C[i, :] is that
+    sum.  The terms sit at k = 0, 1, 2 ..., or with spread as far apart as K
+    allows (a quarter of K for up to four terms), so that a product split along
+    K over up to four slices adds them in its reduction."""
+    a = np.zeros((M, K), np.float64)
+    for i in range(M):
+        vals = OVERFLOW_SUMS[i % len(OVERFLOW_SUMS)]
+        sign = -1.0 if (i // len(OVERFLOW_SUMS)) % 2 else 1.0
+        step = (K // max(4, len(vals))) if spread else 1
+        a[i, np.arange(len(vals)) * step] = sign * np.asarray(vals, np.float64)
+    bits = oracle.round_to(a, "f16")
+    assert np.array_equal(oracle.decode(bits, "f16"), a)              # every term is an FP16 value
+    return bits

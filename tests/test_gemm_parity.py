@@ -10,7 +10,7 @@ import pytest
 import matrix_core_scheduling_amd as mcs
 import oracle
 import seeded_inputs as si
-from tests.gpu_util import assert_bit_exact, assert_within_tolerance, run, upload
+from tests.gpu_util import assert_bit_exact, assert_within_tolerance, overflow_operand, run, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -160,6 +160,23 @@ def test_output_rounds_to_nearest_even(K, elem, trans_b, sched):
     assert inexact > M * N // 4 and ties > 1000, (inexact, ties)
     _, bits = run(elem, M, N, K, a, b, trans_b, schedule=SCHEDS[sched])
     assert_bit_exact(bits, cref, elem, "same", f"RNE K={K} {elem} tb={trans_b} {sched}")
+
+
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved", "tile128", "generic"])
+@pytest.mark.parametrize("trans_b", [0, 1])
+def test_fp16_output_overflow_rounds_to_nearest_even(sched, trans_b):
+    """The FP16 epilogue at the end of the range, bit for bit: round to
+    nearest even carries 65520 and above to infinity with the sign of the sum
+    and keeps 65519 and below finite; the negatives mirror it."""
+    M, N, K = 256, 264, 64
+    a_bits = overflow_operand(M, K)
+    ones = np.full((N, K) if trans_b else (K, N), 0x3C00, np.uint16)
+    cref = oracle.gemm(a_bits, ones, "f16", trans_b, with_sabs=False)
+    want = oracle.decode(oracle.round_to(cref, "f16"), "f16")
+    assert np.isposinf(want).any() and np.isneginf(want).any()
+    assert (want == 65504.0).any() and (want == -65504.0).any() and (want == 2050.0).any()
+    _, bits = run("f16", M, N, K, a_bits, ones, trans_b, schedule=SCHEDS[sched])
+    assert_bit_exact(bits, cref, "f16", "same", f"FP16 overflow tb={trans_b} {sched}")
 
 
 # ---- closed forms ---------------------------------------------------------------

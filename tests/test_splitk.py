@@ -8,7 +8,8 @@ import pytest
 import matrix_core_scheduling_amd as mcs
 import oracle
 import seeded_inputs as si
-from tests.gpu_util import TORCH_DT, _torch, assert_bit_exact, assert_within_tolerance, out_elem, run, upload
+from tests.gpu_util import (TORCH_DT, _torch, assert_bit_exact, assert_within_tolerance, out_elem, overflow_operand,
+                             run, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +131,19 @@ def test_splitk_output_rounds_to_nearest_even(K, elem):
     for splits in (2, 3, 4):
         _, bits, _ = run_splitk(elem, M, N, K, a, b, 1, "same", mcs.GEMM_SCHED_AUTO, splits)
         assert_bit_exact(bits, cref, elem, "same", f"splitk RNE K={K} {elem} splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [2, 4])
+@pytest.mark.parametrize("sched", ["pipelined", "tile128"])
+def test_splitk_fp16_overflow_rounds_to_nearest_even(sched, splits):
+    """The reduction's FP16 conversion at the end of the range, bit for bit:
+    each row's terms sit in different K slices, so the sums that reach 65520
+    and beyond (+inf / -inf) or stay at 65519 and below (65504) are formed in
+    the reduction itself."""
+    M, N, K = 256, 264, 2048
+    a = overflow_operand(M, K, spread=True)
+    ones = np.full((N, K), 0x3C00, np.uint16)
+    cref = oracle.gemm(a, ones, "f16", 1, with_sabs=False)
+    schedule = {"pipelined": mcs.GEMM_SCHED_PIPELINED, "tile128": mcs.GEMM_SCHED_TILE128}[sched]
+    _, bits, _ = run_splitk("f16", M, N, K, a, ones, 1, "same", schedule, splits)
+    assert_bit_exact(bits, cref, "f16", "same", f"split-K FP16 overflow {sched} S={splits}")
