@@ -137,3 +137,65 @@ def overflow_operand(M: int, K: int, spread: bool = False) -> np.ndarray:
     bits = oracle.round_to(a, "f16")
     assert np.array_equal(oracle.decode(bits, "f16"), a)              # every term is an FP16 value
     return bits
+
+
+# Sums of FP16 terms at the bottom of the FP16 range, in units of 2^-24 (the
+# smallest subnormal).  With B = 0.5 the products are exact FP32 values and
+# C = sum / 2 in units of 2^-24: odd sums fall halfway between two FP16
+# subnormals.
+SUBNORMAL_SUMS = [(1,),                # 2^-25: tie between 0 and 2^-24 -> +0
+                  (3,),                # 1.5 * 2^-24: tie -> 2 * 2^-24 (even)
+                  (5,),                # 2.5 * 2^-24: tie -> 2 * 2^-24
+                  (1024, 1),           # 2^-15 + 2^-25: tie -> 2^-15 (512 units, even)
+                  (1023, 1023, 1),     # 1023.5 units: tie between 1023 (odd) and 1024 = 2^-14, normal
+                  (7, 9, 1024, 512),   # 776 units, exact
+                  (2047,)]             # 1023.5 units again, from one subnormal term
+
+
+def subnormal_operand(M: int, K: int) -> np.ndarray:
+    """A (M x K FP16 bits) whose row i holds the terms of SUBNORMAL_SUMS[i % 7]
+    times 2^-24 (subnormal or small normal FP16 values), negated on every
+    other block of 7 rows."""
+    a = np.zeros((M, K), np.float64)
+    for i in range(M):
+        vals = SUBNORMAL_SUMS[i % len(SUBNORMAL_SUMS)]
+        sign = -1.0 if (i // len(SUBNORMAL_SUMS)) % 2 else 1.0
+        a[i, :len(vals)] = sign * np.asarray(vals, np.float64) * 2.0 ** -24
+    bits = oracle.round_to(a, "f16")
+    assert np.array_equal(oracle.decode(bits, "f16"), a)              # every term is an FP16 value
+    return bits
+
+
+# BF16 terms in units of 2^-133 (the smallest BF16 subnormal; 2^-126 is the
+# smallest normal).  With B = 0.5 every product is an FP32 denormal and C is
+# the sum / 2 in units of 2^-133: odd sums fall halfway between two BF16
+# subnormals.
+BF16_SUBNORMAL_SUMS = [(1,), (3,), (5,), (255, 1), (127, 127, 1), (7, 9, 100), (300,)]
+
+
+def bf16_subnormal_operand(M: int, K: int) -> np.ndarray:
+    """A (M x K BF16 bits), row i the terms of BF16_SUBNORMAL_SUMS[i % 7] times
+    2^-133, negated on every other block of 7 rows."""
+    a = np.zeros((M, K), np.float64)
+    for i in range(M):
+        vals = BF16_SUBNORMAL_SUMS[i % len(BF16_SUBNORMAL_SUMS)]
+        sign = -1.0 if (i // len(BF16_SUBNORMAL_SUMS)) % 2 else 1.0
+        a[i, :len(vals)] = sign * np.asarray(vals, np.float64) * 2.0 ** -133
+    bits = oracle.round_to(a, "bf16")
+    assert np.array_equal(oracle.decode(bits, "bf16"), a)
+    return bits
+
+
+def fp8_subnormal_operand(M: int, K: int) -> np.ndarray:
+    """A (M x K FP8 E4M3 bytes): row i holds the E4M3 subnormals m * 2^-9,
+    m = 1 .. 7 (bit pattern m, exponent field 0), in a pattern that varies
+    with i, plus the smallest normal 2^-6 (pattern 8) on every third row, and
+    negated rows (sign bit) on every other block of 7 rows."""
+    a = np.zeros((M, K), np.uint8)
+    for i in range(M):
+        n = 1 + i % 7
+        ms = [(i + 3 * t) % 7 + 1 for t in range(n)]
+        if i % 3 == 0:
+            ms.append(8)
+        a[i, :len(ms)] = np.asarray(ms, np.uint8) | (0x80 if (i // 7) % 2 else 0)
+    return a

@@ -8,7 +8,7 @@ import pytest
 import matrix_core_scheduling_amd as mcs
 import oracle
 import seeded_inputs as si
-from tests.gpu_util import assert_bit_exact, assert_within_tolerance, run
+from tests.gpu_util import assert_bit_exact, assert_within_tolerance, fp8_subnormal_operand, run
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,22 @@ def test_interleaved_matches_pipelined_bitwise(out):
         assert np.array_equal(p, i), (M, N, K)
         t = run("fp8", M, N, K, a, b, 1, out=out, schedule=mcs.GEMM_SCHED_TILE128)[1]
         assert np.array_equal(p, t), (M, N, K)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved", "tile128", "generic"])
+def test_fp8_subnormal_operands(sched, out):
+    """E4M3 subnormal operands (m * 2^-9, m = 1 .. 7) enter the products at
+    their value: the sums are exact in FP32 and in BF16, so every element must
+    match the oracle bit for bit."""
+    M, N, K = 256, 264, 128
+    a = fp8_subnormal_operand(M, K)
+    assert ((a & 0x78) == 0).sum() > M and (a & 0x07).any()             # subnormal patterns present
+    one = np.full((N, K), 0x38, np.uint8)                              # B = 1.0, given N x K
+    cref = oracle.gemm(a, one, "fp8", 1, with_sabs=False)
+    schedule = mcs.GEMM_SCHED_GENERIC if sched == "generic" else SCHEDS[sched]
+    _, bits = run("fp8", M, N, K, a, one, 1, out=out, schedule=schedule)
+    assert_bit_exact(bits, cref, "fp8", out, f"FP8 subnormals out={out} {sched}")
 
 
 def test_nan_operand_propagates():

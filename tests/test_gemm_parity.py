@@ -10,7 +10,8 @@ import pytest
 import matrix_core_scheduling_amd as mcs
 import oracle
 import seeded_inputs as si
-from tests.gpu_util import assert_bit_exact, assert_within_tolerance, overflow_operand, run, upload
+from tests.gpu_util import (assert_bit_exact, assert_within_tolerance, bf16_subnormal_operand, overflow_operand,
+                             run, subnormal_operand, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -177,6 +178,36 @@ def test_fp16_output_overflow_rounds_to_nearest_even(sched, trans_b):
     assert (want == 65504.0).any() and (want == -65504.0).any() and (want == 2050.0).any()
     _, bits = run("f16", M, N, K, a_bits, ones, trans_b, schedule=SCHEDS[sched])
     assert_bit_exact(bits, cref, "f16", "same", f"FP16 overflow tb={trans_b} {sched}")
+
+
+@pytest.mark.parametrize("out", ["f32", "same"])
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved", "tile128", "generic"])
+def test_fp16_subnormal_operands_and_outputs(sched, out):
+    """The bottom of the FP16 range, bit for bit: subnormal operands enter the
+    products at their value (FP32 output: the exact sums), and subnormal FP16
+    outputs round to nearest even, ties included (2^-25 -> 0, 1.5 * 2^-24 ->
+    2^-23, 1023.5 * 2^-24 -> 2^-14)."""
+    M, N, K = 256, 264, 64
+    a = subnormal_operand(M, K)
+    half = np.full((N, K), 0x3800, np.uint16)                          # B = 0.5, given N x K
+    cref = oracle.gemm(a, half, "f16", 1, with_sabs=False)
+    _, bits = run("f16", M, N, K, a, half, 1, out=out, schedule=SCHEDS[sched])
+    assert_bit_exact(bits, cref, "f16", out, f"FP16 subnormals out={out} {sched}")
+
+
+@pytest.mark.parametrize("out", ["f32", "same"])
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved", "tile128", "generic"])
+def test_bf16_subnormal_operands_and_outputs(sched, out):
+    """BF16 subnormal operands whose products and sums are FP32 denormals, bit
+    for bit: FP32 output keeps the exact denormal sums, BF16 output rounds them
+    to nearest even (ties included)."""
+    M, N, K = 256, 264, 64
+    a = bf16_subnormal_operand(M, K)
+    half = np.full((N, K), 0x3F00, np.uint16)                          # B = 0.5, given N x K
+    cref = oracle.gemm(a, half, "bf16", 1, with_sabs=False)
+    assert (cref != 0).any() and (np.abs(cref) < 2.0 ** -126).any()
+    _, bits = run("bf16", M, N, K, a, half, 1, out=out, schedule=SCHEDS[sched])
+    assert_bit_exact(bits, cref, "bf16", out, f"BF16 subnormals out={out} {sched}")
 
 
 # ---- closed forms ---------------------------------------------------------------
