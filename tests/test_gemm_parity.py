@@ -210,6 +210,32 @@ def test_bf16_subnormal_operands_and_outputs(sched, out):
     assert_bit_exact(bits, cref, "bf16", out, f"BF16 subnormals out={out} {sched}")
 
 
+@pytest.mark.parametrize("elem", ["f16", "bf16"])
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved", "tile128", "generic"])
+def test_infinities_and_nan_reach_the_ieee_outputs(elem, sched):
+    """Special operands through the FP32 accumulator and the epilogue, class
+    for class against the oracle (IEEE binary64 products and sums): an
+    infinity times positive, negative and zero partners gives +inf, -inf and
+    NaN; +inf and -inf in one dot product give NaN; a NaN spoils its column.
+    The other outputs are integer sums below 2048, exact and bit for bit."""
+    M, N, K = 256, 264, 256
+    a = si.matrix_bits(elem, "int5", M, K, seed=70, stream=0)
+    b = si.matrix_bits(elem, "int5", N, K, seed=70, stream=1)                # N x K
+    pinf, ninf, nan = (0x7C00, 0xFC00, 0x7E00) if elem == "f16" else (0x7F80, 0xFF80, 0x7FC0)
+    a[3, 10] = pinf                     # row 3: sign of B[:, 10], NaN where it is 0
+    a[5, 20], a[5, 21] = pinf, ninf     # row 5: NaN where B[:, 20] and B[:, 21] have one sign
+    a[9, 40] = ninf                     # row 9: the opposite sign of B[:, 40], NaN where it is 0
+    b[7, 30] = nan                      # column 7: NaN in every row
+    cref = oracle.gemm(a, b, elem, 1, with_sabs=False)
+    want = oracle.decode(oracle.round_to(cref, elem), elem)
+    assert np.isnan(want).any() and np.isposinf(want).any() and np.isneginf(want).any()
+    c, _ = run(elem, M, N, K, a, b, 1, schedule=SCHEDS[sched])
+    for name, cls in (("NaN", np.isnan), ("+inf", np.isposinf), ("-inf", np.isneginf)):
+        assert np.array_equal(cls(c), cls(want)), (name, sched, np.argwhere(cls(c) != cls(want))[:3].tolist())
+    fin = np.isfinite(want)
+    assert np.array_equal(c[fin], want[fin]), sched
+
+
 # ---- closed forms ---------------------------------------------------------------
 
 @pytest.mark.parametrize("elem", ["f16", "bf16"])
