@@ -87,17 +87,37 @@ struct AttnParams {
 
 // Workgroup -> (batch*head, query block): each XCD takes a contiguous range,
 // so the query blocks of one head share that XCD's L2 copy of K and V.  With
-// causal masks the last query blocks of a head see the most keys; they are
-// dispatched first (kReverse), so the light blocks fill the tail.
-template <bool kReverse>
+// causal masks query block qb sees qb + 1 blocks of keys, so the order matters
+// for the tail: the range is taken in pairs of heads, and within a pair the
+// blocks go heaviest first, alternating the two heads (15 of head 2c, 15 of
+// head 2c+1, 14, 14, ...).  That is longest-first dispatch within 2 nq
+// workgroups, which keeps the two heads' K and V in L2 together; dispatching
+// one head after the other, heaviest first, leaves the last CUs of an XCD
+// about 10 % more work than the mean (list scheduling over 16 heads of 16
+// blocks on 32 CUs: 75 units against 68).  A last unpaired head keeps its
+// heaviest-first order, and so does every head when an XCD's range holds
+// fewer than two heads (pairs would then put the heavy halves of two heads on
+// one XCD and the light halves on the next).  Each (batch*head, query block)
+// is produced once.
+template <bool kCausal>
 __device__ __forceinline__ void attn_coords(const AttnParams &p, int wg, int &bh, int &qb) {
     const int total = p.nq * p.groups;
     const int xcd = wg & 7, j = wg >> 3;
     const int q = total >> 3, r = total & 7;
     const int v = xcd * q + min(xcd, r) + j;
-    bh = v / p.nq;
-    qb = v - bh * p.nq;
-    if constexpr (kReverse) qb = p.nq - 1 - qb;
+    if constexpr (kCausal) {
+        const int pair = v / (2 * p.nq), t = v - pair * 2 * p.nq;
+        if (q >= 2 * p.nq && 2 * pair + 1 < p.groups) {
+            bh = 2 * pair + (t & 1);
+            qb = p.nq - 1 - (t >> 1);
+        } else {
+            bh = v / p.nq;
+            qb = p.nq - 1 - (v - bh * p.nq);
+        }
+    } else {
+        bh = v / p.nq;
+        qb = v - bh * p.nq;
+    }
 }
 
 // Combine the values of lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes
