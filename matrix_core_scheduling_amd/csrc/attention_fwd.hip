@@ -477,13 +477,13 @@ constexpr int kW4Waves = 4;
 
 // O += x . y with the accumulator in AGPRs, where the 4-wave form keeps O
 // (128 registers per lane) so that its VGPRs hold the scores, P and the
-// operands (the compiler's own MFMAs, the score products, are built with
-// their accumulators in VGPRs).  The instruction is written out; the
-// compiler does not see it as an MFMA, so the form keeps every hazard of it
-// out of the compiler's reach by construction: x (V fragments, from LDS)
-// and y (P, from VALU work at least one phase earlier) are written long
-// before, O is read by a VALU only after mfma_drain, and an accumulator's
-// two products of a block are 32 MFMAs apart.
+// operands.  The instruction is written out; the compiler does not see it
+// as an MFMA and pads no wait states around it, so the form keeps every
+// hazard out of reach by construction: x (V fragments, from LDS) and y (P,
+// from VALU work at least one phase earlier) are written long before, O is
+// read by a VALU only after mfma_drain and written back (rescale) at least
+// two wait states before the next product, and an accumulator's two
+// products of a block are 32 MFMAs apart.
 template <int kElem>
 __device__ __forceinline__ void mfma_agpr(f32x4 &acc, i32x4 x, i32x4 y) {
     if constexpr (kElem == kElemBF16)
@@ -497,10 +497,12 @@ __device__ __forceinline__ void mfma_agpr(f32x4 &acc, i32x4 x, i32x4 y) {
 // (64 registers per lane) and O both live in AGPRs and its VGPRs hold the
 // scores, P and the streamed operands.  Written out like mfma_agpr, with
 // the same care for what the compiler cannot see: the K fragments come from
-// LDS (the compiler waits for them), Q is written once before the loop, an
-// accumulator's products are 4 MFMAs apart, and the softmax reads S only
-// after at least 11 more instructions or an explicit mfma_drain.  kFirst
-// starts from zero (its result early-clobber: it is a new value).
+// LDS (the compiler waits for them), Q is moved into its AGPRs right after
+// its load and followed by s_nop before any product reads it, an
+// accumulator's products are 4 MFMAs apart (the hardware interlocks that),
+// and the softmax reads S only after at least 11 more instructions or an
+// explicit mfma_drain.  kFirst starts from zero (its result early-clobber:
+// it is a new value).
 template <int kElem, bool kFirst>
 __device__ __forceinline__ void mfma_qk(f32x4 &acc, i32x4 x, i32x4 y) {
     if constexpr (kFirst) {
