@@ -239,17 +239,23 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                 for (int kt = 0; kt < 4; ++kt) kf[kt][dc] = lds_read128(a + kt * 16 * kRowBytes);
             }
         };
-        auto read_v = [&](int j, int c0, int c1) {
+        // V bases of block j, once for both halves of its reads (computing
+        // them per half had the compiler share the adds and copy them into
+        // each half's opaque register)
+        auto v_bases = [&](int j, uint32_t (&vb)[8]) {
             const uint32_t b = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + kKVTile;
             for (int dt = 0; dt < 8; ++dt) {
-                uint32_t a = b + vofs[dt];
-                asm volatile("" : "+v"(a));
+                vb[dt] = b + vofs[dt];
+                asm volatile("" : "+v"(vb[dt]));
+            }
+        };
+        auto read_v = [&](const uint32_t (&vb)[8], int c0, int c1) {
+            for (int dt = 0; dt < 8; ++dt)
                 for (int c = c0; c < c1; ++c) {
-                    const i32x2 lo = lds_read64_tr(a + (32 * c) * kRowBytes);
-                    const i32x2 hi = lds_read64_tr(a + (32 * c + 16) * kRowBytes);
+                    const i32x2 lo = lds_read64_tr(vb[dt] + (32 * c) * kRowBytes);
+                    const i32x2 hi = lds_read64_tr(vb[dt] + (32 * c + 16) * kRowBytes);
                     vf[dt][c] = i32x4{lo.x, lo.y, hi.x, hi.y};
                 }
-            }
         };
         // The MFMA stages run `mid` once half of their fragments are consumed:
         // reads into the registers those fragments held.
@@ -386,7 +392,8 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             // stage 0: S(i+1); the V(i) fragments; copies of block i+3 (issued
             // among the MFMAs, off the softmax stages' critical path); wait for
             // block i+2
-            qk([&] { read_v(i, 0, 1); copy_block(i + 3); }, [&] { read_v(i, 1, 2); });
+            uint32_t vb[8];
+            qk([&] { v_bases(i, vb); read_v(vb, 0, 1); copy_block(i + 3); }, [&] { read_v(vb, 1, 2); });
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<4>();                // block i+2 (only block i+3's four copies may fly)
             rendezvous(sg);
@@ -417,7 +424,11 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         for (; i + 1 < nblk; ++i) trip(i, std::true_type{});
         // ---- drain: the last block's alpha and P V
         rescale();
-        read_v(nblk - 1, 0, 2);
+        {
+            uint32_t vb[8];
+            v_bases(nblk - 1, vb);
+            read_v(vb, 0, 2);
+        }
         wait_lgkmcnt<0>();
         rendezvous(sg);
         pv(nothing, nothing);
