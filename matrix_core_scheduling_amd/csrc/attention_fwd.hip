@@ -249,6 +249,18 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                 asm volatile("" : "+v"(vb[dt]));
             }
         };
+        uint32_t vb[8];                                     // V bases of the block being read
+        auto read_v_piece = [&](int u) {
+            const int dt = u >> 1;
+            const i32x2 x = lds_read64_tr(vb[dt] + (16 * (u & 1)) * kRowBytes);
+            if (u & 1) {
+                vf[dt][0].z = x.x;
+                vf[dt][0].w = x.y;
+            } else {
+                vf[dt][0].x = x.x;
+                vf[dt][0].y = x.y;
+            }
+        };
         auto read_v = [&](const uint32_t (&vb)[8], int c0, int c1) {
             for (int dt = 0; dt < 8; ++dt)
                 for (int c = c0; c < c1; ++c) {
@@ -259,28 +271,64 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         };
         // The MFMA stages run `mid` once half of their fragments are consumed:
         // reads into the registers those fragments held.
-        auto qk = [&](auto mid, auto tail) {
+        // The score stage.  With `inter`, each MFMA of the second half is
+        // followed by one transposing read of the first half of the block's
+        // V fragments (a block of 16 reads would hold this wave's MFMAs back
+        // while it issues them); `side` (the copies) and `tail` follow.
+        auto qk = [&](auto inter, auto side, auto tail) {
+            constexpr bool kInter = decltype(inter)::value;
             for (int dc = 0; dc < 4; ++dc) {
+                if (dc == 2) __builtin_amdgcn_sched_barrier(0);
                 for (int mt = 0; mt < 2; ++mt)
-                    for (int kt = 0; kt < 4; ++kt)
+                    for (int kt = 0; kt < 4; ++kt) {
                         s[mt][kt] = mfma<kElem>(kf[kt][dc], qf[mt][dc],
                                                 dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mt][kt]);
-                if (dc == 1 || dc == 3) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (dc == 1) mid(); else tail();
-                    __builtin_amdgcn_sched_barrier(0);
+                        if constexpr (kInter) {
+                            if (dc >= 2) {
+                                const int u = 8 * (dc - 2) + 4 * mt + kt;     // 0 .. 15
+                                read_v_piece(u);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
+                    }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            side();
+            tail();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // The P V stage.  With `inter` (the block index of the K fragments to
+        // read), every second MFMA of the second half is followed by one read
+        // of the first half of those fragments, as in the score stage; the
+        // rest of them (`tail`) follows the stage's last MFMA.
+        auto pv = [&](auto inter, int jk, auto tail) {
+            constexpr bool kInter = decltype(inter)::value;
+            uint32_t kb[2];
+            if constexpr (kInter) {
+                const uint32_t b = lds0 + static_cast<uint32_t>(jk & (kKVSlots - 1)) * kKVSlot;
+                for (int dc = 0; dc < 2; ++dc) {
+                    kb[dc] = b + kofs[dc];
+                    asm volatile("" : "+v"(kb[dc]));
                 }
             }
-        };
-        auto pv = [&](auto mid, auto tail) {
             for (int c = 0; c < 2; ++c) {
+                if (c == 1) __builtin_amdgcn_sched_barrier(0);
                 for (int mt = 0; mt < 2; ++mt)
-                    for (int dt = 0; dt < 8; ++dt)
+                    for (int dt = 0; dt < 8; ++dt) {
                         o[mt][dt >> 2][dt & 3] = mfma<kElem>(vf[dt][c], pf[mt][c], o[mt][dt >> 2][dt & 3]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (c == 0) mid(); else tail();
-                __builtin_amdgcn_sched_barrier(0);
+                        if constexpr (kInter) {
+                            const int n = 8 * mt + dt;                          // 0 .. 15
+                            if (c == 1 && (n & 1)) {
+                                const int u = n >> 1, dc = u >> 2, kt = u & 3;  // piece 0 .. 7
+                                kf[kt][dc] = lds_read128(kb[dc] + kt * 16 * kRowBytes);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
+                    }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            tail();
+            __builtin_amdgcn_sched_barrier(0);
         };
         auto nothing = [] {};
         // keys past the end, and (causal) keys above the diagonal, score -inf
@@ -376,7 +424,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         rendezvous(sg);                     // ... and everyone's
         read_k(0, 0, 4);
         wait_lgkmcnt<0>();
-        qk(nothing, nothing);
+        qk(std::false_type{}, nothing, nothing);
         mask(0);
         softmax_max();
         softmax_exp();
@@ -392,8 +440,8 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             // stage 0: S(i+1); the V(i) fragments; copies of block i+3 (issued
             // among the MFMAs, off the softmax stages' critical path); wait for
             // block i+2
-            uint32_t vb[8];
-            qk([&] { v_bases(i, vb); read_v(vb, 0, 1); copy_block(i + 3); }, [&] { read_v(vb, 1, 2); });
+            v_bases(i, vb);
+            qk(std::true_type{}, [&] { copy_block(i + 3); }, [&] { read_v(vb, 1, 2); });
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<4>();                // block i+2 (only block i+3's four copies may fly)
             rendezvous(sg);
@@ -405,7 +453,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             wait_lgkmcnt<0>();
             rendezvous(sg);
             // stage 2: O += P(i) V(i); first half of the K(i+2) fragments
-            pv([&] { read_k(i + 2, 0, 2); }, [&] { read_k(i + 2, 2, 4); });
+            pv(std::true_type{}, i + 2, [&] { read_k(i + 2, 2, 4); });
             rendezvous(sg);
             // stage 3: P(i+1), row sums, K(i+2) fragments (read after S is
             // consumed, so S and the K fragments are not live together)
@@ -424,14 +472,11 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         for (; i + 1 < nblk; ++i) trip(i, std::true_type{});
         // ---- drain: the last block's alpha and P V
         rescale();
-        {
-            uint32_t vb[8];
-            v_bases(nblk - 1, vb);
-            read_v(vb, 0, 2);
-        }
+        v_bases(nblk - 1, vb);
+        read_v(vb, 0, 2);
         wait_lgkmcnt<0>();
         rendezvous(sg);
-        pv(nothing, nothing);
+        pv(std::false_type{}, 0, nothing);
         if (kOffset && !groupB) rendezvous(sg); // group A closes the offset
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                    // zero-window copies past the end
