@@ -441,11 +441,15 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             // among the MFMAs, off the softmax stages' critical path); wait for
             // block i+2
             v_bases(i, vb);
-            qk(std::true_type{}, [&] { copy_block(i + 3); }, [&] { read_v(vb, 1, 2); });
+            qk(std::true_type{}, [&] { copy_block(i + 3); }, nothing);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<4>();                // block i+2 (only block i+3's four copies may fly)
             rendezvous(sg);
-            // stage 1: rescale O, row max of S(i+1)
+            // stage 1: the second half of the V(i) fragments (this stage's
+            // arithmetic is light, and its end waits for LDS anyway); rescale
+            // O, row max of S(i+1)
+            read_v(vb, 1, 2);
+            __builtin_amdgcn_sched_barrier(0);
             rescale();                      // by alpha(i), before softmax_max sets alpha(i+1)
             if constexpr (decltype(masked)::value) mask(i + 1);
             softmax_max();
