@@ -201,16 +201,24 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         // the descriptor stays on the scalar unit.
         const int nfull = p.Sk / kKeys;
         const uint32_t tail_rec = static_cast<uint32_t>(p.Sk - nfull * kKeys) * kRowBytes;
-        auto copy_block = [&](int j) {
+        // The descriptors and LDS destination of block j's copies, and its
+        // four pieces of this wave (K pieces 0, 1, then V pieces 0, 1).
+        struct CopySet { i32x4 rk, rv; uint32_t dst; };
+        auto copy_set = [&](int j) {
             const uint32_t nrec = j < nfull ? (j < nblk ? kKVTile : 0u) : (j < nblk ? tail_rec : 0u);
             const int64_t at = kbase + static_cast<int64_t>(j) * kKVTile;
-            const i32x4 rk = make_rsrc(p.K + at, nrec);
-            const i32x4 rv = make_rsrc(p.V + at, nrec);
-            const uint32_t dst = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + 2 * wave * 1024;
-            copy16<0>(rk, dst, cpK[0]);
-            copy16<1024>(rk, dst, cpK[1]);
-            copy16<kKVTile>(rv, dst, cpV[0]);
-            copy16<kKVTile + 1024>(rv, dst, cpV[1]);
+            return CopySet{make_rsrc(p.K + at, nrec), make_rsrc(p.V + at, nrec),
+                           lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + 2 * wave * 1024};
+        };
+        auto copy_piece = [&](const CopySet &cs, int q) {
+            if (q == 0) copy16<0>(cs.rk, cs.dst, cpK[0]);
+            else if (q == 1) copy16<1024>(cs.rk, cs.dst, cpK[1]);
+            else if (q == 2) copy16<kKVTile>(cs.rv, cs.dst, cpV[0]);
+            else copy16<kKVTile + 1024>(cs.rv, cs.dst, cpV[1]);
+        };
+        auto copy_block = [&](int j) {
+            const CopySet cs = copy_set(j);
+            for (int q = 0; q < 4; ++q) copy_piece(cs, q);
         };
 
         // fragment read offsets within a slot
@@ -271,11 +279,13 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         };
         // The MFMA stages run `mid` once half of their fragments are consumed:
         // reads into the registers those fragments held.
-        // The score stage.  With `inter`, each MFMA of the second half is
-        // followed by one transposing read of the first half of the block's
-        // V fragments (a block of 16 reads would hold this wave's MFMAs back
-        // while it issues them); `side` (the copies) and `tail` follow.
-        auto qk = [&](auto inter, auto side, auto tail) {
+        // The score stage.  With `inter`, every fourth MFMA of the first half
+        // is followed by one of this wave's copies of a later block
+        // (`copies(q)`, q = 0 .. 3) and each MFMA of the second half by one
+        // transposing read of the first half of the block's V fragments (a
+        // block of 16 reads would hold this wave's MFMAs back while it issues
+        // them); `side` and `tail` follow.
+        auto qk = [&](auto inter, auto copies, auto side, auto tail) {
             constexpr bool kInter = decltype(inter)::value;
             for (int dc = 0; dc < 4; ++dc) {
                 if (dc == 2) __builtin_amdgcn_sched_barrier(0);
@@ -283,6 +293,13 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                     for (int kt = 0; kt < 4; ++kt) {
                         s[mt][kt] = mfma<kElem>(kf[kt][dc], qf[mt][dc],
                                                 dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mt][kt]);
+                        if constexpr (kInter) {
+                            const int n = 8 * dc + 4 * mt + kt;
+                            if (n < 16 && (n & 3) == 3) {            // copy piece n / 4 after MFMAs 3, 7, 11, 15
+                                copies(n >> 2);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
                         if constexpr (kInter) {
                             if (dc >= 2) {
                                 const int u = 8 * (dc - 2) + 4 * mt + kt;     // 0 .. 15
@@ -424,7 +441,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         rendezvous(sg);                     // ... and everyone's
         read_k(0, 0, 4);
         wait_lgkmcnt<0>();
-        qk(std::false_type{}, nothing, nothing);
+        qk(std::false_type{}, [](int) {}, nothing, nothing);
         mask(0);
         softmax_max();
         softmax_exp();
@@ -441,7 +458,8 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             // among the MFMAs, off the softmax stages' critical path); wait for
             // block i+2
             v_bases(i, vb);
-            qk(std::true_type{}, [&] { copy_block(i + 3); }, nothing);
+            const CopySet cs = copy_set(i + 3);
+            qk(std::true_type{}, [&](int q) { copy_piece(cs, q); }, nothing, nothing);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<4>();                // block i+2 (only block i+3's four copies may fly)
             rendezvous(sg);
