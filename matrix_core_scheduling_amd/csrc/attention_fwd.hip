@@ -13,41 +13,50 @@
 // 64.  Per block each wave runs 32 MFMAs 16x16x32 for S = Q K^T (its 32 rows
 // x 64 keys) and 32 for O += P V (32 rows x 128), FP32 accumulation.
 //
-// Stages of one trip (i = 0 .. blocks-2), each ended by a workgroup barrier;
-// group B runs one stage behind group A (an extra barrier on entry for B and
-// on exit for A, as in the GEMM), so each MFMA stage of one group overlaps a
-// softmax stage of the other:
-//   0  MFMA   S(i+1) = Q K(i+1)^T; the V(i) fragments are read into the
-//             registers of the K fragments as those are used (half after
-//             the first two d-chunks, half after the last); the copies of
-//             block i+3 go out with the first half; wait for block i+2
-//   1  VALU   O *= alpha(i); row max of S(i+1): m(i+1),
-//             alpha(i+1) = 2^(m(i) - m(i+1))
-//   2  MFMA   O += P(i) V(i); the K(i+2) fragments read the same way
-//   3  VALU   P(i+1) = 2^(c S(i+1) - m(i+1)) rounded to the operand type,
-//             l = alpha(i+1) l + row sums
-// (the operand reads sit in the MFMA stages: the softmax stages, not the
-// matrix stages, are the long ones)
-// with c = scale * log2(e).  A prologue computes S(0), P(0); a drain applies
-// alpha and P V of the last block; then O / l is stored with
-// lse = (m + log2 l) ln 2.
+// Two stages per trip (i = 0 .. blocks-2), each ended by a workgroup
+// barrier; group B runs one stage behind group A (an extra barrier on entry
+// for B and on exit for A, as in the GEMM), so the MFMA stage of one group
+// overlaps the softmax stage of the other:
+//   M  MFMA   S(i+1) = Q K(i+1)^T, then O += P(i) V(i) (64 MFMAs).  The
+//             fragment reads go out one after each MFMA, into registers the
+//             stage has just freed: the first half of the V(i) fragments
+//             during the second half of the score MFMAs (into the used K
+//             fragments' registers), the second half of V(i) during the
+//             first half of the P V MFMAs, and K(i+2) during the second
+//             half.  This wave's copies of K(i+4) and V(i+2) follow every
+//             fourth of the first 16 MFMAs; wait for the previous trip's.
+//   V  VALU   row max of S(i+1): m(i+1), alpha(i+1) = 2^(m(i) - m(i+1));
+//             O *= alpha(i+1); P(i+1) = 2^(c S(i+1) - m(i+1)) rounded to the
+//             operand type; l = alpha(i+1) l + row sums
+// with c = scale * log2(e).  The page's figure splits the softmax into two
+// stages between the two products; here both products share one stage and
+// the whole softmax the other, which halves the barriers per block and
+// pairs each group's 64 MFMAs with the other group's whole softmax.  The
+// sequence of operations on every accumulator is the same either way.  A
+// prologue computes S(0), P(0); a drain does P V of the last block; then
+// O / l is stored with lse = (m + log2 l) ln 2.
 //
-// LDS: a ring of four blocks [K | V] of 16 KiB each (64 keys x 256 bytes),
-// filled by buffer_load ... lds (all 8 waves, two 1-KiB pieces of K and two
-// of V each per block); keys past the end read as zeros and are masked.  K
-// rows store 16-byte chunk c at c ^ (row & 15) (the ds_read_b128 of 16 rows
-// at one chunk is conflict-free); V rows at c ^ 2(row & 7) (each half-wave
-// of a transposing ds_read_b64_tr_b16 touches 8 rows x 32 bytes, distinct
-// banks).  Waits:
-//   * copy -> read: block i+2 is copied during trip i-1 (stage 0) and each
-//     wave waits vmcnt(4) (only block i+3's four copies, issued later in the
-//     same stage, may still fly) at the end of stage 0 of trip i; its K is
-//     read in stage 2 of trip i (the other group's wait is then two stages
-//     back), its V in trip i+2.
-//   * read -> refill: block i+3 goes into the slot of block i-1, whose V was
-//     last read in stage 0 of trip i-1 (lgkmcnt(0) before stage 1's
-//     barrier; the trailing group's one stage later), four stages before
-//     the copies.
+// LDS: two rings of four 16-KiB slots (64 keys x 256 bytes), one for K
+// blocks and one for V blocks, filled by buffer_load ... lds (all 8 waves,
+// two 1-KiB pieces of each block per wave); keys past the end read as zeros
+// and are masked.  K rows store 16-byte chunk c at c ^ (row & 15) (the
+// ds_read_b128 of 16 rows at one chunk is conflict-free); V rows at
+// c ^ 2(row & 7) (each half-wave of a transposing ds_read_b64_tr_b16 touches
+// 8 rows x 32 bytes, distinct banks).  K(j) is read two trips before V(j)
+// (in the M stage of trip j-2 against trip j), so each has its own ring.
+// With global stage g (group A's stage g, group B's stage g-1; A's trip i
+// is stages 2i and 2i+1):
+//   * read -> refill: a wave's reads of the M stage complete before the
+//     barrier that ends its V stage (lgkmcnt(0)).  K(j) is read last by
+//     group B in stage 2j-3, done before barrier 2j-2; its slot takes
+//     K(j+4), copied in trip j (stage 2j for A, 2j+1 for B).  V(j) is read
+//     last in stage 2j+1, done before barrier 2j+2; V(j+4) is copied in
+//     trip j+2 (stage 2j+4 or later).
+//   * copy -> read: a wave waits for its copies of trip k (vmcnt(4): only
+//     trip k+1's four may still fly) at the end of its M stage of trip k+1,
+//     that is before barrier 2k+3 in group B and 2k+2 in group A.  Their
+//     first reader is group A in stage 2k+4 (K(k+4) in trip k+2, V(k+2) in
+//     trip k+2), after that barrier.
 //
 // The probabilities are packed straight from the S accumulators: a lane
 // holds 4 consecutive keys of one row per 16-key tile, so the PV MFMA takes
@@ -71,6 +80,8 @@ constexpr int kAttnWaves = 8;
 constexpr uint32_t kKVTile = kKeys * kRowBytes;            // 16 KiB
 constexpr uint32_t kKVSlot = 2 * kKVTile;                  // K | V
 constexpr int kKVSlots = 4;
+constexpr int kRing = 4;                                   // 8-wave form: K ring, V ring
+static_assert(2 * kRing * kKVTile == kKVSlots * kKVSlot, "both forms use 128 KiB of LDS");
 constexpr float kLazy = 8.f;                               // shift slack of the online softmax
 
 struct AttnParams {
@@ -183,6 +194,9 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         const uint32_t lds0 = lds_address(smem);
         stagger_poison_lds<kKVSlots * kKVSlot, kAttnWaves * 64>(lds0);
         Stagger sg(p.stagger_seed);
+        // two rings of kRing 16-KiB slots: K blocks, then V blocks
+        auto k_slot = [&](int j) { return lds0 + static_cast<uint32_t>(j & (kRing - 1)) * kKVTile; };
+        auto v_slot = [&](int j) { return lds0 + static_cast<uint32_t>(kRing + (j & (kRing - 1))) * kKVTile; };
         // copy lanes: wave w moves pieces 2w, 2w+1 (4 rows x 256 bytes each)
         // of the K and of the V block; lane (x, pch) fills physical chunk pch
         // of row x of a piece
@@ -201,24 +215,34 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         // the descriptor stays on the scalar unit.
         const int nfull = p.Sk / kKeys;
         const uint32_t tail_rec = static_cast<uint32_t>(p.Sk - nfull * kKeys) * kRowBytes;
-        // The descriptors and LDS destination of block j's copies, and its
-        // four pieces of this wave (K pieces 0, 1, then V pieces 0, 1).
-        struct CopySet { i32x4 rk, rv; uint32_t dst; };
-        auto copy_set = [&](int j) {
-            const uint32_t nrec = j < nfull ? (j < nblk ? kKVTile : 0u) : (j < nblk ? tail_rec : 0u);
-            const int64_t at = kbase + static_cast<int64_t>(j) * kKVTile;
-            return CopySet{make_rsrc(p.K + at, nrec), make_rsrc(p.V + at, nrec),
-                           lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + 2 * wave * 1024};
+        auto window = [&](int j) {
+            return j < nfull ? (j < nblk ? kKVTile : 0u) : (j < nblk ? tail_rec : 0u);
+        };
+        // The descriptors and LDS destinations of the copies of K block jk and
+        // V block jv, and this wave's four pieces of them (K pieces 0, 1, then
+        // V pieces 0, 1).
+        struct CopySet { i32x4 rk, rv; uint32_t dk, dv; };
+        auto copy_set = [&](int jk, int jv) {
+            const int64_t ak = kbase + static_cast<int64_t>(jk) * kKVTile;
+            const int64_t av = kbase + static_cast<int64_t>(jv) * kKVTile;
+            return CopySet{make_rsrc(p.K + ak, window(jk)), make_rsrc(p.V + av, window(jv)),
+                           k_slot(jk) + 2 * wave * 1024, v_slot(jv) + 2 * wave * 1024};
         };
         auto copy_piece = [&](const CopySet &cs, int q) {
-            if (q == 0) copy16<0>(cs.rk, cs.dst, cpK[0]);
-            else if (q == 1) copy16<1024>(cs.rk, cs.dst, cpK[1]);
-            else if (q == 2) copy16<kKVTile>(cs.rv, cs.dst, cpV[0]);
-            else copy16<kKVTile + 1024>(cs.rv, cs.dst, cpV[1]);
+            if (q == 0) copy16<0>(cs.rk, cs.dk, cpK[0]);
+            else if (q == 1) copy16<1024>(cs.rk, cs.dk, cpK[1]);
+            else if (q == 2) copy16<0>(cs.rv, cs.dv, cpV[0]);
+            else copy16<1024>(cs.rv, cs.dv, cpV[1]);
         };
-        auto copy_block = [&](int j) {
-            const CopySet cs = copy_set(j);
-            for (int q = 0; q < 4; ++q) copy_piece(cs, q);
+        auto copy_k = [&](int j) {
+            const CopySet cs = copy_set(j, j);
+            copy_piece(cs, 0);
+            copy_piece(cs, 1);
+        };
+        auto copy_v = [&](int j) {
+            const CopySet cs = copy_set(j, j);
+            copy_piece(cs, 2);
+            copy_piece(cs, 3);
         };
 
         // fragment read offsets within a slot
@@ -240,7 +264,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         // rest of every read's address is its immediate offset.
         // K fragments of d-chunks dc0 .. dc1-1, V fragments of key chunks c0 .. c1-1
         auto read_k = [&](int j, int dc0, int dc1) {
-            const uint32_t b = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot;
+            const uint32_t b = k_slot(j);
             for (int dc = dc0; dc < dc1; ++dc) {
                 uint32_t a = b + kofs[dc];
                 asm volatile("" : "+v"(a));
@@ -251,22 +275,23 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         // them per half had the compiler share the adds and copy them into
         // each half's opaque register)
         auto v_bases = [&](int j, uint32_t (&vb)[8]) {
-            const uint32_t b = lds0 + static_cast<uint32_t>(j & (kKVSlots - 1)) * kKVSlot + kKVTile;
+            const uint32_t b = v_slot(j);
             for (int dt = 0; dt < 8; ++dt) {
                 vb[dt] = b + vofs[dt];
                 asm volatile("" : "+v"(vb[dt]));
             }
         };
         uint32_t vb[8];                                     // V bases of the block being read
-        auto read_v_piece = [&](int u) {
+        // one transposing read: half u & 1 of the V fragment [u >> 1][c]
+        auto read_v_piece = [&](int c, int u) {
             const int dt = u >> 1;
-            const i32x2 x = lds_read64_tr(vb[dt] + (16 * (u & 1)) * kRowBytes);
+            const i32x2 x = lds_read64_tr(vb[dt] + (32 * c + 16 * (u & 1)) * kRowBytes);
             if (u & 1) {
-                vf[dt][0].z = x.x;
-                vf[dt][0].w = x.y;
+                vf[dt][c].z = x.x;
+                vf[dt][c].w = x.y;
             } else {
-                vf[dt][0].x = x.x;
-                vf[dt][0].y = x.y;
+                vf[dt][c].x = x.x;
+                vf[dt][c].y = x.y;
             }
         };
         auto read_v = [&](const uint32_t (&vb)[8], int c0, int c1) {
@@ -303,7 +328,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                         if constexpr (kInter) {
                             if (dc >= 2) {
                                 const int u = 8 * (dc - 2) + 4 * mt + kt;     // 0 .. 15
-                                read_v_piece(u);
+                                read_v_piece(0, u);
                                 __builtin_amdgcn_sched_barrier(0);
                             }
                         }
@@ -315,15 +340,18 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             __builtin_amdgcn_sched_barrier(0);
         };
         // The P V stage.  With `inter` (the block index of the K fragments to
-        // read), every second MFMA of the second half is followed by one read
-        // of the first half of those fragments, as in the score stage; the
-        // rest of them (`tail`) follows the stage's last MFMA.
-        auto pv = [&](auto inter, int jk, auto tail) {
+        // read), each MFMA of the first half is followed by one transposing
+        // read of the second half of the V fragments (the registers of the K
+        // fragments the score stage used up) and each MFMA of the second half
+        // by one read of the next K fragments (16 b128 reads: d-chunks 0 and 1
+        // into the registers of the V fragments of the first half, 2 and 3
+        // into those of the second half as its MFMAs use them).
+        auto pv = [&](auto inter, int jk) {
             constexpr bool kInter = decltype(inter)::value;
-            uint32_t kb[2];
+            uint32_t kb[4];
             if constexpr (kInter) {
-                const uint32_t b = lds0 + static_cast<uint32_t>(jk & (kKVSlots - 1)) * kKVSlot;
-                for (int dc = 0; dc < 2; ++dc) {
+                const uint32_t b = k_slot(jk);
+                for (int dc = 0; dc < 4; ++dc) {
                     kb[dc] = b + kofs[dc];
                     asm volatile("" : "+v"(kb[dc]));
                 }
@@ -335,16 +363,12 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                         o[mt][dt >> 2][dt & 3] = mfma<kElem>(vf[dt][c], pf[mt][c], o[mt][dt >> 2][dt & 3]);
                         if constexpr (kInter) {
                             const int n = 8 * mt + dt;                          // 0 .. 15
-                            if (c == 1 && (n & 1)) {
-                                const int u = n >> 1, dc = u >> 2, kt = u & 3;  // piece 0 .. 7
-                                kf[kt][dc] = lds_read128(kb[dc] + kt * 16 * kRowBytes);
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
+                            if (c == 0) read_v_piece(1, n);
+                            else kf[n & 3][n >> 2] = lds_read128(kb[n >> 2] + (n & 3) * 16 * kRowBytes);
+                            __builtin_amdgcn_sched_barrier(0);
                         }
                     }
             }
-            __builtin_amdgcn_sched_barrier(0);
-            tail();
             __builtin_amdgcn_sched_barrier(0);
         };
         auto nothing = [] {};
@@ -434,19 +458,26 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
                     for (int t = 0; t < 4; ++t) o[mt][h][t] *= alpha[mt];
         };
 
-        // ---- prologue (both groups in step): blocks 0-2 in flight, S(0), P(0)
-        for (int j = 0; j < 3; ++j) copy_block(j);
+        // ---- prologue (both groups in step): K blocks 0-3 and V blocks 0-1 in
+        // flight, S(0), P(0)
+        copy_k(0);
+        copy_k(1);
+        copy_v(0);
+        copy_k(2);
+        copy_v(1);
+        copy_k(3);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<8>();                    // block 0 (this wave's pieces)
+        wait_vmcnt<10>();                   // K(0) (this wave's pieces)
         rendezvous(sg);                     // ... and everyone's
         read_k(0, 0, 4);
         wait_lgkmcnt<0>();
         qk(std::false_type{}, [](int) {}, nothing, nothing);
         mask(0);
         softmax_max();
+        rescale();
         softmax_exp();
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<4>();                    // block 1
+        wait_vmcnt<4>();                    // K(1), V(0), K(2)
         rendezvous(sg);
         read_k(1, 0, 4);
         wait_lgkmcnt<0>();
@@ -454,33 +485,22 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
 
         // one trip; kMasked: block i+1 may hold keys some row must not see
         auto trip = [&](int i, auto masked) {
-            // stage 0: S(i+1); the V(i) fragments; copies of block i+3 (issued
-            // among the MFMAs, off the softmax stages' critical path); wait for
-            // block i+2
+            // MFMA stage: S(i+1) and O += P(i) V(i), the V(i) and K(i+2)
+            // fragments read among them; the copies of K(i+4) and V(i+2) go
+            // out in the first quarter; wait for the previous trip's copies
             v_bases(i, vb);
-            const CopySet cs = copy_set(i + 3);
+            const CopySet cs = copy_set(i + 4, i + 2);
             qk(std::true_type{}, [&](int q) { copy_piece(cs, q); }, nothing, nothing);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_vmcnt<4>();                // block i+2 (only block i+3's four copies may fly)
+            pv(std::true_type{}, i + 2);
+            wait_vmcnt<4>();                // K(i+3), V(i+1) (only this trip's four copies may fly)
             rendezvous(sg);
-            // stage 1: the second half of the V(i) fragments (this stage's
-            // arithmetic is light, and its end waits for LDS anyway); rescale
-            // O, row max of S(i+1)
-            read_v(vb, 1, 2);
-            __builtin_amdgcn_sched_barrier(0);
-            rescale();                      // by alpha(i), before softmax_max sets alpha(i+1)
+            // softmax stage: row max of S(i+1): m(i+1), alpha(i+1); O and l
+            // rescaled; P(i+1)
             if constexpr (decltype(masked)::value) mask(i + 1);
             softmax_max();
-            __builtin_amdgcn_sched_barrier(0);
-            wait_lgkmcnt<0>();
-            rendezvous(sg);
-            // stage 2: O += P(i) V(i); first half of the K(i+2) fragments
-            pv(std::true_type{}, i + 2, [&] { read_k(i + 2, 2, 4); });
-            rendezvous(sg);
-            // stage 3: P(i+1), row sums, K(i+2) fragments (read after S is
-            // consumed, so S and the K fragments are not live together)
+            rescale();
             softmax_exp();
-            wait_lgkmcnt<0>();
+            wait_lgkmcnt<0>();              // this wave's reads of the MFMA stage
             rendezvous(sg);
         };
         // leading blocks no row of the workgroup needs masked: every key
@@ -492,13 +512,11 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         for (; i + 1 < min(nplain, nblk); ++i) trip(i, std::false_type{});
 #pragma unroll 1
         for (; i + 1 < nblk; ++i) trip(i, std::true_type{});
-        // ---- drain: the last block's alpha and P V
-        rescale();
+        // ---- drain: P V of the last block
         v_bases(nblk - 1, vb);
         read_v(vb, 0, 2);
         wait_lgkmcnt<0>();
-        rendezvous(sg);
-        pv(std::false_type{}, 0, nothing);
+        pv(std::false_type{}, 0);
         if (kOffset && !groupB) rendezvous(sg); // group A closes the offset
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                    // zero-window copies past the end
