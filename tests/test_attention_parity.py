@@ -92,6 +92,20 @@ def test_shapes_every_element(shape, elem, causal, sched):
     check(elem, q, k, v, 1 / math.sqrt(128), causal, what=f"{shape} {elem} causal={causal} {sched}", sched=sched)
 
 
+# 2 .. 8 blocks of 64 keys, full and ragged last blocks: the K and V rings of
+# four slots wrap, and the trips near the end copy blocks past the last one
+BLOCK_COUNTS = [(nb, 64 * nb - (23 if nb % 2 else 0)) for nb in range(2, 9)]
+
+
+@pytest.mark.parametrize("sched", ["pipelined", "interleaved"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nb,sk", BLOCK_COUNTS, ids=lambda x: str(x))
+def test_every_block_count(nb, sk, causal, sched):
+    assert (sk + 63) // 64 == nb
+    q, k, v = qkv("f16", 1, 2, sk, sk, 128, seed=900 + nb)
+    check("f16", q, k, v, 1 / math.sqrt(128), causal, what=f"blocks={nb} Sk={sk}", sched=sched)
+
+
 @pytest.mark.parametrize("sched", ["pipelined", "interleaved"])
 def test_uniform_values_and_other_scales(sched):
     # scale 4: scores span hundreds in log2 units, so a running max that is not
