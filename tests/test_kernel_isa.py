@@ -38,23 +38,30 @@ SOURCES = {"gemm_pipelined_kernel": "gemm_pipelined.hip", "gemm_interleaved_kern
            "gemm_tile128_kernel": "gemm_tile128.hip", "attention_fwd_kernel": "attention_fwd.hip"}
 
 
-def loops(asm: str):
-    """{(kernel symbol, loop header): [instruction mnemonics]} of every loop."""
-    out, fn, cur = {}, None, None
-    for line in asm.splitlines():
+def loops(asm: str, innermost: bool = True):
+    """{(kernel symbol, loop header): [instruction mnemonics]} of every loop
+    (with innermost, only loops that hold no other loop: the main loops; a
+    persistent kernel's loop over its tiles holds them)."""
+    out, fn, cur, outer = {}, None, None, set()
+    lines = asm.splitlines()
+    for n, line in enumerate(lines):
         m = re.match(r"^(_Z\w+):", line)
         if m:
             fn, cur = m.group(1), None
             continue
         if re.match(r"^(\.LBB\w+|; %bb\.\d+):", line):
+            if "Parent Loop" in line and n + 1 < len(lines):
+                line = line + lines[n + 1]       # a nested loop's header: "Loop Header" on the next line
             h = re.search(r"Loop Header", line)
             i = re.search(r"in Loop: Header=(BB\w+)", line)
             cur = (fn, line.split(":")[0].lstrip(".L")) if h else ((fn, i.group(1)) if i else None)
+            if h and "Inner Loop Header" not in line:
+                outer.add(cur)
             continue
         t = line.strip()
         if cur and fn and t and not t.startswith((";", ".")):
             out.setdefault(cur, []).append(t.split()[0])
-    return out
+    return {k: v for k, v in out.items() if not (innermost and k in outer)}
 
 
 @pytest.fixture(scope="module")
