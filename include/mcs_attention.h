@@ -53,7 +53,8 @@ extern "C" {
  * a null pointer where data is needed; GEMM_EALIGN for Q, K, V or O not
  * 16-byte aligned or lse not 4-byte aligned; GEMM_EUNSUPPORTED for
  * another head_dim or sizes whose element counts reach 2^31 per head (or
- * more than 2^31-1 workgroups); GEMM_EHIP if the launch fails.  Empty
+ * more than 2^31-1 query tiles of 256 rows); GEMM_EHIP if the device query
+ * (compute units, read once per device) or the launch fails.  Empty
  * problems (batch, heads or seq_q zero) enqueue nothing; seq_k == 0 writes
  * O = 0 and lse = -inf.
  */
