@@ -98,3 +98,69 @@ def test_graph_replays_match_eager(schedule):
         if rep == 0:
             cref, sabs = oracle.gemm(a, b, "f16", 1, K=K, N=N)
             assert_within_tolerance(oracle.decode(got, "f16"), cref, sabs, "graph replay", out="f16")
+
+
+def _attention(Q, K, V, O, L, B, H, S, causal, stream):
+    import math
+    st = mcs.attention_fwd(mcs.GEMM_DTYPE_F16, B, H, S, S, 128, Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                           O.data_ptr(), L.data_ptr(), 1 / math.sqrt(128), causal, stream)
+    assert st == mcs.GEMM_OK, mcs.gemm_status_string(st)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+def test_attention_graph_replays_match_eager(causal):
+    """attention_fwd (the persistent kernel: one workgroup per CU, its tiles in
+    a fixed order) recorded into a graph and replayed with new Q, K, V in
+    between: O and lse of every replay equal an eager call, bit for bit; two
+    launches on two streams at once give the same bits as well."""
+    torch = pytest.importorskip("torch")
+    import oracle.attention as at
+    B, H, S = 2, 5, 700                     # ragged last tile and last key block; 30 tiles
+    print(f"[gpu] attention graph B={B} H={H} S={S} causal={causal}", flush=True)
+    Q, K, V = (torch.empty((B * H * S, 128), dtype=torch.float16, device="cuda") for _ in range(3))
+    O, Oe = torch.empty_like(Q), torch.empty_like(Q)
+    L, Le = (torch.empty(B * H * S, dtype=torch.float32, device="cuda") for _ in range(2))
+
+    def fill(seed):
+        out = []
+        for i, T in enumerate((Q, K, V)):
+            x = si.matrix_bits("f16", "normal", B * H * S, 128, seed=seed, stream=i)
+            T.copy_(torch.from_numpy(x.view(np.int16)).view(torch.float16))
+            out.append(x.reshape(B, H, S, 128))
+        return out
+
+    fill(8300)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _attention(Q, K, V, O, L, B, H, S, causal, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _attention(Q, K, V, O, L, B, H, S, causal, torch.cuda.current_stream().cuda_stream)
+    for rep in range(3):
+        q, k, v = fill(8301 + rep)
+        O.fill_(5.0)
+        L.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _attention(Q, K, V, Oe, Le, B, H, S, causal, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert torch.equal(O.view(torch.int16), Oe.view(torch.int16)), f"replay {rep}: O differs from eager"
+        assert torch.equal(L.view(torch.int32), Le.view(torch.int32)), f"replay {rep}: lse differs from eager"
+        if rep == 0:
+            oref, lref, a, sabs = at.attention(q, k, v, "f16", 1 / np.sqrt(128), bool(causal))
+            got = oracle.decode(_bits(O).reshape(B, H, S, 128), "f16")
+            assert at.within_tolerance(got, oref, a, sabs, 128, S, "f16").all(), "graph replay vs the oracle"
+    # two launches at once on two streams, same inputs: the eager bits
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [(torch.full_like(Q, 3.0), torch.full_like(L, 7.0)) for _ in streams]
+    torch.cuda.synchronize()
+    for s, (o, l) in zip(streams, outs):
+        _attention(Q, K, V, o, l, B, H, S, causal, s.cuda_stream)
+    torch.cuda.synchronize()
+    for o, l in outs:
+        assert torch.equal(o.view(torch.int16), Oe.view(torch.int16)), "O on a second stream differs"
+        assert torch.equal(l.view(torch.int32), Le.view(torch.int32)), "lse on a second stream differs"
