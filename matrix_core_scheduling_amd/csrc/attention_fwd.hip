@@ -52,7 +52,8 @@
 // and are masked.  The rings run on across tiles: block j of a tile sits in
 // slot (g0 + j) mod 4, g0 the number of blocks of the workgroup's earlier
 // tiles, so the next tile's first blocks land where this tile's would have
-// gone, under the same waits (the last trips' copies are the next tile's).  K rows store 16-byte chunk c at c ^ (row & 15) (the
+// gone, under the same waits (the last trips' copies are the next tile's).
+// K rows store 16-byte chunk c at c ^ (row & 15) (the
 // ds_read_b128 of 16 rows at one chunk is conflict-free); V rows at
 // c ^ 2(row & 7) (each half-wave of a transposing ds_read_b64_tr_b16 touches
 // 8 rows x 32 bytes, distinct banks).  K(j) is read two trips before V(j)
@@ -262,469 +263,463 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
     }
     // g0: ring position of the tile's block 0 (block j of the tile sits in
     // slot (g0 + j) mod 4 of each ring); pre: the previous tile already
-    // copied this tile's K blocks 0-2 and V block 0; settle: the previous
-    // tile's copies past its end (zero windows) may still be landing in
-    // this tile's slots
+    // copied this tile's K blocks 0-3 and V blocks 0-1 and loaded its Q;
+    // settle: the previous tile's copies past its end (zero windows) may
+    // still be landing in this tile's slots
     int g0 = 0;
     bool pre = false, settle = false;
 #pragma unroll 1
     for (int k = 0;; ++k) {
-    int bhn = bh, qbn = qb, nbn = 0;
-    const bool more = attn_tile<kCausal>(p, k + 1, bhn, qbn, nbn);
-    if (!more) {        // the last tile reloads its own Q below (in bounds, unused)
-        bhn = bh;
-        qbn = qb;
-        nbn = 0;
-    }
-    // copies past this tile's last block fetch the next tile's first blocks
-    // (K 0-3 and V 0-1, the last two from the tile's last trip)
-    const bool pf = more && nblk >= 2 && nbn >= 3;
-    // The lane index and the sequence lengths are opaque per tile: what
-    // derives from them is computed in the tile, not kept in registers
-    // across all of the workgroup's tiles
-    const int lane = fresh_lane();
-    int Sk = p.Sk, Sq = p.Sq, off = p.off;
-    asm volatile("" : "+s"(Sk), "+s"(Sq), "+s"(off));
-    const int g = lane >> 4, r16 = lane & 15;
-    const int q0 = qb * kQRows;
-    const int wrow = q0 + 32 * wave;                           // this wave's first query row
-    const int64_t qbase = static_cast<int64_t>(bh) * Sq * kRowBytes;
-    const int64_t kbase = static_cast<int64_t>(bh) * Sk * kRowBytes;
-
-    const int64_t kbase_n = static_cast<int64_t>(bhn) * Sk * kRowBytes;
-
-    f32x4 o[2][2][4];                                          // [mt][d half][16-column tile]
-    for (int mt = 0; mt < 2; ++mt)
-        for (int h = 0; h < 2; ++h)
-            for (int t = 0; t < 4; ++t) o[mt][h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, alpha[2] = {1.f, 1.f};
-
-    if (nblk > 0) {
-        // two rings of kRing 16-KiB slots: K blocks, then V blocks
-        auto slot_of = [&](int j) { return static_cast<uint32_t>((g0 + j) & (kRing - 1)); };
-        auto k_slot = [&](int j) { return lds0 + slot_of(j) * kKVTile; };
-        auto v_slot = [&](int j) { return lds0 + (kRing + slot_of(j)) * kKVTile; };
-        // copy lanes: wave w moves pieces 2w, 2w+1 (4 rows x 256 bytes each)
-        // of the K and of the V block; lane (x, pch) fills physical chunk pch
-        // of row x of a piece
-        uint32_t cpK[2], cpV[2];
-        {
-            const int x = lane >> 4, pch = lane & 15;
-            for (int i = 0; i < 2; ++i) {
-                const int row = 4 * (2 * wave + i) + x;
-                cpK[i] = static_cast<uint32_t>(row * kRowBytes + (pch ^ (row & 15)) * 16);
-                cpV[i] = static_cast<uint32_t>(row * kRowBytes + (pch ^ (2 * (row & 7))) * 16);
-            }
+        int bhn = bh, qbn = qb, nbn = 0;
+        const bool more = attn_tile<kCausal>(p, k + 1, bhn, qbn, nbn);
+        if (!more) {        // the last tile reloads its own Q below (in bounds, unused)
+            bhn = bh;
+            qbn = qb;
+            nbn = 0;
         }
-        // Window of block j: whole for the blocks of 64 existing keys, the
-        // tail's rows for a partial last block, empty past the last block the
-        // workgroup needs.  Compares and selects of uniform values only, so
-        // the descriptor stays on the scalar unit.
-        const int nfull = Sk / kKeys;
-        const uint32_t tail_rec = static_cast<uint32_t>(Sk - nfull * kKeys) * kRowBytes;
-        // Source offset and window of block j of this tile; with pf, blocks
-        // past the last are the next tile's blocks j - nblk (at most its
-        // third, so every one of them exists).  Selects of uniform values
-        // only: branches here would sit in every trip.
-        const int64_t xbase = pf ? kbase_n - static_cast<int64_t>(nblk) * kKVTile : kbase;
-        auto source = [&](int j, int64_t &at, uint32_t &nrec, auto tail) {
-            if constexpr (!decltype(tail)::value) {     // block j is the tile's own
-                at = kbase + static_cast<int64_t>(j) * kKVTile;
-                nrec = j < nfull ? kKVTile : tail_rec;
-                return;
-            }
-            const bool own = j < nblk;
-            at = (own ? kbase : xbase) + static_cast<int64_t>(j) * kKVTile;
-            const int t = own ? j : j - nblk;
-            const uint32_t w = t < nfull ? kKVTile : tail_rec;
-            nrec = (own || (pf && t < nbn)) ? w : 0u;
-        };
-        // The descriptors and LDS destinations of the copies of K block jk and
-        // V block jv, and this wave's four pieces of them (K pieces 0, 1, then
-        // V pieces 0, 1).
-        struct CopySet { i32x4 rk, rv; uint32_t dk, dv; };
-        auto copy_set = [&](int jk, int jv, auto tail) {
-            int64_t ak, av;
-            uint32_t nk, nv;
-            source(jk, ak, nk, tail);
-            source(jv, av, nv, tail);
-            return CopySet{make_rsrc(p.K + ak, nk), make_rsrc(p.V + av, nv),
-                           k_slot(jk) + 2 * wave * 1024, v_slot(jv) + 2 * wave * 1024};
-        };
-        auto copy_piece = [&](const CopySet &cs, int q) {
-            if (q == 0) copy16<0>(cs.rk, cs.dk, cpK[0]);
-            else if (q == 1) copy16<1024>(cs.rk, cs.dk, cpK[1]);
-            else if (q == 2) copy16<0>(cs.rv, cs.dv, cpV[0]);
-            else copy16<1024>(cs.rv, cs.dv, cpV[1]);
-        };
-        auto copy_k = [&](int j) {
-            const CopySet cs = copy_set(j, j, std::true_type{});
-            copy_piece(cs, 0);
-            copy_piece(cs, 1);
-        };
-        auto copy_v = [&](int j) {
-            const CopySet cs = copy_set(j, j, std::true_type{});
-            copy_piece(cs, 2);
-            copy_piece(cs, 3);
-        };
+        // copies past this tile's last block fetch the next tile's first blocks
+        // (K 0-3 and V 0-1, the last two from the tile's last trip)
+        const bool pf = more && nblk >= 2 && nbn >= 3;
+        // The lane index and the sequence lengths are opaque per tile: what
+        // derives from them is computed in the tile, not kept in registers
+        // across all of the workgroup's tiles
+        const int lane = fresh_lane();
+        int Sk = p.Sk, Sq = p.Sq, off = p.off;
+        asm volatile("" : "+s"(Sk), "+s"(Sq), "+s"(off));
+        const int g = lane >> 4, r16 = lane & 15;
+        const int q0 = qb * kQRows;
+        const int wrow = q0 + 32 * wave;                           // this wave's first query row
+        const int64_t qbase = static_cast<int64_t>(bh) * Sq * kRowBytes;
+        const int64_t kbase = static_cast<int64_t>(bh) * Sk * kRowBytes;
 
-        // fragment read offsets within a slot
-        uint32_t kofs[4], vofs[4 * 2];
-        for (int dc = 0; dc < 4; ++dc)
-            kofs[dc] = static_cast<uint32_t>(r16 * kRowBytes + (((4 * dc + g) ^ r16) * 16));
-        {
-            const int rr = 4 * (g & 1) + (r16 >> 2);               // (k-row) & 7 of this lane's reads
-            const int base = (4 * g + (r16 >> 2)) * kRowBytes + 16 * ((r16 & 3) >> 1) + 8 * (r16 & 1);
-            for (int dt = 0; dt < 8; ++dt) vofs[dt] = static_cast<uint32_t>(base + 32 * (dt ^ rr));
-        }
+        const int64_t kbase_n = static_cast<int64_t>(bhn) * Sk * kRowBytes;
 
-        i32x4 kf[4][4];     // K block fragments [16-key tile][32-d chunk]
-        i32x4 vf[8][2];     // V block fragments [16-d tile][32-key chunk]
-        i32x4 pf[2][2];     // P [mt][32-key chunk], operand type
-        f32x4 s[2][4];      // S [mt][16-key tile]
+        f32x4 o[2][2][4];                                          // [mt][d half][16-column tile]
+        for (int mt = 0; mt < 2; ++mt)
+            for (int h = 0; h < 2; ++h)
+                for (int t = 0; t < 4; ++t) o[mt][h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, alpha[2] = {1.f, 1.f};
 
-        // One address add per lane base (kept opaque to the compiler); the
-        // rest of every read's address is its immediate offset.
-        // K fragments of d-chunks dc0 .. dc1-1, V fragments of key chunks c0 .. c1-1
-        auto read_k = [&](int j, int dc0, int dc1) {
-            const uint32_t b = k_slot(j);
-            for (int dc = dc0; dc < dc1; ++dc) {
-                uint32_t a = b + kofs[dc];
-                asm volatile("" : "+v"(a));
-                for (int kt = 0; kt < 4; ++kt) kf[kt][dc] = lds_read128(a + kt * 16 * kRowBytes);
-            }
-        };
-        // V bases of block j, once for both halves of its reads (computing
-        // them per half had the compiler share the adds and copy them into
-        // each half's opaque register)
-        auto v_bases = [&](int j, uint32_t (&vb)[8]) {
-            const uint32_t b = v_slot(j);
-            for (int dt = 0; dt < 8; ++dt) {
-                vb[dt] = b + vofs[dt];
-                asm volatile("" : "+v"(vb[dt]));
-            }
-        };
-        uint32_t vb[8];                                     // V bases of the block being read
-        // one transposing read: half u & 1 of the V fragment [u >> 1][c]
-        auto read_v_piece = [&](int c, int u) {
-            const int dt = u >> 1;
-            const i32x2 x = lds_read64_tr(vb[dt] + (32 * c + 16 * (u & 1)) * kRowBytes);
-            if (u & 1) {
-                vf[dt][c].z = x.x;
-                vf[dt][c].w = x.y;
-            } else {
-                vf[dt][c].x = x.x;
-                vf[dt][c].y = x.y;
-            }
-        };
-        auto read_v = [&](const uint32_t (&vb)[8], int c0, int c1) {
-            for (int dt = 0; dt < 8; ++dt)
-                for (int c = c0; c < c1; ++c) {
-                    const i32x2 lo = lds_read64_tr(vb[dt] + (32 * c) * kRowBytes);
-                    const i32x2 hi = lds_read64_tr(vb[dt] + (32 * c + 16) * kRowBytes);
-                    vf[dt][c] = i32x4{lo.x, lo.y, hi.x, hi.y};
+        if (nblk > 0) {
+            // two rings of kRing 16-KiB slots: K blocks, then V blocks
+            auto slot_of = [&](int j) { return static_cast<uint32_t>((g0 + j) & (kRing - 1)); };
+            auto k_slot = [&](int j) { return lds0 + slot_of(j) * kKVTile; };
+            auto v_slot = [&](int j) { return lds0 + (kRing + slot_of(j)) * kKVTile; };
+            // copy lanes: wave w moves pieces 2w, 2w+1 (4 rows x 256 bytes each)
+            // of the K and of the V block; lane (x, pch) fills physical chunk pch
+            // of row x of a piece
+            uint32_t cpK[2], cpV[2];
+            {
+                const int x = lane >> 4, pch = lane & 15;
+                for (int i = 0; i < 2; ++i) {
+                    const int row = 4 * (2 * wave + i) + x;
+                    cpK[i] = static_cast<uint32_t>(row * kRowBytes + (pch ^ (row & 15)) * 16);
+                    cpV[i] = static_cast<uint32_t>(row * kRowBytes + (pch ^ (2 * (row & 7))) * 16);
                 }
-        };
-        // The MFMA stages run `mid` once half of their fragments are consumed:
-        // reads into the registers those fragments held.
-        // The score stage.  With `inter`, every fourth MFMA of the first half
-        // is followed by one of this wave's copies of a later block
-        // (`copies(q)`, q = 0 .. 3) and each MFMA of the second half by one
-        // transposing read of the first half of the block's V fragments (a
-        // block of 16 reads would hold this wave's MFMAs back while it issues
-        // them); `side` and `tail` follow.
-        auto qk = [&](auto inter, auto copies, auto side, auto tail) {
-            constexpr bool kInter = decltype(inter)::value;
-            for (int dc = 0; dc < 4; ++dc) {
-                if (dc == 2) __builtin_amdgcn_sched_barrier(0);
-                for (int mt = 0; mt < 2; ++mt)
-                    for (int kt = 0; kt < 4; ++kt) {
-                        s[mt][kt] = mfma<kElem>(kf[kt][dc], qf[mt][dc],
-                                                dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mt][kt]);
-                        if constexpr (kInter) {
-                            const int n = 8 * dc + 4 * mt + kt;
-                            if (n < 16 && (n & 3) == 3) {            // copy piece n / 4 after MFMAs 3, 7, 11, 15
-                                copies(n >> 2);
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
-                        }
-                        if constexpr (kInter) {
-                            if (dc >= 2) {
-                                const int u = 8 * (dc - 2) + 4 * mt + kt;     // 0 .. 15
-                                read_v_piece(0, u);
-                                __builtin_amdgcn_sched_barrier(0);
-                            }
-                        }
-                    }
             }
-            __builtin_amdgcn_sched_barrier(0);
-            side();
-            tail();
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        // The P V stage.  With `inter` (the block index of the K fragments to
-        // read), each MFMA of the first half is followed by one transposing
-        // read of the second half of the V fragments (the registers of the K
-        // fragments the score stage used up) and each MFMA of the second half
-        // by one read of the next K fragments (16 b128 reads: d-chunks 0 and 1
-        // into the registers of the V fragments of the first half, 2 and 3
-        // into those of the second half as its MFMAs use them).
-        auto pv = [&](auto inter, int jk) {
-            constexpr bool kInter = decltype(inter)::value;
-            uint32_t kb[4];
-            if constexpr (kInter) {
-                const uint32_t b = k_slot(jk);
+            // Window of block j: whole for the blocks of 64 existing keys, the
+            // tail's rows for a partial last block, empty past the last block the
+            // workgroup needs.  Compares and selects of uniform values only, so
+            // the descriptor stays on the scalar unit.
+            const int nfull = Sk / kKeys;
+            const uint32_t tail_rec = static_cast<uint32_t>(Sk - nfull * kKeys) * kRowBytes;
+            // Source offset and window of block j of this tile; with pf, blocks
+            // past the last are the next tile's blocks j - nblk (at most its
+            // third, so every one of them exists).  Selects of uniform values
+            // only: branches here would sit in every trip.
+            const int64_t xbase = pf ? kbase_n - static_cast<int64_t>(nblk) * kKVTile : kbase;
+            auto source = [&](int j, int64_t &at, uint32_t &nrec, auto tail) {
+                if constexpr (!decltype(tail)::value) {     // block j is the tile's own
+                    at = kbase + static_cast<int64_t>(j) * kKVTile;
+                    nrec = j < nfull ? kKVTile : tail_rec;
+                    return;
+                }
+                const bool own = j < nblk;
+                at = (own ? kbase : xbase) + static_cast<int64_t>(j) * kKVTile;
+                const int t = own ? j : j - nblk;
+                const uint32_t w = t < nfull ? kKVTile : tail_rec;
+                nrec = (own || (pf && t < nbn)) ? w : 0u;
+            };
+            // The descriptors and LDS destinations of the copies of K block jk and
+            // V block jv, and this wave's four pieces of them (K pieces 0, 1, then
+            // V pieces 0, 1).
+            struct CopySet { i32x4 rk, rv; uint32_t dk, dv; };
+            auto copy_set = [&](int jk, int jv, auto tail) {
+                int64_t ak, av;
+                uint32_t nk, nv;
+                source(jk, ak, nk, tail);
+                source(jv, av, nv, tail);
+                return CopySet{make_rsrc(p.K + ak, nk), make_rsrc(p.V + av, nv),
+                               k_slot(jk) + 2 * wave * 1024, v_slot(jv) + 2 * wave * 1024};
+            };
+            auto copy_piece = [&](const CopySet &cs, int q) {
+                if (q == 0) copy16<0>(cs.rk, cs.dk, cpK[0]);
+                else if (q == 1) copy16<1024>(cs.rk, cs.dk, cpK[1]);
+                else if (q == 2) copy16<0>(cs.rv, cs.dv, cpV[0]);
+                else copy16<1024>(cs.rv, cs.dv, cpV[1]);
+            };
+            auto copy_k = [&](int j) {
+                const CopySet cs = copy_set(j, j, std::true_type{});
+                copy_piece(cs, 0);
+                copy_piece(cs, 1);
+            };
+            auto copy_v = [&](int j) {
+                const CopySet cs = copy_set(j, j, std::true_type{});
+                copy_piece(cs, 2);
+                copy_piece(cs, 3);
+            };
+
+            // fragment read offsets within a slot
+            uint32_t kofs[4], vofs[4 * 2];
+            for (int dc = 0; dc < 4; ++dc)
+                kofs[dc] = static_cast<uint32_t>(r16 * kRowBytes + (((4 * dc + g) ^ r16) * 16));
+            {
+                const int rr = 4 * (g & 1) + (r16 >> 2);               // (k-row) & 7 of this lane's reads
+                const int base = (4 * g + (r16 >> 2)) * kRowBytes + 16 * ((r16 & 3) >> 1) + 8 * (r16 & 1);
+                for (int dt = 0; dt < 8; ++dt) vofs[dt] = static_cast<uint32_t>(base + 32 * (dt ^ rr));
+            }
+
+            i32x4 kf[4][4];     // K block fragments [16-key tile][32-d chunk]
+            i32x4 vf[8][2];     // V block fragments [16-d tile][32-key chunk]
+            i32x4 pf[2][2];     // P [mt][32-key chunk], operand type
+            f32x4 s[2][4];      // S [mt][16-key tile]
+
+            // One address add per lane base (kept opaque to the compiler); the
+            // rest of every read's address is its immediate offset.
+            // K fragments of d-chunks dc0 .. dc1-1, V fragments of key chunks c0 .. c1-1
+            auto read_k = [&](int j, int dc0, int dc1) {
+                const uint32_t b = k_slot(j);
+                for (int dc = dc0; dc < dc1; ++dc) {
+                    uint32_t a = b + kofs[dc];
+                    asm volatile("" : "+v"(a));
+                    for (int kt = 0; kt < 4; ++kt) kf[kt][dc] = lds_read128(a + kt * 16 * kRowBytes);
+                }
+            };
+            // V bases of block j, once for both halves of its reads (computing
+            // them per half had the compiler share the adds and copy them into
+            // each half's opaque register)
+            auto v_bases = [&](int j, uint32_t (&vb)[8]) {
+                const uint32_t b = v_slot(j);
+                for (int dt = 0; dt < 8; ++dt) {
+                    vb[dt] = b + vofs[dt];
+                    asm volatile("" : "+v"(vb[dt]));
+                }
+            };
+            uint32_t vb[8];                                     // V bases of the block being read
+            // one transposing read: half u & 1 of the V fragment [u >> 1][c]
+            auto read_v_piece = [&](int c, int u) {
+                const int dt = u >> 1;
+                const i32x2 x = lds_read64_tr(vb[dt] + (32 * c + 16 * (u & 1)) * kRowBytes);
+                if (u & 1) {
+                    vf[dt][c].z = x.x;
+                    vf[dt][c].w = x.y;
+                } else {
+                    vf[dt][c].x = x.x;
+                    vf[dt][c].y = x.y;
+                }
+            };
+            auto read_v = [&](const uint32_t (&vb)[8], int c0, int c1) {
+                for (int dt = 0; dt < 8; ++dt)
+                    for (int c = c0; c < c1; ++c) {
+                        const i32x2 lo = lds_read64_tr(vb[dt] + (32 * c) * kRowBytes);
+                        const i32x2 hi = lds_read64_tr(vb[dt] + (32 * c + 16) * kRowBytes);
+                        vf[dt][c] = i32x4{lo.x, lo.y, hi.x, hi.y};
+                    }
+            };
+            // The score products.  With `inter`, every fourth MFMA of the first
+            // half is followed by one of this wave's copies of later blocks
+            // (`copies(q)`, q = 0 .. 3) and each MFMA of the second half by one
+            // transposing read of the first half of the V fragments, into the
+            // registers of the K fragments already used (a block of 16 reads
+            // would hold this wave's MFMAs back while it issues them).
+            auto qk = [&](auto inter, auto copies) {
+                constexpr bool kInter = decltype(inter)::value;
                 for (int dc = 0; dc < 4; ++dc) {
-                    kb[dc] = b + kofs[dc];
-                    asm volatile("" : "+v"(kb[dc]));
+                    if (dc == 2) __builtin_amdgcn_sched_barrier(0);
+                    for (int mt = 0; mt < 2; ++mt)
+                        for (int kt = 0; kt < 4; ++kt) {
+                            s[mt][kt] = mfma<kElem>(kf[kt][dc], qf[mt][dc],
+                                                    dc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : s[mt][kt]);
+                            if constexpr (kInter) {
+                                const int n = 8 * dc + 4 * mt + kt;
+                                if (n < 16 && (n & 3) == 3) {            // copy piece n / 4 after MFMAs 3, 7, 11, 15
+                                    copies(n >> 2);
+                                    __builtin_amdgcn_sched_barrier(0);
+                                }
+                            }
+                            if constexpr (kInter) {
+                                if (dc >= 2) {
+                                    const int u = 8 * (dc - 2) + 4 * mt + kt;     // 0 .. 15
+                                    read_v_piece(0, u);
+                                    __builtin_amdgcn_sched_barrier(0);
+                                }
+                            }
+                        }
                 }
-            }
-            for (int c = 0; c < 2; ++c) {
-                if (c == 1) __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // The P V stage.  With `inter` (the block index of the K fragments to
+            // read), each MFMA of the first half is followed by one transposing
+            // read of the second half of the V fragments (the registers of the K
+            // fragments the score stage used up) and each MFMA of the second half
+            // by one read of the next K fragments (16 b128 reads: d-chunks 0 and 1
+            // into the registers of the V fragments of the first half, 2 and 3
+            // into those of the second half as its MFMAs use them).
+            auto pv = [&](auto inter, int jk) {
+                constexpr bool kInter = decltype(inter)::value;
+                uint32_t kb[4];
+                if constexpr (kInter) {
+                    const uint32_t b = k_slot(jk);
+                    for (int dc = 0; dc < 4; ++dc) {
+                        kb[dc] = b + kofs[dc];
+                        asm volatile("" : "+v"(kb[dc]));
+                    }
+                }
+                for (int c = 0; c < 2; ++c) {
+                    if (c == 1) __builtin_amdgcn_sched_barrier(0);
+                    for (int mt = 0; mt < 2; ++mt)
+                        for (int dt = 0; dt < 8; ++dt) {
+                            o[mt][dt >> 2][dt & 3] = mfma<kElem>(vf[dt][c], pf[mt][c], o[mt][dt >> 2][dt & 3]);
+                            if constexpr (kInter) {
+                                const int n = 8 * mt + dt;                          // 0 .. 15
+                                if (c == 0) read_v_piece(1, n);
+                                else kf[n & 3][n >> 2] = lds_read128(kb[n >> 2] + (n & 3) * 16 * kRowBytes);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            // keys past the end, and (causal) keys above the diagonal, score -inf
+            auto mask = [&](int j) {
+                const int k0 = j * kKeys;
+                bool need = k0 + kKeys > Sk;
+                if constexpr (kCausal) need = need || (k0 + kKeys - 1 > wrow + off);
+                if (need) {
+                    const int ln = fresh_lane();                      // (no lane value kept since the tile began)
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const int lim = kCausal ? min(Sk, wrow + 16 * mt + (ln & 15) + off + 1) : Sk;
+                        const int t = lim - k0 - 4 * (ln >> 4);       // first masked 16kt + e of this lane
+                        for (int kt = 0; kt < 4; ++kt)
+                            for (int e = 0; e < 4; ++e)
+                                if (16 * kt + e >= t) s[mt][kt][e] = -INFINITY;
+                    }
+                }
+            };
+            // The two softmax halves are pure arithmetic, which the compiler would
+            // otherwise move across the stage walls; each half starts from values
+            // passed through an empty asm, so its work stays in its stage.
+            auto pin_s = [&]() {
                 for (int mt = 0; mt < 2; ++mt)
-                    for (int dt = 0; dt < 8; ++dt) {
-                        o[mt][dt >> 2][dt & 3] = mfma<kElem>(vf[dt][c], pf[mt][c], o[mt][dt >> 2][dt & 3]);
-                        if constexpr (kInter) {
-                            const int n = 8 * mt + dt;                          // 0 .. 15
-                            if (c == 0) read_v_piece(1, n);
-                            else kf[n & 3][n >> 2] = lds_read128(kb[n >> 2] + (n & 3) * 16 * kRowBytes);
-                            __builtin_amdgcn_sched_barrier(0);
+                    for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[mt][kt]));
+            };
+            // first half: row maxima of S and the running shift m.  m moves only
+            // when a row's maximum exceeds it by more than kLazy (log2 units): the
+            // exponentials then stay below 2^kLazy, and O and l are rescaled by
+            // alpha = 2^(m_old - m_new) only in those rows (lazy rescaling).  Each
+            // lane first compares the maximum of its own 16 scores of the row (times
+            // c) with m + kLazy; only when some lane of the wave exceeds it does the
+            // wave combine the four lanes of each row (c > 0 and rounding is
+            // monotonic, so the largest lane product is the row maximum times c:
+            // the decision is the same as from the row maximum itself).
+            auto softmax_max = [&]() {
+                pin_s();
+                float lm[2];
+                bool up = false;
+                for (int mt = 0; mt < 2; ++mt) {
+                    // a tree of three-input maxima (depth 3, not a chain of 15)
+                    const f32x4 *x = s[mt];
+                    const float t0 = fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]);
+                    const float t1 = fmaxf(fmaxf(x[0][3], x[1][0]), x[1][1]);
+                    const float t2 = fmaxf(fmaxf(x[1][2], x[1][3]), x[2][0]);
+                    const float t3 = fmaxf(fmaxf(x[2][1], x[2][2]), x[2][3]);
+                    const float t4 = fmaxf(fmaxf(x[3][0], x[3][1]), x[3][2]);
+                    lm[mt] = fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), x[3][3])) * p.c;
+                    up = up || lm[mt] > m[mt] + kLazy;
+                }
+                alpha[0] = alpha[1] = 1.f;
+                if (__builtin_amdgcn_ballot_w64(up) != 0) {
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const float mx = row_reduce(lm[mt], [](float a, float b) { return fmaxf(a, b); });
+                        if (mx > m[mt] + kLazy) {
+                            alpha[mt] = __builtin_amdgcn_exp2f(m[mt] - mx);
+                            m[mt] = mx;
                         }
                     }
+                }
+                asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(alpha[0]), "+v"(alpha[1]));
+            };
+            // second half: P = 2^(c S - m) in the operand type, running row sums
+            auto softmax_exp = [&]() {
+                pin_s();
+                for (int mt = 0; mt < 2; ++mt) {
+                    const float ref = m[mt] == -INFINITY ? 0.f : m[mt];
+                    float part[4];                          // per 16-key tile, then a tree
+                    for (int c = 0; c < 2; ++c) {
+                        i32x2 h[2];
+                        for (int u = 0; u < 2; ++u) {
+                            f32x4 pr;
+                            for (int e = 0; e < 4; ++e)
+                                pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][2 * c + u][e], p.c, -ref));
+                            part[2 * c + u] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                            h[u] = pack4<kElem>(pr);
+                        }
+                        pf[mt][c] = i32x4{h[0].x, h[0].y, h[1].x, h[1].y};
+                    }
+                    l[mt] = l[mt] * alpha[mt] + ((part[0] + part[1]) + (part[2] + part[3]));
+                }
+            };
+            // O *= alpha, skipped when no row of the wave changed its max
+            auto rescale = [&]() {
+                if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f) == 0) return;
+                for (int mt = 0; mt < 2; ++mt)
+                    for (int h = 0; h < 2; ++h)
+                        for (int t = 0; t < 4; ++t) o[mt][h][t] *= alpha[mt];
+            };
+
+            // ---- prologue (both groups in step): K blocks 0-3 and V blocks 0-1 in
+            // flight (or, after a tile that fetched them and this tile's Q, only
+            // the previous tile's stores), S(0), P(0)
+            auto wait_pre = [&] {
+                if (p.lse)
+                    wait_vmcnt<kStoresO + kStoresL>();
+                else
+                    wait_vmcnt<kStoresO>();
+            };
+            if (settle) wait_vmcnt<0>();
+            if (!pre) {
+                copy_k(0);
+                copy_k(1);
+                copy_v(0);
+                copy_k(2);
+                copy_v(1);
+                copy_k(3);
             }
             __builtin_amdgcn_sched_barrier(0);
-        };
-        auto nothing = [] {};
-        // keys past the end, and (causal) keys above the diagonal, score -inf
-        auto mask = [&](int j) {
-            const int k0 = j * kKeys;
-            bool need = k0 + kKeys > Sk;
-            if constexpr (kCausal) need = need || (k0 + kKeys - 1 > wrow + off);
-            if (need) {
-                const int ln = fresh_lane();                      // (no lane value kept since the tile began)
-                for (int mt = 0; mt < 2; ++mt) {
-                    const int lim = kCausal ? min(Sk, wrow + 16 * mt + (ln & 15) + off + 1) : Sk;
-                    const int t = lim - k0 - 4 * (ln >> 4);       // first masked 16kt + e of this lane
-                    for (int kt = 0; kt < 4; ++kt)
-                        for (int e = 0; e < 4; ++e)
-                            if (16 * kt + e >= t) s[mt][kt][e] = -INFINITY;
-                }
-            }
-        };
-        // The two softmax halves are pure arithmetic, which the compiler would
-        // otherwise move across the stage walls; each half starts from values
-        // passed through an empty asm, so its work stays in its stage.
-        auto pin_s = [&]() {
-            for (int mt = 0; mt < 2; ++mt)
-                for (int kt = 0; kt < 4; ++kt) asm volatile("" : "+v"(s[mt][kt]));
-        };
-        // first half: row maxima of S and the running shift m.  m moves only
-        // when a row's maximum exceeds it by more than kLazy (log2 units): the
-        // exponentials then stay below 2^kLazy, and O and l are rescaled by
-        // alpha = 2^(m_old - m_new) only in those rows (lazy rescaling).  Each
-        // lane first compares the maximum of its own 16 scores of the row (times
-        // c) with m + kLazy; only when some lane of the wave exceeds it does the
-        // wave combine the four lanes of each row (c > 0 and rounding is
-        // monotonic, so the largest lane product is the row maximum times c:
-        // the decision is the same as from the row maximum itself).
-        auto softmax_max = [&]() {
-            pin_s();
-            float lm[2];
-            bool up = false;
-            for (int mt = 0; mt < 2; ++mt) {
-                // a tree of three-input maxima (depth 3, not a chain of 15)
-                const f32x4 *x = s[mt];
-                const float t0 = fmaxf(fmaxf(x[0][0], x[0][1]), x[0][2]);
-                const float t1 = fmaxf(fmaxf(x[0][3], x[1][0]), x[1][1]);
-                const float t2 = fmaxf(fmaxf(x[1][2], x[1][3]), x[2][0]);
-                const float t3 = fmaxf(fmaxf(x[2][1], x[2][2]), x[2][3]);
-                const float t4 = fmaxf(fmaxf(x[3][0], x[3][1]), x[3][2]);
-                lm[mt] = fmaxf(fmaxf(fmaxf(t0, t1), t2), fmaxf(fmaxf(t3, t4), x[3][3])) * p.c;
-                up = up || lm[mt] > m[mt] + kLazy;
-            }
-            alpha[0] = alpha[1] = 1.f;
-            if (__builtin_amdgcn_ballot_w64(up) != 0) {
-                for (int mt = 0; mt < 2; ++mt) {
-                    const float mx = row_reduce(lm[mt], [](float a, float b) { return fmaxf(a, b); });
-                    if (mx > m[mt] + kLazy) {
-                        alpha[mt] = __builtin_amdgcn_exp2f(m[mt] - mx);
-                        m[mt] = mx;
-                    }
-                }
-            }
-            asm volatile("" : "+v"(m[0]), "+v"(m[1]), "+v"(alpha[0]), "+v"(alpha[1]));
-        };
-        // second half: P = 2^(c S - m) in the operand type, running row sums
-        auto softmax_exp = [&]() {
-            pin_s();
-            for (int mt = 0; mt < 2; ++mt) {
-                const float ref = m[mt] == -INFINITY ? 0.f : m[mt];
-                float part[4];                          // per 16-key tile, then a tree
-                for (int c = 0; c < 2; ++c) {
-                    i32x2 h[2];
-                    for (int u = 0; u < 2; ++u) {
-                        f32x4 pr;
-                        for (int e = 0; e < 4; ++e)
-                            pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][2 * c + u][e], p.c, -ref));
-                        part[2 * c + u] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-                        h[u] = pack4<kElem>(pr);
-                    }
-                    pf[mt][c] = i32x4{h[0].x, h[0].y, h[1].x, h[1].y};
-                }
-                l[mt] = l[mt] * alpha[mt] + ((part[0] + part[1]) + (part[2] + part[3]));
-            }
-        };
-        // O *= alpha, skipped when no row of the wave changed its max
-        auto rescale = [&]() {
-            if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f) == 0) return;
-            for (int mt = 0; mt < 2; ++mt)
-                for (int h = 0; h < 2; ++h)
-                    for (int t = 0; t < 4; ++t) o[mt][h][t] *= alpha[mt];
-        };
-
-        // ---- prologue (both groups in step): K blocks 0-3 and V blocks 0-1 in
-        // flight (or, after a tile that fetched them and this tile's Q, only
-        // the previous tile's stores), S(0), P(0)
-        auto wait_pre = [&] {
-            if (p.lse)
-                wait_vmcnt<kStoresO + kStoresL>();
+            if (pre)
+                wait_pre();                     // everything but the previous tile's stores
             else
-                wait_vmcnt<kStoresO>();
-        };
-        if (settle) wait_vmcnt<0>();
-        if (!pre) {
-            copy_k(0);
-            copy_k(1);
-            copy_v(0);
-            copy_k(2);
-            copy_v(1);
-            copy_k(3);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (pre)
-            wait_pre();                     // everything but the previous tile's stores
-        else
-            wait_vmcnt<10>();               // K(0) (this wave's pieces) and Q
-        for (int mt = 0; mt < 2; ++mt) {
-            const bool in = wrow + 16 * mt + r16 < Sq;
-            for (int dc = 0; dc < 4; ++dc) qf[mt][dc] = in ? qf[mt][dc] : i32x4{0, 0, 0, 0};
-        }
-        rendezvous(sg);                     // ... and everyone's
-        read_k(0, 0, 4);
-        wait_lgkmcnt<0>();
-        qk(std::false_type{}, [](int) {}, nothing, nothing);
-        mask(0);
-        softmax_max();
-        rescale();
-        softmax_exp();
-        __builtin_amdgcn_sched_barrier(0);
-        if (pre)
-            wait_pre();
-        else
-            wait_vmcnt<4>();                // K(1), V(0), K(2)
-        rendezvous(sg);
-        read_k(1, 0, 4);
-        wait_lgkmcnt<0>();
-        if (kOffset && groupB) rendezvous(sg);  // group B falls one stage behind
-
-        // one trip; kMasked: block i+1 may hold keys some row must not see
-        // tail: copies may reach past the tile's last block; last: the tile's
-        // last trip, whose softmax stage also loads the next tile's Q into
-        // the registers of this tile's (free once its last scores are made)
-        auto trip = [&](int i, auto masked, auto tail, auto last) {
-            // MFMA stage: S(i+1) and O += P(i) V(i), the V(i) and K(i+2)
-            // fragments read among them; the copies of K(i+4) and V(i+2) go
-            // out in the first quarter; wait for the previous trip's copies
-            v_bases(i, vb);
-            // (the descriptors are made after the first MFMAs, not ahead of them)
-            CopySet cs;
-            qk(std::true_type{}, [&](int q) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (q == 0) cs = copy_set(i + 4, i + 2, tail);
-                copy_piece(cs, q);
-            }, nothing, nothing);
-            pv(std::true_type{}, i + 2);
-            wait_vmcnt<4>();                // K(i+3), V(i+1) (only this trip's four copies may fly)
-            rendezvous(sg);
-            // softmax stage: row max of S(i+1): m(i+1), alpha(i+1); O and l
-            // rescaled; P(i+1)
-            if constexpr (decltype(last)::value) {
-                if (pf) {                   // the next tile's V(1) and K(3)
-                    copy_v(nblk + 1);
-                    copy_k(nblk + 3);
-                }
-                load_q(bhn, qbn, qf);
+                wait_vmcnt<10>();               // K(0) (this wave's pieces) and Q
+            for (int mt = 0; mt < 2; ++mt) {
+                const bool in = wrow + 16 * mt + r16 < Sq;
+                for (int dc = 0; dc < 4; ++dc) qf[mt][dc] = in ? qf[mt][dc] : i32x4{0, 0, 0, 0};
             }
-            if constexpr (decltype(masked)::value) mask(i + 1);
+            rendezvous(sg);                     // ... and everyone's
+            read_k(0, 0, 4);
+            wait_lgkmcnt<0>();
+            qk(std::false_type{}, [](int) {});
+            mask(0);
             softmax_max();
             rescale();
             softmax_exp();
-            wait_lgkmcnt<0>();              // this wave's reads of the MFMA stage
+            __builtin_amdgcn_sched_barrier(0);
+            if (pre)
+                wait_pre();
+            else
+                wait_vmcnt<4>();                // K(1), V(0), K(2)
             rendezvous(sg);
-        };
-        // leading blocks no row of the workgroup needs masked: every key
-        // exists and (causal) every key is visible to the first row
-        int nplain = Sk / kKeys;
-        if constexpr (kCausal) nplain = min(nplain, max(0, (q0 + off + 1) / kKeys));
-        // Trips: unmasked ones whose copies stay in the tile, then the rest
-        // (masked where a row needs it), then the last
-        using F = std::false_type;
-        using T = std::true_type;
-        int i = 0;
-#pragma unroll 1
-        for (; i + 4 < nblk && i + 1 < nplain; ++i) trip(i, F{}, F{}, F{});
-#pragma unroll 1
-        for (; i + 2 < nblk; ++i) trip(i, T{}, T{}, F{});
-        if (i + 1 < nblk) trip(i, T{}, T{}, T{});
-        // ---- drain: P V of the last block (and the next tile's Q after a
-        // tile of one block, which has no trip)
-        v_bases(nblk - 1, vb);
-        read_v(vb, 0, 2);
-        wait_lgkmcnt<0>();
-        pv(std::false_type{}, 0);
-        if (nblk < 2) load_q(bhn, qbn, qf);
-        if (kOffset && !groupB) rendezvous(sg); // group A closes the offset
-        __builtin_amdgcn_sched_barrier(0);
-    } else {
-        load_q(bhn, qbn, qf);
-    }
+            read_k(1, 0, 4);
+            wait_lgkmcnt<0>();
+            if (kOffset && groupB) rendezvous(sg);  // group B falls one stage behind
 
-    // ---- O / l and lse, by buffer stores whose window ends at the head's last
-    // row: every wave issues the same stores (kStoresO, and kStoresL with an
-    // lse buffer), rows past the end are dropped by the window
-    {
-        const int ln = fresh_lane(), gl = ln >> 4;
-        const __amdgpu_buffer_rsrc_t ro =
-            __builtin_amdgcn_make_buffer_rsrc(p.O + qbase, 0, Sq * kRowBytes, 0x00020000);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const float lt = row_reduce(l[mt], [](float a, float b) { return a + b; });
-            const float inv = lt > 0.f ? 1.f / lt : 0.f;
-            for (int h = 0; h < 2; ++h)
-                for (int t = 0; t < 4; ++t) o[mt][h][t] *= inv;
-            const int row = wrow + 16 * mt + (ln & 15);
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                for (int nt = 0; nt < 4; nt += 2) {
-                    const i32x4 v = pack_pair<kElem>(o[mt][h][nt], o[mt][h][nt + 1]);
-                    const int col = 64 * h + 16 * nt + ((gl & 1) ? 16 + 4 * (gl - 1) : 4 * gl);
-                    __builtin_amdgcn_raw_buffer_store_b128(v, ro, row * kRowBytes + 2 * col, 0, 0);
+            // one trip; kMasked: block i+1 may hold keys some row must not see
+            // tail: copies may reach past the tile's last block; last: the tile's
+            // last trip, whose softmax stage also loads the next tile's Q into
+            // the registers of this tile's (free once its last scores are made)
+            auto trip = [&](int i, auto masked, auto tail, auto last) {
+                // MFMA stage: S(i+1) and O += P(i) V(i), the V(i) and K(i+2)
+                // fragments read among them; the copies of K(i+4) and V(i+2) go
+                // out in the first quarter; wait for the previous trip's copies
+                v_bases(i, vb);
+                // (the descriptors are made after the first MFMAs, not ahead of them)
+                CopySet cs;
+                qk(std::true_type{}, [&](int q) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (q == 0) cs = copy_set(i + 4, i + 2, tail);
+                    copy_piece(cs, q);
+                });
+                pv(std::true_type{}, i + 2);
+                wait_vmcnt<4>();                // K(i+3), V(i+1) (only this trip's four copies may fly)
+                rendezvous(sg);
+                // softmax stage: row max of S(i+1): m(i+1), alpha(i+1); O and l
+                // rescaled; P(i+1)
+                if constexpr (decltype(last)::value) {
+                    if (pf) {                   // the next tile's V(1) and K(3)
+                        copy_v(nblk + 1);
+                        copy_k(nblk + 3);
+                    }
+                    load_q(bhn, qbn, qf);
                 }
-            if (p.lse) {
-                const __amdgpu_buffer_rsrc_t rl =
-                    __builtin_amdgcn_make_buffer_rsrc(p.lse + static_cast<int64_t>(bh) * Sq, 0, Sq * 4, 0x00020000);
-                const float v = lt > 0.f ? (m[mt] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f : -INFINITY;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rl, gl == 0 ? 4 * row : 0x7FFFFFF0, 0, 0);
+                if constexpr (decltype(masked)::value) mask(i + 1);
+                softmax_max();
+                rescale();
+                softmax_exp();
+                wait_lgkmcnt<0>();              // this wave's reads of the MFMA stage
+                rendezvous(sg);
+            };
+            // leading blocks no row of the workgroup needs masked: every key
+            // exists and (causal) every key is visible to the first row
+            int nplain = Sk / kKeys;
+            if constexpr (kCausal) nplain = min(nplain, max(0, (q0 + off + 1) / kKeys));
+            // Trips: unmasked ones whose copies stay in the tile, then the rest
+            // (masked where a row needs it), then the last
+            using F = std::false_type;
+            using T = std::true_type;
+            int i = 0;
+#pragma unroll 1
+            for (; i + 4 < nblk && i + 1 < nplain; ++i) trip(i, F{}, F{}, F{});
+#pragma unroll 1
+            for (; i + 2 < nblk; ++i) trip(i, T{}, T{}, F{});
+            if (i + 1 < nblk) trip(i, T{}, T{}, T{});
+            // ---- drain: P V of the last block (and the next tile's Q after a
+            // tile of one block, which has no trip)
+            v_bases(nblk - 1, vb);
+            read_v(vb, 0, 2);
+            wait_lgkmcnt<0>();
+            pv(std::false_type{}, 0);
+            if (nblk < 2) load_q(bhn, qbn, qf);
+            if (kOffset && !groupB) rendezvous(sg); // group A closes the offset
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            load_q(bhn, qbn, qf);
+        }
+
+        // ---- O / l and lse, by buffer stores whose window ends at the head's last
+        // row: every wave issues the same stores (kStoresO, and kStoresL with an
+        // lse buffer), rows past the end are dropped by the window
+        {
+            const int ln = fresh_lane(), gl = ln >> 4;
+            const __amdgpu_buffer_rsrc_t ro =
+                __builtin_amdgcn_make_buffer_rsrc(p.O + qbase, 0, Sq * kRowBytes, 0x00020000);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const float lt = row_reduce(l[mt], [](float a, float b) { return a + b; });
+                const float inv = lt > 0.f ? 1.f / lt : 0.f;
+                for (int h = 0; h < 2; ++h)
+                    for (int t = 0; t < 4; ++t) o[mt][h][t] *= inv;
+                const int row = wrow + 16 * mt + (ln & 15);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    for (int nt = 0; nt < 4; nt += 2) {
+                        const i32x4 v = pack_pair<kElem>(o[mt][h][nt], o[mt][h][nt + 1]);
+                        const int col = 64 * h + 16 * nt + ((gl & 1) ? 16 + 4 * (gl - 1) : 4 * gl);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, ro, row * kRowBytes + 2 * col, 0, 0);
+                    }
+                if (p.lse) {
+                    const __amdgpu_buffer_rsrc_t rl =
+                        __builtin_amdgcn_make_buffer_rsrc(p.lse + static_cast<int64_t>(bh) * Sq, 0, Sq * 4, 0x00020000);
+                    const float v = lt > 0.f ? (m[mt] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f : -INFINITY;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rl, gl == 0 ? 4 * row : 0x7FFFFFF0, 0, 0);
+                }
             }
         }
-    }
-    if (!more) break;
-    settle = nblk > 0 && !pf;
-    g0 += nblk;
-    pre = pf;
-    bh = bhn;
-    qb = qbn;
-    nblk = nbn;
+        if (!more) break;
+        settle = nblk > 0 && !pf;
+        g0 += nblk;
+        pre = pf;
+        bh = bhn;
+        qb = qbn;
+        nblk = nbn;
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();                        // copies past the last tile's end
