@@ -278,8 +278,11 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             nbn = 0;
         }
         // copies past this tile's last block fetch the next tile's first blocks
-        // (K 0-3 and V 0-1, the last two from the tile's last trip)
-        const bool pf = more && nblk >= 2 && nbn >= 3;
+        // (K 0-3 and V 0-1, the last two from the tile's last trip).  Only
+        // when all of them are the next tile's own: with fewer than 4 blocks
+        // its K 3 would be a block of the tile after it, which this tile does
+        // not fetch.
+        const bool pf = more && nblk >= 2 && nbn >= 4;
         // The lane index and the sequence lengths are opaque per tile: what
         // derives from them is computed in the tile, not kept in registers
         // across all of the workgroup's tiles
@@ -325,8 +328,8 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
             const uint32_t tail_rec = static_cast<uint32_t>(Sk - nfull * kKeys) * kRowBytes;
             // Source offset and window of block j of this tile; with pf, blocks
             // past the last are the next tile's blocks j - nblk (at most its
-            // third, so every one of them exists).  Selects of uniform values
-            // only: branches here would sit in every trip.
+            // fourth, which it has).  Selects of uniform values only: branches
+            // here would sit in every trip.
             const int64_t xbase = pf ? kbase_n - static_cast<int64_t>(nblk) * kKVTile : kbase;
             auto source = [&](int j, int64_t &at, uint32_t &nrec, auto tail) {
                 if constexpr (!decltype(tail)::value) {     // block j is the tile's own

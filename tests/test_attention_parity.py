@@ -106,6 +106,26 @@ def test_every_block_count(nb, sk, causal, sched):
     check("f16", q, k, v, 1 / math.sqrt(128), causal, what=f"blocks={nb} Sk={sk}", sched=sched)
 
 
+# More tiles than CUs, so that each persistent workgroup of the 8-wave kernel
+# runs several tiles in a row: (B, H, Sq, Sk, causal) and the tile-to-tile
+# path each exercises (blocks per tile in brackets)
+TRANSITIONS = [
+    (2, 300, 256, 200, False),   # [4] -> [4]: the next tile's first blocks and Q fetched ahead
+    (2, 300, 256, 130, False),   # [3] -> [3]: not fetched ahead (the next tile's block 3 would be
+                                 # the first block of the tile after it); zero windows settle first
+    (2, 300, 256, 100, False),   # [2] -> [2]: likewise
+    (1, 120, 600, 150, True),    # [0], [1], [3] mixed: tiles without blocks, one block, three
+    (1, 120, 600, 460, True),    # [2], [6], [8] mixed: fetched ahead into the longer tiles only
+]
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,causal", TRANSITIONS, ids=lambda x: str(x))
+def test_persistent_tile_transitions(B, H, Sq, Sk, causal):
+    assert B * H * ((Sq + 255) // 256) > 256
+    q, k, v = qkv("f16", B, H, Sq, Sk, 128, seed=7000 + Sk + Sq)
+    check("f16", q, k, v, 1 / math.sqrt(128), causal, what=f"{B}x{H}x{Sq}x{Sk} causal={causal}")
+
+
 @pytest.mark.parametrize("sched", ["pipelined", "interleaved"])
 def test_uniform_values_and_other_scales(sched):
     # scale 4: scores span hundreds in log2 units, so a running max that is not
