@@ -142,6 +142,26 @@ def test_attention_bitwise_under_stagger(elem, causal, sched):
         assert np.array_equal(lse, l_ref), f"run {r}: {(lse != l_ref).sum()} lse values differ under stagger"
 
 
+@pytest.mark.parametrize("sched", ["pipelined", "in_phase"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_tile_to_tile_bitwise_under_stagger(causal, sched):
+    """More tiles (300) than CUs: every persistent workgroup of the 8-wave
+    kernel runs several tiles in a row, with the next tile's blocks and Q
+    fetched during the last trips of the one before."""
+    B, H, Sq, Sk, D = 1, 100, 768, 512, 128
+    print(f"[gpu] race stress attention tiles f16 causal={causal} sched={sched} {B}x{H}x{Sq}x{Sk}", flush=True)
+    q = si.matrix_bits("f16", "normal", B * H * Sq, D, seed=7501, stream=0).reshape(B, H, Sq, D)
+    k = si.matrix_bits("f16", "normal", B * H * Sk, D, seed=7501, stream=1).reshape(B, H, Sk, D)
+    v = si.matrix_bits("f16", "normal", B * H * Sk, D, seed=7501, stream=2).reshape(B, H, Sk, D)
+    s = SCHED[sched]
+    o_ref, l_ref = _attention_bits(mcs.load(), "f16", q, k, v, 0.088, causal, s)
+    assert not np.isnan(oracle.decode(o_ref, "f16")).any()
+    for r in range(REPEATS):
+        o, lse = _attention_bits(mcs.load_stagger(), "f16", q, k, v, 0.088, causal, s)
+        assert np.array_equal(o, o_ref), f"run {r}: {(o != o_ref).sum()} O elements differ under stagger"
+        assert np.array_equal(lse, l_ref), f"run {r}: {(lse != l_ref).sum()} lse values differ under stagger"
+
+
 def test_stagger_build_is_the_one_that_runs():
     """The race-stress library really runs its own, slower kernels: its pauses
     add ~1,000 cycles per barrier against ~500 cycles of work per stage."""
