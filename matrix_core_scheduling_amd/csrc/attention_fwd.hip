@@ -718,7 +718,7 @@ __global__ void __launch_bounds__(kAttnWaves * 64) attention_fwd_kernel(AttnPara
         }
         if (!more) break;
         settle = nblk > 0 && !pf;
-        g0 += nblk;
+        g0 = (g0 + nblk) & (kRing - 1);  // only the ring position matters
         pre = pf;
         bh = bhn;
         qb = qbn;
