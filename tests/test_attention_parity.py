@@ -116,6 +116,8 @@ TRANSITIONS = [
     (2, 300, 256, 100, False),   # [2] -> [2]: likewise
     (1, 120, 600, 150, True),    # [0], [1], [3] mixed: tiles without blocks, one block, three
     (1, 120, 600, 460, True),    # [2], [6], [8] mixed: fetched ahead into the longer tiles only
+    (1, 123, 768, 300, False),   # [5] -> [5], 369 tiles: the XCDs' ranges differ by one tile
+    (1, 123, 768, 700, True),    # causal [3], [7], [11] with a ragged last block, 369 tiles
 ]
 
 
