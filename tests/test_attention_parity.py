@@ -237,3 +237,24 @@ def test_four_wave_form_full_size(name):
     _, l4, b4 = run_attention(w.dtype, q, k, v, w.scale, w.causal, sched="interleaved")
     assert np.array_equal(b4, b8), (name, int((b4 != b8).sum()))
     assert np.array_equal(l4, l8), name
+
+
+@pytest.mark.parametrize("B,H,Sq,Sk,causal", [(2, 300, 256, 200, False), (1, 120, 600, 460, True)],
+                         ids=lambda x: str(x))
+def test_without_lse_same_output(B, H, Sq, Sk, causal):
+    """lse = NULL (no lse stores: the waits between tiles count fewer stores)
+    gives O bit for bit as with lse, over more tiles than CUs."""
+    torch = _torch()
+    q, k, v = qkv("f16", B, H, Sq, Sk, 128, seed=7300 + Sk)
+    _, _, bits = run_attention("f16", q, k, v, 1 / math.sqrt(128), causal)
+    Q, _ = upload(q.reshape(-1, 128), "f16")
+    K, _ = upload(k.reshape(-1, 128), "f16")
+    V, _ = upload(v.reshape(-1, 128), "f16")
+    O = torch.full((B * H * Sq * 128,), -5.0, dtype=torch.float16, device="cuda")
+    print(f"[gpu] attention without lse B={B} H={H} Sq={Sq} Sk={Sk} causal={causal}", flush=True)
+    st = mcs.attention_fwd(DT["f16"], B, H, Sq, Sk, 128, Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(),
+                           None, 1 / math.sqrt(128), int(causal), torch.cuda.current_stream().cuda_stream)
+    assert st == mcs.GEMM_OK, mcs.gemm_status_string(st)
+    torch.cuda.synchronize()
+    got = O.cpu().view(torch.int16).numpy().view(np.uint16).reshape(B, H, Sq, 128)
+    assert np.array_equal(got, bits), f"{(got != bits).sum()} O elements differ without lse"
