@@ -50,7 +50,17 @@
 // stage R-2 (S1 copies six, S3 two), so both memory stages end with
 // vmcnt(8) lgkmcnt(0); every copy has a full K-step to land.  At most 64
 // fragment VGPRs are live with B given N x K (a0 a1 b0 b1 is 16+16+32+32,
-// never all four), 80 with B given K x N (32+32+16+16).
+// never all four), 88 with B given K x N (32+32+16+16, plus the 8 of the
+// next b0 that S1 reads early).
+// Two per-layout adjustments (StageTuning below):
+//   * B given N x K: each MFMA stage's last two MFMAs are issued at the head
+//     of the next memory stage, after the rendezvous (they read only
+//     registers, so no LDS dependency moves).
+//   * B given K x N: S1 also reads k-slice 0 of b0[nxt] (S0 is done with b0)
+//     and S3 only k-slice 1; S1 copies b0 first, so after the b0 copy of
+//     step t+1 (issued in S1 of t-1) only a0, a1 and S3's b1 follow by the end
+//     of S3 of t-1: S3 ends with vmcnt(6).  That copy has three stages to
+//     land; every other keeps a full K-step.
 // The LDS reads open each memory stage so that their latency overlaps the
 // address and descriptor work of the copies.  Copies of K-steps past the end
 // use an empty buffer window, so they write zeros (buffer loads outside the
@@ -78,6 +88,24 @@ namespace mcs {
 namespace {
 
 constexpr int kCopyWait = 8;               // vmcnt at the end of each memory stage
+
+// Per-layout stage tuning (A/B measured in one process on rotating inputs,
+// results bitwise identical):
+//   kTail: with B given N x K each MFMA stage leaves its last two MFMAs to the
+//     start of the following memory stage, issued there at the memory stage's
+//     raised priority; the matrix pipe then has work queued the moment the
+//     rendezvous releases both groups (+0.6..1.4 % on 4096^2 x 8192, BF16
+//     8192^3 and FP8 8192^3).  With B given K x N it gained nothing.
+//   kEarlyB: with B given K x N the S3 reads (a0, a1 and b0: 24 read
+//     instructions, the transposing ones included) outweigh S1's (8), so S1
+//     also reads k-slice 0 of the next step's b0; its copy then goes first in
+//     S1's copy order and S3 ends with vmcnt(6) (+1.5..2.2 % on
+//     16384x2048x8192, 4096^2 x 8192 and 8192^3).  With B given N x K it lost.
+template <bool kTransB> struct StageTuning {
+    static constexpr int kTail = kTransB ? 2 : 0;
+    static constexpr bool kEarlyB = !kTransB;
+    static constexpr int kWaitS3 = kEarlyB ? 6 : kCopyWait;
+};
 
 // Wave layout.  B given N x K: 4 (M) x 2 (N) waves, wave (wm, wn) owning rows
 // 32wm.. of every A half and columns 64wn.. of every B half.  B given K x N:
@@ -121,15 +149,17 @@ struct Pipeline : Loader<kElem, kTransB, 8> {
                 a[mt][ks] = lds_read128(base + fa.row[ks] + mt * 2048);
     }
 
+    // The fragment pieces b[nt][ks] with kNt0 <= nt < kNt1 and kKs0 <= ks < kKs1.
+    template <int kNt0 = 0, int kNt1 = L::kNT, int kKs0 = 0, int kKs1 = 2>
     __device__ __forceinline__ void read_b(i32x4 (&b)[L::kNT][2], uint32_t buf, int h) const {
         const uint32_t base = lds0 + buf + kOffB + h * kHalf;
         if constexpr (kTransB) {
-            for (int nt = 0; nt < L::kNT; ++nt)
-                for (int ks = 0; ks < 2; ++ks)
+            for (int nt = kNt0; nt < kNt1; ++nt)
+                for (int ks = kKs0; ks < kKs1; ++ks)
                     b[nt][ks] = lds_read128(base + fb.row[ks] + nt * 2048);
         } else {
-            for (int nt = 0; nt < L::kNT; ++nt)
-                for (int ks = 0; ks < 2; ++ks) {
+            for (int nt = kNt0; nt < kNt1; ++nt)
+                for (int ks = kKs0; ks < kKs1; ++ks) {
                     const i32x2 lo = lds_read64_tr(base + fb.tr[nt] + (32 * ks + 0) * 256);
                     const i32x2 hi = lds_read64_tr(base + fb.tr[nt] + (32 * ks + 4) * 256);
                     b[nt][ks] = i32x4{lo.x, lo.y, hi.x, hi.y};
@@ -141,20 +171,31 @@ struct Pipeline : Loader<kElem, kTransB, 8> {
 // One quadrant's MFMAs over the K-step: two 16x16x32 k-slices for 16-bit
 // operands, or one 16x16x128 FP8 MFMA over both chunks.  The tiles go in a
 // snake (columns forward on even rows of tiles, backward on odd ones), so
-// within a k-slice consecutive MFMAs differ in one operand only.
-template <int kElem, int kMT, int kNT>
+// within a k-slice consecutive MFMAs differ in one operand only.  Only the
+// MFMAs numbered kBegin..kEnd-1 of that sequence are issued, so a stage can
+// leave its last few for after the rendezvous.
+template <int kElem, int kMT, int kNT, int kBegin = 0, int kEnd = 1 << 30>
 __device__ __forceinline__ void quadrant(f32x4 (&acc)[kMT][kNT], const i32x4 (&a)[kMT][2],
                                          const i32x4 (&b)[kNT][2]) {
     if constexpr (kElem == kElemFP8) {
+#pragma unroll
         for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
             for (int j = 0; j < kNT; ++j) {
+                const int i = mt * kNT + j;
+                if (i < kBegin || i >= kEnd) continue;
                 const int nt = mt & 1 ? kNT - 1 - j : j;
                 acc[mt][nt] = mfma_fp8(b[nt][0], b[nt][1], a[mt][0], a[mt][1], acc[mt][nt]);
             }
     } else {
+#pragma unroll
         for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
             for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
                 for (int j = 0; j < kNT; ++j) {
+                    const int i = (ks * kMT + mt) * kNT + j;
+                    if (i < kBegin || i >= kEnd) continue;
                     const int nt = mt & 1 ? kNT - 1 - j : j;
                     acc[mt][nt] = mfma<kElem>(b[nt][ks], a[mt][ks], acc[mt][nt]);
                 }
@@ -166,9 +207,10 @@ __device__ __forceinline__ void mem_stage_begin() { __builtin_amdgcn_s_setprio(1
 // End of a memory stage: this wave's copies for the reads two stages later
 // have landed, and so have its own LDS reads (their registers feed the next
 // stage and their half may be refilled two stages on).
+template <int kWait = kCopyWait>
 __device__ __forceinline__ void mem_stage_end(Stagger &sg) {
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kCopyWait>();
+    wait_vmcnt<kWait>();
     wait_lgkmcnt<0>();
     __builtin_amdgcn_s_setprio(0);
     rendezvous(sg);
@@ -189,6 +231,9 @@ gemm_pipelined_kernel(GemmParams pin) {
     const int wave = pl.wave;
 
     using L = WaveLayout<kTransB>;
+    constexpr int kQ = (kElem == kElemFP8 ? 1 : 2) * L::kMT * L::kNT;   // MFMAs per quadrant
+    using T = StageTuning<kTransB>;
+    constexpr int kTail = T::kTail < kQ ? T::kTail : kQ;   // MFMAs issued after the rendezvous
     f32x4 acc[2][2][L::kMT][L::kNT];
     for (int qa = 0; qa < 2; ++qa)
         for (int qb = 0; qb < 2; ++qb)
@@ -198,14 +243,17 @@ gemm_pipelined_kernel(GemmParams pin) {
     i32x4 a0[L::kMT][2], a1[L::kMT][2], b0[L::kNT][2], b1[L::kNT][2];
 
     // ---- prologue: the copy stream of steps 0 and 1 in steady-state order
-    // (a0 a1 b0, then b1, per step), then the fragments S0 of step 0 needs.
+    // (a0 a1 b0 -- b0 a0 a1 when b0 is read early -- then b1, per step), then
+    // the fragments S0 of step 0 needs.
+    if constexpr (T::kEarlyB) pl.copy_b(0, 0, 0);
     pl.copy_a(0, 0, 0);
     pl.copy_a(0, 0, 1);
-    pl.copy_b(0, 0, 0);
+    if constexpr (!T::kEarlyB) pl.copy_b(0, 0, 0);
     pl.copy_b(0, 0, 1);
+    if constexpr (T::kEarlyB) pl.copy_b(1, kBuf, 0);
     pl.copy_a(1, kBuf, 0);
     pl.copy_a(1, kBuf, 1);
-    pl.copy_b(1, kBuf, 0);
+    if constexpr (!T::kEarlyB) pl.copy_b(1, kBuf, 0);
     pl.copy_b(1, kBuf, 1);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<10>();                   // a0(0) a1(0) b0(0) landed (this wave's part)
@@ -215,7 +263,7 @@ gemm_pipelined_kernel(GemmParams pin) {
     pl.read_b(b0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt<0>();
-    wait_vmcnt<kCopyWait>();            // b1(0) landed: the state at the end of S3 of step -1
+    wait_vmcnt<T::kWaitS3>();           // b1(0) (and b0(1)) landed: the state at the end of S3 of step -1
     rendezvous(pl.sg);
 
     if constexpr (kOffset) {
@@ -231,26 +279,37 @@ gemm_pipelined_kernel(GemmParams pin) {
             const int s = t + u;
             // S0: quadrants Q00 and Q10
             quadrant<kElem>(acc[0][0], a0, b0);
-            quadrant<kElem>(acc[1][0], a1, b0);
+            quadrant<kElem, L::kMT, L::kNT, 0, kQ - kTail>(acc[1][0], a1, b0);
             rendezvous(pl.sg);
             // S1
             mem_stage_begin();
+            quadrant<kElem, L::kMT, L::kNT, kQ - kTail, kQ>(acc[1][0], a1, b0);
+            __builtin_amdgcn_sched_barrier(0);
             pl.read_b(b1, cur, 1);
+            if constexpr (T::kEarlyB) {
+                pl.template read_b<0, L::kNT, 0, 1>(b0, nxt, 0);
+                pl.copy_b(s + 2, cur, 0);
+            }
             pl.copy_a(s + 2, cur, 0);
             pl.copy_a(s + 2, cur, 1);
-            pl.copy_b(s + 2, cur, 0);
+            if constexpr (!T::kEarlyB) pl.copy_b(s + 2, cur, 0);
             mem_stage_end(pl.sg);
             // S2: quadrants Q01 and Q11
             quadrant<kElem>(acc[0][1], a0, b1);
-            quadrant<kElem>(acc[1][1], a1, b1);
+            quadrant<kElem, L::kMT, L::kNT, 0, kQ - kTail>(acc[1][1], a1, b1);
             rendezvous(pl.sg);
             // S3
             mem_stage_begin();
+            quadrant<kElem, L::kMT, L::kNT, kQ - kTail, kQ>(acc[1][1], a1, b1);
+            __builtin_amdgcn_sched_barrier(0);
             pl.read_a(a0, nxt, 0);
             pl.read_a(a1, nxt, 1);
-            pl.read_b(b0, nxt, 0);
+            if constexpr (T::kEarlyB)
+                pl.template read_b<0, L::kNT, 1, 2>(b0, nxt, 0);
+            else
+                pl.read_b(b0, nxt, 0);
             pl.copy_b(s + 2, cur, 1);
-            mem_stage_end(pl.sg);
+            mem_stage_end<T::kWaitS3>(pl.sg);
         }
     }
 

@@ -182,6 +182,64 @@ def test_pipelined_lds_reads_per_layout(asm):
     assert seen == {0, 1}
 
 
+def _stages(ops):
+    """The loop's instructions cut at every s_barrier: [[mnemonics of one stage], ...].
+    The loop is a cycle, and its header can fall inside a stage: the pieces
+    before the first barrier and after the last one are one stage."""
+    out, cur = [], []
+    for o in ops:
+        if o == "s_barrier":
+            out.append(cur)
+            cur = []
+        else:
+            cur.append(o)
+    out[0] = cur + out[0]
+    return out
+
+
+def test_pipelined_stage_tuning(asm):
+    """The per-layout stage tuning of the 8-wave loop, as compiled.  With B
+    given N x K every memory stage opens (after s_setprio 1) with the last two
+    MFMAs of the MFMA stage before it, and nothing else is an MFMA there; both
+    memory stages end with vmcnt(8).  With B given K x N there are no such
+    MFMAs, S1 reads 12 fragments (b1 and k-slice 0 of the next b0: 8 + 4
+    transposing reads) and S3 20 (a0, a1: 16, and k-slice 1 of b0: 4), and
+    the memory stages end with vmcnt(8) (S1) and vmcnt(6) (S3)."""
+    seen = set()
+    for (fn, hdr), ops in loops(asm["gemm_pipelined_kernel"]).items():
+        if "gemm_pipelined_kernel" not in fn:
+            continue
+        m = re.search(r"kernelILi(\d)ELb(\d)E", fn)
+        elem, trans_b = int(m.group(1)), int(m.group(2))
+        stages = [st for st in _stages(ops)]
+        mem = [st for st in stages if "s_setprio" in st and any(o.startswith("buffer_load") for o in st)]
+        assert len(mem) == 4, f"{fn}: {len(mem)} memory stages per iteration"
+        for st in mem:
+            body = st[st.index("s_setprio") + 1:]
+            mfma = [o for o in body if o.startswith("v_mfma")]
+            if trans_b:
+                assert len(mfma) == 2 and all(o.startswith("v_mfma") for o in body[:2]), f"{fn}: {body[:6]}"
+            else:
+                assert not mfma, f"{fn}: {len(mfma)} MFMAs in a memory stage"
+        if not trans_b:
+            reads = [sum(o.startswith("ds_read") for o in st) for st in mem]
+            assert reads in ([12, 20, 12, 20], [20, 12, 20, 12]), f"{fn}: reads per memory stage {reads}"
+        seen.add((elem, trans_b))
+    assert seen == {(0, 0), (0, 1), (1, 0), (1, 1), (2, 1)}
+
+
+def test_pipelined_copy_waits(asm):
+    """The vmcnt of the waits in the 8-wave kernel: 8 with B given N x K
+    (prologue 10, epilogue 0); 8 and 6 with B given K x N, whose S1 copy order
+    puts b0 first so that S3's wait covers the next step's b0 that S1 reads
+    early."""
+    for fn, lines in _function(asm["gemm_pipelined_kernel"], "gemm_pipelined_kernel").items():
+        trans_b = int(re.search(r"kernelILi\dELb(\d)E", fn).group(1))
+        vm = set(re.findall(r"s_waitcnt vmcnt\((\d+)\)", "\n".join(lines)))
+        want = {"0", "8", "10"} if trans_b else {"0", "6", "8", "10"}
+        assert vm == want, f"{fn}: vmcnt values {sorted(vm)}"
+
+
 def _function(asm_text, name_part):
     """{symbol: [lines]} of every function whose symbol contains name_part."""
     out, fn = {}, None
