@@ -52,10 +52,14 @@
 // fragment VGPRs are live with B given N x K (a0 a1 b0 b1 is 16+16+32+32,
 // never all four), 88 with B given K x N (32+32+16+16, plus the 8 of the
 // next b0 that S1 reads early).
-// Two per-layout adjustments (StageTuning below):
+// Per-layout adjustments (StageTuning below):
 //   * B given N x K: each MFMA stage's last two MFMAs are issued at the head
 //     of the next memory stage, after the rendezvous (they read only
-//     registers, so no LDS dependency moves).
+//     registers, so no LDS dependency moves); and b0 is copied in S3 before
+//     b1 instead of in S1, so S1 ends with vmcnt(6): after the b0 copy of
+//     step t+1 (S3 of t-1) come b1's two and S1's four by the end of S1 of
+//     t.  That copy has about two and a half stages to land.  b0 of step t
+//     was last read in S3 of t-1, four stages before its refill.
 //   * B given K x N: S1 also reads k-slice 0 of b0[nxt] (S0 is done with b0)
 //     and S3 only k-slice 1; S1 copies b0 first, so after the b0 copy of
 //     step t+1 (issued in S1 of t-1) only a0, a1 and S3's b1 follow by the end
@@ -101,9 +105,15 @@ constexpr int kCopyWait = 8;               // vmcnt at the end of each memory st
 //     also reads k-slice 0 of the next step's b0; its copy then goes first in
 //     S1's copy order and S3 ends with vmcnt(6) (+1.5..2.2 % on
 //     16384x2048x8192, 4096^2 x 8192 and 8192^3).  With B given N x K it lost.
+//   kLateB0: with B given N x K the copies of b0 move from S1 to S3 (S1
+//     copies a0 a1, S3 b0 b1: four each), so S1 ends with vmcnt(6) and the
+//     b0 copy has about two and a half stages to land (+0.2..1 % on
+//     4096^2 x 8192, 4096^2 x 16384, BF16 and FP8 8192^3).
 template <bool kTransB> struct StageTuning {
     static constexpr int kTail = kTransB ? 2 : 0;
     static constexpr bool kEarlyB = !kTransB;
+    static constexpr bool kLateB0 = kTransB;
+    static constexpr int kWaitS1 = kLateB0 ? 6 : kCopyWait;
     static constexpr int kWaitS3 = kEarlyB ? 6 : kCopyWait;
 };
 
@@ -292,8 +302,8 @@ gemm_pipelined_kernel(GemmParams pin) {
             }
             pl.copy_a(s + 2, cur, 0);
             pl.copy_a(s + 2, cur, 1);
-            if constexpr (!T::kEarlyB) pl.copy_b(s + 2, cur, 0);
-            mem_stage_end(pl.sg);
+            if constexpr (!T::kEarlyB && !T::kLateB0) pl.copy_b(s + 2, cur, 0);
+            mem_stage_end<T::kWaitS1>(pl.sg);
             // S2: quadrants Q01 and Q11
             quadrant<kElem>(acc[0][1], a0, b1);
             quadrant<kElem, L::kMT, L::kNT, 0, kQ - kTail>(acc[1][1], a1, b1);
@@ -308,6 +318,7 @@ gemm_pipelined_kernel(GemmParams pin) {
                 pl.template read_b<0, L::kNT, 1, 2>(b0, nxt, 0);
             else
                 pl.read_b(b0, nxt, 0);
+            if constexpr (T::kLateB0) pl.copy_b(s + 2, cur, 0);
             pl.copy_b(s + 2, cur, 1);
             mem_stage_end<T::kWaitS3>(pl.sg);
         }

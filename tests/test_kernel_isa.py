@@ -200,11 +200,11 @@ def _stages(ops):
 def test_pipelined_stage_tuning(asm):
     """The per-layout stage tuning of the 8-wave loop, as compiled.  With B
     given N x K every memory stage opens (after s_setprio 1) with the last two
-    MFMAs of the MFMA stage before it, and nothing else is an MFMA there; both
-    memory stages end with vmcnt(8).  With B given K x N there are no such
-    MFMAs, S1 reads 12 fragments (b1 and k-slice 0 of the next b0: 8 + 4
-    transposing reads) and S3 20 (a0, a1: 16, and k-slice 1 of b0: 4), and
-    the memory stages end with vmcnt(8) (S1) and vmcnt(6) (S3)."""
+    MFMAs of the MFMA stage before it, and nothing else is an MFMA there; each
+    memory stage issues four copies (S1 a0 a1, S3 b0 b1).  With B given K x N
+    there are no such MFMAs, S1 reads 12 fragments (b1 and k-slice 0 of the
+    next b0: 8 + 4 transposing reads) and S3 20 (a0, a1: 16, and k-slice 1 of
+    b0: 4), and S1 issues six copies (b0 a0 a1), S3 two (b1)."""
     seen = set()
     for (fn, hdr), ops in loops(asm["gemm_pipelined_kernel"]).items():
         if "gemm_pipelined_kernel" not in fn:
@@ -221,22 +221,26 @@ def test_pipelined_stage_tuning(asm):
                 assert len(mfma) == 2 and all(o.startswith("v_mfma") for o in body[:2]), f"{fn}: {body[:6]}"
             else:
                 assert not mfma, f"{fn}: {len(mfma)} MFMAs in a memory stage"
-        if not trans_b:
+        copies = [sum(o.startswith("buffer_load") for o in st) for st in mem]
+        if trans_b:
+            assert copies == [4, 4, 4, 4], f"{fn}: copies per memory stage {copies}"
+        else:
             reads = [sum(o.startswith("ds_read") for o in st) for st in mem]
             assert reads in ([12, 20, 12, 20], [20, 12, 20, 12]), f"{fn}: reads per memory stage {reads}"
+            assert copies in ([6, 2, 6, 2], [2, 6, 2, 6]), f"{fn}: copies per memory stage {copies}"
         seen.add((elem, trans_b))
     assert seen == {(0, 0), (0, 1), (1, 0), (1, 1), (2, 1)}
 
 
 def test_pipelined_copy_waits(asm):
-    """The vmcnt of the waits in the 8-wave kernel: 8 with B given N x K
-    (prologue 10, epilogue 0); 8 and 6 with B given K x N, whose S1 copy order
-    puts b0 first so that S3's wait covers the next step's b0 that S1 reads
-    early."""
+    """The vmcnt of the waits in the 8-wave kernel (prologue 10, epilogue 0):
+    with B given N x K S1 ends with 6 (b0 is copied in S3, before b1) and S3
+    with 8; with B given K x N S1 ends with 8 and S3 with 6 (S1's copy order
+    puts b0 first, and S1 reads k-slice 0 of the next b0 early)."""
     for fn, lines in _function(asm["gemm_pipelined_kernel"], "gemm_pipelined_kernel").items():
         trans_b = int(re.search(r"kernelILi\dELb(\d)E", fn).group(1))
         vm = set(re.findall(r"s_waitcnt vmcnt\((\d+)\)", "\n".join(lines)))
-        want = {"0", "8", "10"} if trans_b else {"0", "6", "8", "10"}
+        want = {"0", "6", "8", "10"}
         assert vm == want, f"{fn}: vmcnt values {sorted(vm)}"
 
 
