@@ -273,7 +273,7 @@ gemm_pipelined_kernel(GemmParams pin) {
     pl.read_b(b0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt<0>();
-    wait_vmcnt<T::kWaitS3>();           // b1(0) (and b0(1)) landed: the state at the end of S3 of step -1
+    wait_vmcnt<T::kWaitS3>();           // b1(0) landed (with b0 read early, b0(1) too): the state at the end of S3 of step -1
     rendezvous(pl.sg);
 
     if constexpr (kOffset) {
