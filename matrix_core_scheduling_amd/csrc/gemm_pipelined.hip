@@ -38,7 +38,8 @@
 //     refilled no earlier than two stages after the stage that read it, one
 //     stage later than an in-phase schedule would allow because group B lags.
 //
-// Schedule of K-step t (cur = buffer of t, nxt = buffer of t+1); aX/bX are
+// Base schedule of K-step t (each B layout adjusts it, below; cur = buffer
+// of t, nxt = buffer of t+1); aX/bX are
 // the A rows / B columns of half X; reads fill registers for the next stage:
 //     S0 MFMA Q00 + Q10 (a0 a1 . b0)
 //     S1 mem: read b1[cur];          copy a0, a1, b0 [cur] <- t+2
