@@ -20,7 +20,9 @@ many loads outstanding as the wave issued after the newest load that some
 later read, due by then, depends on.  The model lists, per layout, which
 halves each memory stage reads (for the next stage) and copies (two K-steps
 ahead), derives the largest safe count for each wait, checks every refill's
-distance, and compares the counts with the compiled loop's.
+distance, and compares the counts with the compiled loop's.  The 4-wave
+within-wave interleaved kernel (all waves in step, two barriers per K-step)
+gets the same treatment at the end of the file.
 """
 import os
 import re
@@ -189,3 +191,73 @@ def test_compiled_waits_match_the_model(asm):
             assert len(vm) == 1, (fn, vm)
             want = s1 if reads == min(sum(o.startswith("ds_read") for o in x) for x in mem) else s3
             assert vm[0] == want, f"{fn}: memory stage with {reads} reads waits vmcnt({vm[0]}), model {want}"
+
+
+# ---- the 4-wave within-wave interleaved kernel ------------------------------
+# One wave per SIMD, all waves in step: every barrier is passed by all waves
+# together, each wave having waited for its own copies (vmcnt) and reads
+# (lgkmcnt(0)) first.  Per K-step s two segments, each opened by a barrier:
+# after the top barrier clusters c00 and c01 read B1 and A1 of step s and copy
+# A0 and B0 of step s + 2; after the middle barrier c10 and c11 read A0 and B0
+# of step s + 1 and copy B1 and A1 of step s + 2.  Each wave copies its share
+# of a half with 4 loads (4 waves).
+PIECES4 = 4
+SEGMENTS4 = [  # (reads (half, step offset), copies (halves for step + 2, in issue order))
+    ([("b1", 0), ("a1", 0)], ["a0", "b0"]),
+    ([("a0", 1), ("b0", 1)], ["b1", "a1"]),
+]
+
+
+def simulate4(steps=10):
+    """(issues [(half, step, segment)], reads [(half, step, segment)]); segment
+    2s + k follows the k-th barrier of step s; the prologue's copies (steps 0
+    and 1 in the steady-state order) are segment -1."""
+    order = SEGMENTS4[0][1] + SEGMENTS4[1][1]
+    issues = [(h, u, -1) for u in (0, 1) for h in order for _ in range(PIECES4)]
+    reads = []
+    for s in range(steps):
+        for k, (rd, cp) in enumerate(SEGMENTS4):
+            g = 2 * s + k
+            reads += [(h, s + d, g) for h, d in rd]
+            issues += [(h, s + 2, g) for h in cp for _ in range(PIECES4)]
+    return issues, reads
+
+
+def max_wait4(issues, reads, seg):
+    """Largest vmcnt allowed at the barrier that opens segment `seg`: the reads
+    of that segment need every load of their halves issued before it."""
+    last = max(i for i, x in enumerate(issues) if x[2] < seg)
+    bound = None
+    for h, u, g in reads:
+        if g != seg:
+            continue
+        newest = max(i for i, x in enumerate(issues) if x[0] == h and x[1] == u)
+        assert newest <= last, f"{h}({u}) read in segment {g} before its copy"
+        bound = last - newest if bound is None else min(bound, last - newest)
+    return bound
+
+
+def test_model4_refills_follow_a_barrier():
+    """A copy overwrites a half only in a segment after the one that last read
+    its previous occupant (that read completed before the barrier between)."""
+    issues, reads = simulate4()
+    for h, u, g in issues:
+        prev = [rg for rh, ru, rg in reads if rh == h and ru == u - 2]
+        if prev:
+            assert g > max(prev), (h, u, g, max(prev))
+
+
+def test_model4_counts():
+    issues, reads = simulate4()
+    assert {max_wait4(issues, reads, seg) for seg in range(8, 12)} == {16}
+
+
+def test_compiled_waits_match_the_model_4wave(tmp_path):
+    """Every wait in the 4-wave kernel's loops is the model's count."""
+    want = {max_wait4(*simulate4(), seg) for seg in range(8, 12)}
+    text = open(build.device_asm("gemm_interleaved.hip", str(tmp_path / "i.s"))).read()
+    fns = re.findall(r"^(_Z\w*gemm_interleaved_kernel\w*):", text, re.M)
+    assert len(fns) == 10
+    for fn in fns:
+        vm = {int(m) for o in loop_lines(text, fn) for m in re.findall(r"vmcnt\((\d+)\)", o)}
+        assert vm == want, f"{fn}: loop waits vmcnt{sorted(vm)}, model {sorted(want)}"
