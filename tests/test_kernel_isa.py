@@ -38,10 +38,11 @@ SOURCES = {"gemm_pipelined_kernel": "gemm_pipelined.hip", "gemm_interleaved_kern
            "gemm_tile128_kernel": "gemm_tile128.hip", "attention_fwd_kernel": "attention_fwd.hip"}
 
 
-def loops(asm: str, innermost: bool = True):
+def loops(asm: str, innermost: bool = True, full: bool = False):
     """{(kernel symbol, loop header): [instruction mnemonics]} of every loop
     (with innermost, only loops that hold no other loop: the main loops; a
-    persistent kernel's loop over its tiles holds them)."""
+    persistent kernel's loop over its tiles holds them); with full, whole
+    instruction lines instead of mnemonics."""
     out, fn, cur, outer = {}, None, None, set()
     lines = asm.splitlines()
     for n, line in enumerate(lines):
@@ -60,7 +61,7 @@ def loops(asm: str, innermost: bool = True):
             continue
         t = line.strip()
         if cur and fn and t and not t.startswith((";", ".")):
-            out.setdefault(cur, []).append(t.split()[0])
+            out.setdefault(cur, []).append(t if full else t.split()[0])
     return {k: v for k, v in out.items() if not (innermost and k in outer)}
 
 

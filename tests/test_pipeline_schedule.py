@@ -261,3 +261,58 @@ def test_compiled_waits_match_the_model_4wave(tmp_path):
     for fn in fns:
         vm = {int(m) for o in loop_lines(text, fn) for m in re.findall(r"vmcnt\((\d+)\)", o)}
         assert vm == want, f"{fn}: loop waits vmcnt{sorted(vm)}, model {sorted(want)}"
+
+
+# ---- the attention forward kernel's trips -----------------------------------
+# Two stages per trip i: M (both products; reads V(i) and K(i+2) among the
+# MFMAs; copies K(i+4) and V(i+2), 2 loads each per wave; ends with a vmcnt
+# wait) and V (the softmax; ends with lgkmcnt(0)).  K blocks and V blocks
+# live in two rings of four slots.  Group B runs one stage behind group A,
+# as in the GEMM: a block read by the leading group in stage R needs the
+# trailing group's copies waited at the end of its stage R - 2, and reads
+# issued in an M stage complete at the end of the V stage after it, so a
+# slot may be refilled from three stages after the reading M stage on.
+RING = 4
+
+
+def simulate_attention(trips=12):
+    issues, reads = [], []          # (ring, block, stage)
+    for i in range(trips):
+        g = 2 * i                    # M stage of trip i
+        reads += [("V", i, g), ("K", i + 2, g)]
+        issues += [("K", i + 4, g)] * 2 + [("V", i + 2, g)] * 2
+    return issues, reads
+
+
+def test_attention_model_wait_and_ring_distances():
+    issues, reads = simulate_attention()
+    # copy -> read: the wait at the end of the M stage of trip i covers the
+    # reads of the M stage of trip i + 1
+    for i in range(3, 9):
+        end = 2 * i
+        last = max(n for n, x in enumerate(issues) if x[2] <= end)
+        need = [max(n for n, x in enumerate(issues) if x[:2] == r[:2]) for r in reads if r[2] == end + 2]
+        assert min(last - n for n in need) == 4
+    # read -> refill: block j's slot (j mod 4) is refilled by block j + 4
+    for ring, j, g in issues:
+        prev = [rg for rr, rj, rg in reads if rr == ring and rj == j - RING]
+        if prev:
+            assert g - max(prev) >= 3, (ring, j, g, max(prev))
+
+
+def test_attention_trip_loops_wait_as_modelled():
+    """Every trip loop of the 8-wave attention kernel waits vmcnt(4) (once, at
+    the end of its M stage) and lgkmcnt(0) at the end of its V stage."""
+    import tempfile
+    from tests.test_kernel_isa import loops
+    with tempfile.TemporaryDirectory() as d:
+        text = open(build.device_asm("attention_fwd.hip", os.path.join(d, "a.s"))).read()
+    seen = 0
+    for (fn, hdr), lines in loops(text, full=True).items():
+        if "attention_fwd_kernel" not in fn:
+            continue
+        vm = [int(m) for l in lines for m in re.findall(r"vmcnt\((\d+)\)", l)]
+        assert vm == [4], f"{fn} {hdr}: vmcnt {vm}"
+        assert any(re.search(r"lgkmcnt\(0\)", l) for l in lines), (fn, hdr)
+        seen += 1
+    assert seen == 16        # 8 instantiations x (unmasked, masked) trip loops
